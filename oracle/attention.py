@@ -1,0 +1,72 @@
+"""Decode attention over the compressed cache (plus an optional window of
+recent full-precision tokens).
+
+iThome, "why not just round": score = Q . K, output = softmax(score) . V.
+Roadmap §3.2: decode scores keys straight from the codes (rotate q once, look
+the codebook up per query) and runs the softmax in the exp2 domain; the
+oracle computes the same quantities directly in fp64, with no splitting.
+Hub, "vLLM integration" (hybrid mode): the most recent 128 tokens (configurable)
+stay in full precision and join the same attention.
+
+Readings: logits are sm_scale * score with sm_scale = 1/sqrt(d) by default
+(the iThome formula writes score = Q . K without a scale); query head h uses KV
+head h // G with G = num_q_heads / num_kv_heads (consecutive grouping); every
+cached token is attended; recent tokens are scored exactly, <q, k> with the
+bf16 key and unrotated query.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from . import keys as _keys
+from . import values as _values
+
+__all__ = ["decode_one_sequence", "softmax_attend"]
+
+
+def softmax_attend(logits, values) -> np.ndarray:
+    """Textbook softmax(logits) @ values in fp64 (logits [T], values [T, d]).
+    An empty set of tokens gives a zero vector."""
+    logits = np.asarray(logits, dtype=np.float64)
+    values = np.asarray(values, dtype=np.float64)
+    if logits.size == 0:
+        return np.zeros(values.shape[-1])
+    w = np.exp(logits - logits.max())
+    return (w / w.sum()) @ values
+
+
+def decode_one_sequence(q, fields_per_head, ctx, recent_k=None, recent_v=None, sm_scale=None):
+    """Attention output and raw scores for one sequence.
+
+    ``q``: [Hq, d] query (fp32-exact values).
+    ``fields_per_head``: list over KV heads of the dicts returned by
+    ``oracle.paged.read_tokens`` (quantised tokens, all the same length L).
+    ``ctx``: dict with d1, d2, S, c32.
+    ``recent_k``/``recent_v``: [Hkv, R, d] full-precision window or None.
+
+    Returns (out [Hq, d], scores [Hq, L + R]) where scores are the unscaled
+    estimates for the quantised tokens followed by exact <q, k> for the
+    recent ones."""
+    q = np.asarray(q, dtype=np.float64)
+    Hq, d = q.shape
+    Hkv = len(fields_per_head)
+    G = Hq // Hkv
+    scale = (1.0 / np.sqrt(d)) if sm_scale is None else float(sm_scale)
+    outs, scores = [], []
+    for h in range(Hq):
+        f = fields_per_head[h // G]
+        est = _keys.estimate_scores(q[h], f["idx"], f["sign"], f["n16"], f["g16"],
+                                    ctx["d1"], ctx["d2"], ctx["S"], ctx["c32"])
+        vhat = _values.dequantize_values(f["q"], f["s16"], f["z16"])
+        if recent_k is not None:
+            rk = np.asarray(recent_k[h // G], dtype=np.float64)
+            rv = np.asarray(recent_v[h // G], dtype=np.float64)
+            exact = rk @ q[h]
+            s_all = np.concatenate([est, exact])
+            v_all = np.concatenate([vhat, rv], axis=0)
+        else:
+            s_all, v_all = est, vhat
+        outs.append(softmax_attend(scale * s_all, v_all))
+        scores.append(s_all)
+    return np.stack(outs), np.stack(scores)

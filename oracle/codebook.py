@@ -1,0 +1,157 @@
+"""Lloyd-Max codebook for one coordinate of a randomly rotated unit vector.
+
+Hub, "technical principle", steps 1-2: after the random orthogonal rotation
+each coordinate of the (unit) key direction follows a Beta-type law, and the
+method precomputes optimal (Lloyd-Max) scalar codebooks of 2, 3 and 4 bits for
+head_dim 128 and 256; quantising a coordinate means finding its nearest
+codeword.  iThome, "the core idea of TurboQuant": for MSE, each rotated
+coordinate is given its closest optimal centroid.
+
+The law of one coordinate U of a uniform point on the sphere S^(d-1) has
+density  f(u) = (1-u^2)^((d-3)/2) / B(1/2, (d-1)/2)  on [-1, 1]; equivalently
+(U+1)/2 ~ Beta(a, a) with a = (d-1)/2, which is the pages' "Beta distribution".
+
+Lloyd's conditions (the textbook definition of a Lloyd-Max quantiser):
+thresholds are midpoints of neighbouring centroids, and each centroid is the
+conditional mean of U over its cell.  Both are evaluated here in closed form:
+
+* cell mass  P(a < U <= b) = I_{(b+1)/2}(a, a) - I_{(a+1)/2}(a, a)
+  (regularised incomplete beta);
+* first moment  E[U 1{a<U<=b}] = ((1-a^2)^((d-1)/2) - (1-b^2)^((d-1)/2))
+  / ((d-1) B(1/2, (d-1)/2))  (the antiderivative of u (1-u^2)^((d-3)/2)).
+
+The density is even, so the optimal quantiser is odd-symmetric; each iterate
+is averaged with its reflection so that symmetry (and a middle threshold of
+exactly 0 for even level counts) holds to the last bit.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+from scipy import special
+
+__all__ = [
+    "beta_half",
+    "density",
+    "cell_mass",
+    "cell_first_moment",
+    "lloyd_max",
+    "tables_fp32",
+    "distortion",
+]
+
+
+def beta_half(d: int) -> float:
+    """B(1/2, (d-1)/2), the normaliser of the coordinate density."""
+    return math.exp(special.betaln(0.5, (d - 1) / 2.0))
+
+
+def density(u, d: int):
+    """f(u) = (1-u^2)^((d-3)/2) / B(1/2, (d-1)/2) on [-1, 1]."""
+    u = np.asarray(u, dtype=np.float64)
+    return np.power(np.clip(1.0 - u * u, 0.0, None), (d - 3) / 2.0) / beta_half(d)
+
+
+def _cdf(x, d: int):
+    """P(U <= x) through the Beta(a, a) law of (U+1)/2; upper tail when x > 0."""
+    a = (d - 1) / 2.0
+    x = np.asarray(x, dtype=np.float64)
+    y = (x + 1.0) / 2.0
+    lo = special.betainc(a, a, np.clip(y, 0.0, 1.0))
+    hi = 1.0 - special.betaincc(a, a, np.clip(y, 0.0, 1.0))
+    return np.where(x <= 0.0, lo, hi)
+
+
+def _sf(x, d: int):
+    """P(U > x)."""
+    a = (d - 1) / 2.0
+    x = np.asarray(x, dtype=np.float64)
+    y = (x + 1.0) / 2.0
+    return special.betaincc(a, a, np.clip(y, 0.0, 1.0))
+
+
+def cell_mass(a, b, d: int):
+    """P(a < U <= b).  Upper-tail differences are used right of 0 to keep
+    relative accuracy in the outer cells."""
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    left = _cdf(b, d) - _cdf(a, d)
+    right = _sf(a, d) - _sf(b, d)
+    return np.where(a >= 0.0, right, left)
+
+
+def cell_first_moment(a, b, d: int):
+    """E[U 1{a < U <= b}] in closed form."""
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    e = (d - 1) / 2.0
+    pa = np.power(np.clip(1.0 - a * a, 0.0, None), e)
+    pb = np.power(np.clip(1.0 - b * b, 0.0, None), e)
+    return (pa - pb) / ((d - 1) * beta_half(d))
+
+
+def _initial_centroids(d: int, levels: int) -> np.ndarray:
+    """Start from the conditional means of equal-mass cells (quantiles of the
+    law), which never underflow the density."""
+    a = (d - 1) / 2.0
+    probs = np.arange(levels + 1, dtype=np.float64) / levels
+    y = special.betaincinv(a, a, probs)
+    edges = 2.0 * y - 1.0
+    edges[0], edges[-1] = -1.0, 1.0
+    return cell_first_moment(edges[:-1], edges[1:], d) / cell_mass(edges[:-1], edges[1:], d)
+
+
+def lloyd_max(d: int, bits: int, tol: float = 1e-14, max_iter: int = 100000):
+    """Run Lloyd's iteration to a fixed point.
+
+    Stops when no centroid moves by more than ``tol`` times the largest
+    centroid magnitude.  Returns ``(centroids, thresholds, iterations)`` in
+    fp64, centroids ascending (index 0 the most negative), ``2**bits`` of
+    them, and ``2**bits - 1`` thresholds (midpoints)."""
+    levels = 1 << bits
+    c = _initial_centroids(d, levels)
+    c = 0.5 * (c - c[::-1])
+    it = 0
+    for it in range(1, max_iter + 1):
+        t = 0.5 * (c[:-1] + c[1:])
+        lo = np.concatenate(([-1.0], t))
+        hi = np.concatenate((t, [1.0]))
+        c_new = cell_first_moment(lo, hi, d) / cell_mass(lo, hi, d)
+        c_new = 0.5 * (c_new - c_new[::-1])
+        delta = float(np.max(np.abs(c_new - c)))
+        c = c_new
+        if delta <= tol * float(np.max(np.abs(c))):
+            break
+    t = 0.5 * (c[:-1] + c[1:])
+    return c, t, it
+
+
+def tables_fp32(d: int, bits: int):
+    """The stored tables: fp32 centroids and fp32 thresholds, where each
+    threshold is the fp32 rounding of the fp64 midpoint."""
+    c, t, _ = lloyd_max(d, bits)
+    return c.astype(np.float32), t.astype(np.float32)
+
+
+def distortion(d: int, centroids, thresholds) -> float:
+    """Total distortion d * E[(U - Q(U))^2] of the quantiser, in closed form.
+
+    Per cell (a, b] with centroid c it is  E[U^2 1] - 2 c E[U 1] + c^2 P.
+    Integrating u * u (1-u^2)^((d-3)/2) by parts gives
+    E[U^2 1{a<U<=b}] = (a (1-a^2)^((d-1)/2) - b (1-b^2)^((d-1)/2)) / (d B)
+    + P(a<U<=b) / d, with B = B(1/2, (d-1)/2); over [-1, 1] this is 1/d."""
+    c = np.asarray(centroids, dtype=np.float64)
+    t = np.asarray(thresholds, dtype=np.float64)
+    lo = np.concatenate(([-1.0], t))
+    hi = np.concatenate((t, [1.0]))
+    e = (d - 1) / 2.0
+    bh = beta_half(d)
+    mass = cell_mass(lo, hi, d)
+    m1 = cell_first_moment(lo, hi, d)
+    pa = np.power(np.clip(1.0 - lo * lo, 0.0, None), e)
+    pb = np.power(np.clip(1.0 - hi * hi, 0.0, None), e)
+    m2 = (lo * pa - hi * pb) / (d * bh) + mass / d
+    per_coord = float(np.sum(m2 - 2.0 * c * m1 + c * c * mass))
+    return d * per_coord

@@ -1,0 +1,116 @@
+"""Paged KV-cache record layout.
+
+iThome (introduction, and "which path vLLM actually takes"): the cache is cut
+into fixed-size blocks located through a block table; the store kernel
+quantises and packs new K/V and writes them into the paged cache, and the
+decode kernel reads the compressed K/V back through the block table.
+
+Reading (the pages fix no byte layout): the pool is
+``pool[num_blocks][num_kv_heads][record]`` with 16 token slots per block.  A
+record holds the 16 slots of one (block, KV head) as consecutive regions, each
+a multiple of 16 bytes:
+
+  Kcodes  [16][b_k*d/8]   slot-major: the LSB-first code stream of each slot
+  Kqjl    [16][d/8]       slot-major: the QJL sign bits of each slot
+  Kmeta   [16][2] fp16    (n, gamma) of each slot
+  Vcodes  [b_v*d/8][16]   byte-major: byte f of every slot's value-code
+                          stream, for f = 0, 1, ... (a 16-row transpose)
+  Vmeta   [d/32][16][2]   fp16 (scale, zero) per (group, slot)
+
+Token t of sequence s lives in block ``block_table[s][t // 16]``, slot
+``t % 16``; the writer addresses slot ``slot_mapping[i]`` of token i as block
+``slot_mapping[i] // 16``, slot ``slot_mapping[i] % 16``.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from . import bits as _bits
+
+__all__ = ["BLOCK", "layout", "write_tokens", "read_tokens", "new_pool"]
+
+BLOCK = 16
+
+
+def layout(d: int, b_k: int, b_v: int) -> dict:
+    kc = BLOCK * (b_k * d // 8)
+    kq = BLOCK * (d // 8)
+    km = BLOCK * 4
+    vc = (b_v * d // 8) * BLOCK
+    vm = (d // 32) * BLOCK * 4
+    off = {}
+    o = 0
+    for name, size in (("kcodes", kc), ("kqjl", kq), ("kmeta", km), ("vcodes", vc), ("vmeta", vm)):
+        off[name] = (o, size)
+        o += size
+    off["bytes"] = o
+    off["d"], off["b_k"], off["b_v"] = d, b_k, b_v
+    return off
+
+
+def new_pool(num_blocks: int, num_kv_heads: int, lay: dict) -> np.ndarray:
+    return np.zeros((num_blocks, num_kv_heads, lay["bytes"]), dtype=np.uint8)
+
+
+def _region_index(lay: dict, name: str, slots, width: int, slot_major: bool):
+    """Byte offsets inside a record of ``width`` bytes per slot for each slot:
+    slot-major regions hold a slot's bytes contiguously, byte-major regions
+    hold byte f of every slot contiguously."""
+    o, _ = lay[name]
+    s = np.asarray(slots, dtype=np.int64)[:, None]
+    f = np.arange(width, dtype=np.int64)[None, :]
+    return o + (s * width + f if slot_major else f * BLOCK + s)
+
+
+def write_tokens(pool, slot_mapping, head: int, kenc: dict, venc: dict, lay: dict) -> None:
+    """Write encoded tokens (rows of ``kenc``/``venc``) of one KV head into the
+    slots named by ``slot_mapping``."""
+    d, b_k, b_v = lay["d"], lay["b_k"], lay["b_v"]
+    ng = d // 32
+    sm = np.asarray(slot_mapping, dtype=np.int64)
+    blk = (sm // BLOCK)[:, None]
+    slot = sm % BLOCK
+    kcodes = _bits.pack(kenc["idx"], b_k)
+    kqjl = _bits.pack(kenc["sign"], 1)
+    kmeta = np.stack([kenc["n16"], kenc["g16"]], axis=1).astype(np.uint16).view(np.uint8)
+    vcodes = _bits.pack(venc["q"], b_v)
+    pool[blk, head, _region_index(lay, "kcodes", slot, b_k * d // 8, True)] = kcodes
+    pool[blk, head, _region_index(lay, "kqjl", slot, d // 8, True)] = kqjl
+    pool[blk, head, _region_index(lay, "kmeta", slot, 4, True)] = kmeta
+    pool[blk, head, _region_index(lay, "vcodes", slot, b_v * d // 8, False)] = vcodes
+    o, _ = lay["vmeta"]
+    for g in range(ng):
+        pair = np.stack([venc["s16"][:, g], venc["z16"][:, g]], axis=1).astype(np.uint16).view(np.uint8)
+        idx = o + (g * BLOCK + slot[:, None]) * 4 + np.arange(4)[None, :]
+        pool[blk, head, idx] = pair
+
+
+def read_tokens(pool, block_table_row, length: int, head: int, lay: dict) -> dict:
+    """Read the first ``length`` tokens of one sequence and KV head back into
+    fields: idx [L, d], sign [L, d], n16, g16 [L], q [L, d], s16, z16 [L, d/32]."""
+    d, b_k, b_v = lay["d"], lay["b_k"], lay["b_v"]
+    ng = d // 32
+    t = np.arange(length, dtype=np.int64)
+    blk = np.asarray(block_table_row, dtype=np.int64)[t // BLOCK][:, None]
+    slot = t % BLOCK
+    kcodes = pool[blk, head, _region_index(lay, "kcodes", slot, b_k * d // 8, True)]
+    kqjl = pool[blk, head, _region_index(lay, "kqjl", slot, d // 8, True)]
+    kmeta = np.ascontiguousarray(pool[blk, head, _region_index(lay, "kmeta", slot, 4, True)]).view(np.uint16)
+    vcodes = pool[blk, head, _region_index(lay, "vcodes", slot, b_v * d // 8, False)]
+    o, _ = lay["vmeta"]
+    s16 = np.zeros((length, ng), np.uint16)
+    z16 = np.zeros((length, ng), np.uint16)
+    for g in range(ng):
+        idx = o + (g * BLOCK + slot[:, None]) * 4 + np.arange(4)[None, :]
+        pair = np.ascontiguousarray(pool[blk, head, idx]).view(np.uint16)
+        s16[:, g], z16[:, g] = pair[:, 0], pair[:, 1]
+    return {
+        "idx": _bits.unpack(kcodes, b_k, d),
+        "sign": _bits.unpack(kqjl, 1, d).astype(np.uint8),
+        "n16": kmeta[:, 0].copy(),
+        "g16": kmeta[:, 1].copy(),
+        "q": _bits.unpack(vcodes, b_v, d),
+        "s16": s16,
+        "z16": z16,
+    }
