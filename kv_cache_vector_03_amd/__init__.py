@@ -1,0 +1,288 @@
+"""MI355X (gfx950) TurboQuant KV-cache hot path — thin Python binding.
+
+Every function here marshals arguments to the C ABI declared in
+``include/tq_api.h`` and calls ``libtq_mi355x.so``; all work of the path runs
+in the library's HIP kernels.  PyTorch supplies device memory and streams
+only.  There is no fallback: if the library is missing, importing the
+binding's entry points raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "TQ_OK", "TQ_EINVAL", "TQ_EUNSUPPORTED", "TQ_EHIP", "TQ_ENOMEM", "TQ_DTYPE_F32", "TQ_DTYPE_BF16",
+    "TqError", "Context", "library_path", "load", "tq_codebook_init", "tq_ctx_destroy", "tq_ctx_tables",
+    "tq_lloyd_max", "tq_record_layout", "tq_draw_params", "tq_block_bytes", "tq_quantize_store",
+    "tq_decode_workspace_bytes", "tq_decode_attention", "tq_last_error", "EXPORTED_SYMBOLS",
+]
+
+TQ_OK, TQ_EINVAL, TQ_EUNSUPPORTED, TQ_EHIP, TQ_ENOMEM = 0, -1, -2, -3, -4
+TQ_DTYPE_F32, TQ_DTYPE_BF16 = 0, 1
+
+EXPORTED_SYMBOLS = [
+    "tq_codebook_init", "tq_ctx_destroy", "tq_ctx_tables", "tq_ctx_preset", "tq_lloyd_max", "tq_record_layout",
+    "tq_draw_params", "tq_block_bytes", "tq_quantize_store", "tq_decode_workspace_bytes", "tq_decode_attention",
+    "tq_last_error",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libtq_mi355x.so")
+
+
+class TqError(RuntimeError):
+    def __init__(self, code, where):
+        super().__init__(f"{where} failed with {code}: {tq_last_error()}")
+        self.code = code
+
+
+class tq_preset(ctypes.Structure):
+    _fields_ = [("head_dim", ctypes.c_int32), ("k_bits", ctypes.c_int32), ("v_bits", ctypes.c_int32),
+                ("v_group", ctypes.c_int32), ("block_size", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("seed", ctypes.c_uint64)]
+
+
+class tq_layout(ctypes.Structure):
+    _fields_ = [("kcodes", ctypes.c_int64), ("kqjl", ctypes.c_int64), ("kmeta", ctypes.c_int64),
+                ("vcodes", ctypes.c_int64), ("vmeta", ctypes.c_int64), ("record_bytes", ctypes.c_int64)]
+
+
+class tq_decode_args(ctypes.Structure):
+    _fields_ = [
+        ("q", ctypes.c_void_p), ("q_dtype", ctypes.c_int32), ("batch", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32), ("num_presets", ctypes.c_int32),
+        ("ctx", ctypes.c_void_p * 2), ("pool", ctypes.c_void_p * 2), ("pool_blocks", ctypes.c_int64 * 2),
+        ("seq_preset", ctypes.c_void_p), ("block_tables", ctypes.c_void_p), ("max_blocks_per_seq", ctypes.c_int32),
+        ("seq_lens", ctypes.c_void_p), ("recent_k", ctypes.c_void_p), ("recent_v", ctypes.c_void_p),
+        ("recent_lens", ctypes.c_void_p), ("recent_window", ctypes.c_int32), ("sm_scale", ctypes.c_float),
+        ("chunk_tokens", ctypes.c_int32), ("max_seq_len", ctypes.c_int32), ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t), ("out", ctypes.c_void_p), ("scores_out", ctypes.c_void_p),
+        ("scores_stride", ctypes.c_int32),
+    ]
+
+
+def load(path: str | None = None):
+    """Load the library once; raises if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = path or library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m kv_cache_vector_03_amd.build`")
+    lib = ctypes.CDLL(path)
+    c = ctypes
+    P = c.c_void_p
+    sig = {
+        "tq_codebook_init": (c.c_int, [c.POINTER(tq_preset), P, P, c.POINTER(P)]),
+        "tq_ctx_destroy": (c.c_int, [P]),
+        "tq_ctx_tables": (c.c_int, [P, P, P, P, P]),
+        "tq_ctx_preset": (c.c_int, [P, c.POINTER(tq_preset)]),
+        "tq_lloyd_max": (c.c_int, [c.c_int32, c.c_int32, P, P]),
+        "tq_record_layout": (c.c_int, [c.POINTER(tq_preset), c.POINTER(tq_layout)]),
+        "tq_draw_params": (c.c_int, [c.c_uint64, c.c_int32, P, P]),
+        "tq_block_bytes": (c.c_size_t, [P]),
+        "tq_quantize_store": (c.c_int, [P, P, P, c.c_int32, c.c_int64, c.c_int32, P, P, c.c_int64, P]),
+        "tq_decode_workspace_bytes": (c.c_size_t, [c.POINTER(tq_decode_args)]),
+        "tq_decode_attention": (c.c_int, [c.POINTER(tq_decode_args), P]),
+        "tq_last_error": (c.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    _LIB = lib
+    return lib
+
+
+def tq_last_error() -> str:
+    if _LIB is None:
+        return ""
+    return _LIB.tq_last_error().decode()
+
+
+def _check(code, where):
+    if code != TQ_OK:
+        raise TqError(code, where)
+
+
+def _ptr(arr) -> int:
+    """Address of a numpy array or torch tensor (None -> NULL)."""
+    if arr is None:
+        return None
+    if hasattr(arr, "data_ptr"):
+        return arr.data_ptr()
+    return arr.ctypes.data
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return TQ_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return TQ_DTYPE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
+
+
+class Context:
+    """Owner of a ``tq_ctx*`` (freed on ``close()`` or garbage collection)."""
+
+    def __init__(self, handle: int, head_dim: int, k_bits: int, v_bits: int):
+        self.handle = handle
+        self.head_dim, self.k_bits, self.v_bits = head_dim, k_bits, v_bits
+
+    @property
+    def block_bytes(self) -> int:
+        return tq_block_bytes(self)
+
+    def close(self):
+        if self.handle:
+            load().tq_ctx_destroy(ctypes.c_void_p(self.handle))
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def tq_codebook_init(head_dim: int, k_bits: int, v_bits: int, seed: int = 0, signs=None, S=None) -> Context:
+    """Create a context.  ``signs`` (int8 [2, d]) and ``S`` (float32 [d, d])
+    are host numpy arrays or None (then drawn from ``seed``)."""
+    lib = load()
+    p = tq_preset(head_dim, k_bits, v_bits, 32, 16, 0, seed)
+    h = ctypes.c_void_p()
+    if signs is not None:
+        import numpy as np
+        signs = np.ascontiguousarray(signs, dtype=np.int8)
+    if S is not None:
+        import numpy as np
+        S = np.ascontiguousarray(S, dtype=np.float32)
+    _check(lib.tq_codebook_init(ctypes.byref(p), _ptr(signs), _ptr(S), ctypes.byref(h)), "tq_codebook_init")
+    return Context(h.value, head_dim, k_bits, v_bits)
+
+
+def tq_ctx_destroy(ctx: Context) -> None:
+    ctx.close()
+
+
+def tq_ctx_tables(ctx: Context):
+    """(centroids, thresholds, signs, S) host copies as numpy arrays."""
+    import numpy as np
+    L = 1 << ctx.k_bits
+    d = ctx.head_dim
+    c = np.zeros(L, np.float32)
+    t = np.zeros(L - 1, np.float32)
+    sg = np.zeros((2, d), np.int8)
+    S = np.zeros((d, d), np.float32)
+    _check(load().tq_ctx_tables(ctx.handle, _ptr(c), _ptr(t), _ptr(sg), _ptr(S)), "tq_ctx_tables")
+    return c, t, sg, S
+
+
+def tq_lloyd_max(head_dim: int, bits: int):
+    import numpy as np
+    c = np.zeros(1 << bits, np.float64)
+    t = np.zeros((1 << bits) - 1, np.float64)
+    _check(load().tq_lloyd_max(head_dim, bits, _ptr(c), _ptr(t)), "tq_lloyd_max")
+    return c, t
+
+
+def tq_record_layout(head_dim: int, k_bits: int, v_bits: int) -> dict:
+    p = tq_preset(head_dim, k_bits, v_bits, 32, 16, 0, 0)
+    out = tq_layout()
+    _check(load().tq_record_layout(ctypes.byref(p), ctypes.byref(out)), "tq_record_layout")
+    return {f: getattr(out, f) for f, _ in tq_layout._fields_}
+
+
+def tq_draw_params(seed: int, head_dim: int):
+    import numpy as np
+    sg = np.zeros((2, head_dim), np.int8)
+    S = np.zeros((head_dim, head_dim), np.float32)
+    _check(load().tq_draw_params(seed, head_dim, _ptr(sg), _ptr(S)), "tq_draw_params")
+    return sg, S
+
+
+def tq_block_bytes(ctx: Context) -> int:
+    return int(load().tq_block_bytes(ctx.handle))
+
+
+def tq_quantize_store(ctx: Context, k, v, slot_mapping, pool, stream=None) -> None:
+    """k, v: device tensors [T, Hkv, d] (bf16 or f32, same dtype);
+    slot_mapping: device int32 [T]; pool: device uint8 [num_blocks, Hkv, record]."""
+    import torch
+    if k.shape != v.shape or k.dtype != v.dtype or k.dim() != 3:
+        raise ValueError("k and v must be [T, Hkv, d] tensors of one dtype")
+    if slot_mapping.dtype != torch.int32 or pool.dtype != torch.uint8:
+        raise TypeError("slot_mapping must be int32 and pool uint8")
+    if not (k.is_contiguous() and v.is_contiguous() and slot_mapping.is_contiguous() and pool.is_contiguous()):
+        raise ValueError("tensors must be contiguous")
+    T, Hkv, d = k.shape
+    if d != ctx.head_dim or pool.dim() != 3 or pool.shape[1] != Hkv or pool.shape[2] != ctx.block_bytes:
+        raise ValueError("shape mismatch between k/v, pool and context")
+    if slot_mapping.numel() != T:
+        raise ValueError("slot_mapping must have one entry per token")
+    _check(load().tq_quantize_store(ctx.handle, _ptr(k), _ptr(v), _dtype_code(k), T, Hkv, _ptr(slot_mapping),
+                                    _ptr(pool), pool.shape[0], _stream(stream)), "tq_quantize_store")
+
+
+def _decode_args(q, ctxs, pools, block_tables, seq_lens, out, workspace=None, seq_preset=None, recent_k=None,
+                 recent_v=None, recent_lens=None, sm_scale=0.0, chunk_tokens=512, max_seq_len=None,
+                 scores_out=None):
+    B, Hq, d = q.shape
+    a = tq_decode_args()
+    a.q = _ptr(q)
+    a.q_dtype = _dtype_code(q)
+    a.batch, a.num_q_heads = B, Hq
+    a.num_kv_heads = pools[0].shape[1]
+    a.num_presets = len(ctxs)
+    for i, (c, p) in enumerate(zip(ctxs, pools)):
+        a.ctx[i] = c.handle
+        a.pool[i] = _ptr(p)
+        a.pool_blocks[i] = p.shape[0]
+    a.seq_preset = _ptr(seq_preset)
+    a.block_tables = _ptr(block_tables)
+    a.max_blocks_per_seq = block_tables.shape[1]
+    a.seq_lens = _ptr(seq_lens)
+    a.recent_k, a.recent_v, a.recent_lens = _ptr(recent_k), _ptr(recent_v), _ptr(recent_lens)
+    a.recent_window = recent_k.shape[2] if recent_k is not None else 0
+    a.sm_scale = sm_scale
+    a.chunk_tokens = chunk_tokens
+    a.max_seq_len = block_tables.shape[1] * 16 if max_seq_len is None else max_seq_len
+    a.workspace = _ptr(workspace)
+    a.workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    a.out = _ptr(out)
+    a.scores_out = _ptr(scores_out)
+    a.scores_stride = scores_out.shape[-1] if scores_out is not None else 0
+    return a
+
+
+def tq_decode_workspace_bytes(q, ctxs, pools, block_tables, seq_lens, out, **kw) -> int:
+    a = _decode_args(q, ctxs, pools, block_tables, seq_lens, out, **kw)
+    n = load().tq_decode_workspace_bytes(ctypes.byref(a))
+    if n == 0:
+        raise TqError(TQ_EINVAL, "tq_decode_workspace_bytes")
+    return int(n)
+
+
+def tq_decode_attention(q, ctxs, pools, block_tables, seq_lens, out, workspace, stream=None, **kw) -> None:
+    """q: device [B, Hq, d] bf16/f32; ctxs/pools: one or two presets;
+    block_tables int32 [B, max_blocks]; seq_lens int32 [B]; out float32 [B, Hq, d];
+    workspace: device uint8 tensor of tq_decode_workspace_bytes(...) bytes.
+    Keyword arguments: seq_preset (int8 [B]), recent_k / recent_v (bf16
+    [B, Hkv, W, d]) with recent_lens (int32 [B]), sm_scale, chunk_tokens,
+    max_seq_len, scores_out (float32 [B, Hq, stride])."""
+    a = _decode_args(q, ctxs, pools, block_tables, seq_lens, out, workspace, **kw)
+    _check(load().tq_decode_attention(ctypes.byref(a), _stream(stream)), "tq_decode_attention")

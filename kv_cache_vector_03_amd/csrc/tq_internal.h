@@ -1,0 +1,70 @@
+// Internal declarations shared by the host library and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "tq_api.h"
+
+namespace tq {
+
+// Per-context device tables.
+struct DevTables {
+  const float* centroids = nullptr;    // [2^k_bits] fp32
+  const float* thresholds = nullptr;   // [2^k_bits - 1] fp32
+  const float* signs1 = nullptr;       // D1 as fp32 +-1 [d]
+  const float* signs2 = nullptr;       // D2 as fp32 +-1 [d]
+  const float* S = nullptr;            // [d][d] fp32 row-major
+  // S^T as MFMA B-operand tiles of v_mfma_f32_16x16x32_f16, fp16 hi/lo split
+  // of (S * 2^kSScaleLog2): tile (nt, kt) holds lane l, element e =
+  // S[16 nt + l%16][32 kt + 8 (l/16) + e]; layout [nt][kt][hi,lo][64][8] fp16.
+  const uint16_t* s_tiles = nullptr;
+  // Decode pair table: entry a | b << k_bits = (bf16 hi c[a], bf16 hi c[b]),
+  // (bf16 lo c[a], bf16 lo c[b]) as two dwords; [2^(2 k_bits)][2] uint32.
+  const uint32_t* pair_lut = nullptr;
+};
+
+struct Layout {
+  int64_t kcodes, kqjl, kmeta, vcodes, vmeta, bytes;
+};
+
+}  // namespace tq
+
+struct tq_ctx {
+  tq_preset preset;
+  int device = 0;
+  int d = 0, kb = 0, vb = 0;
+  std::vector<double> c64, t64;
+  std::vector<float> c32, t32;
+  std::vector<int8_t> signs;  // [2][d]
+  std::vector<float> S;       // [d][d]
+  tq::Layout lay;
+  tq::DevTables dev;
+  void* dev_block = nullptr;  // one allocation holding every device table
+};
+
+namespace tq {
+
+constexpr int kSScaleLog2 = 4;   // S is pre-scaled by 16 before the fp16 split
+constexpr int kRScaleLog2 = 6;   // r is pre-scaled by 64 before the fp16 split
+
+void set_error(const char* fmt, ...);
+
+Layout make_layout(int d, int kb, int vb);
+
+// Kernel launchers (defined in the .hip files); return a hipError_t.
+hipError_t launch_quantize(const tq_ctx* c, const void* k, const void* v, int in_dtype, int64_t num_tokens,
+                           int num_kv_heads, const int32_t* slot_mapping, void* pool, int64_t num_blocks,
+                           hipStream_t stream);
+
+struct DecodePlan {
+  int d, G, num_splits_max, chunk;
+  size_t off_qt, off_p, off_part, bytes;
+};
+DecodePlan plan_decode(const tq_decode_args* a);
+hipError_t launch_decode(const tq_decode_args* a, const DecodePlan& plan, hipStream_t stream);
+
+}  // namespace tq

@@ -1,0 +1,355 @@
+// Fused quantise + pack + paged store for gfx950 (Roadmap §3.1: rotation fused
+// with the quantiser in one launch; Hub, technical principle steps 1-5).
+//
+// Work split: a wave owns a tile of 16 token-heads.  Lane (row = lane/4,
+// part = lane%4) holds coordinates [part*E, part*E+E) of its row, E = d/4, so
+// the Walsh-Hadamard butterflies run in registers for the strides below E and
+// across the 4 lanes of a row (xor 1, xor 2) for the last two.  The QJL
+// projection z = S r of the 16 rows is a dense [16 x d] x [d x d] product: it
+// runs on v_mfma_f32_16x16x32_f16 with fp16 hi/lo splits of the pre-scaled
+// operands (three products per tile: hi*hi + hi*lo + lo*hi), and the sign
+// bits come straight out of the accumulator with a wave ballot.
+#include <hip/hip_runtime.h>
+
+#include "tq_common.hip.h"
+#include "tq_internal.h"
+
+namespace tq {
+
+struct QArgs {
+  const void* k;
+  const void* v;
+  int64_t num_th;  // tokens * kv heads
+  int32_t hkv;
+  const int32_t* slot_mapping;
+  int64_t slots_total;  // 16 * num_blocks
+  uint8_t* pool;
+  int64_t rec;  // record bytes per (block, head)
+  Layout lay;
+  DevTables dev;
+  int64_t num_tiles;
+};
+
+template <int D>
+constexpr int kQWaves = D == 128 ? 8 : 4;  // d = 256 needs up to 512 VGPRs per lane
+
+template <int D>
+struct QLds {
+  static constexpr int KT = D / 32, NT = D / 16;
+  static constexpr bool kTilesInLds = (D == 128);
+  static constexpr int kRowStride = D + 8;  // halves; padding breaks bank conflicts of the A reads
+  static constexpr size_t tiles_bytes = kTilesInLds ? (size_t)NT * KT * 2 * 64 * 8 * 2 : 0;
+  static constexpr size_t a_bytes = (size_t)kQWaves<D> * 2 * 16 * kRowStride * 2;
+  static constexpr size_t ballot_bytes = (size_t)kQWaves<D> * NT * 4 * 8;
+  static constexpr size_t cent_bytes = 64;
+  static constexpr size_t total = tiles_bytes + a_bytes + ballot_bytes + cent_bytes;
+};
+
+template <bool BF16, int N>
+__device__ __forceinline__ void load_row_part(const void* base, int64_t elem_off, float (&x)[N]) {
+  if constexpr (BF16) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(base) + elem_off);
+#pragma unroll
+    for (int i = 0; i < N / 8; ++i) {
+      u32x4 w = __builtin_nontemporal_load(p + i);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[8 * i + 2 * j] = __uint_as_float(w[j] << 16);
+        x[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+      }
+    }
+  } else {
+    const f32x4* p = reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(base) + elem_off);
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i) {
+      f32x4 w = __builtin_nontemporal_load(p + i);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x[4 * i + j] = w[j];
+    }
+  }
+}
+
+template <int D, int KB, int VB, bool BF16>
+__global__ __launch_bounds__(kQWaves<D> * 64) void quantize_kernel(QArgs a) {
+  constexpr int E = D / 4;
+  constexpr int L = 1 << KB;
+  constexpr int KT = D / 32, NT = D / 16;
+  constexpr int RS = QLds<D>::kRowStride;
+  constexpr int SW = E / 32;  // sign-mask words per lane
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  uint16_t* s_tiles = reinterpret_cast<uint16_t*>(lds);
+  uint16_t* s_a = reinterpret_cast<uint16_t*>(lds + QLds<D>::tiles_bytes);
+  uint64_t* s_ballot = reinterpret_cast<uint64_t*>(lds + QLds<D>::tiles_bytes + QLds<D>::a_bytes);
+  float* s_c = reinterpret_cast<float*>(lds + QLds<D>::tiles_bytes + QLds<D>::a_bytes + QLds<D>::ballot_bytes);
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int row = lane >> 2, part = lane & 3;
+
+  if constexpr (QLds<D>::kTilesInLds) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(a.dev.s_tiles);
+    u32x4* dst = reinterpret_cast<u32x4*>(s_tiles);
+    constexpr int n16 = (int)(QLds<D>::tiles_bytes / 16);
+    for (int i = tid; i < n16; i += kQWaves<D> * 64) dst[i] = src[i];
+  }
+  if (tid < L) s_c[tid] = a.dev.centroids[tid];
+  float thr[L - 1];
+#pragma unroll
+  for (int i = 0; i < L - 1; ++i) thr[i] = a.dev.thresholds[i];
+  // D1 / D2 signs of this lane's coordinates as bit masks (bit = negative)
+  uint32_t m1[SW], m2[SW];
+#pragma unroll
+  for (int w = 0; w < SW; ++w) {
+    m1[w] = 0;
+    m2[w] = 0;
+#pragma unroll
+    for (int b = 0; b < 32; ++b) {
+      m1[w] |= (a.dev.signs1[part * E + 32 * w + b] < 0.f ? 1u : 0u) << b;
+      m2[w] |= (a.dev.signs2[part * E + 32 * w + b] < 0.f ? 1u : 0u) << b;
+    }
+  }
+  __syncthreads();
+
+  uint16_t* a_hi = s_a + (size_t)wave * 2 * 16 * RS;
+  uint16_t* a_lo = a_hi + 16 * RS;
+  uint64_t* ballots = s_ballot + (size_t)wave * NT * 4;
+  const float inv_sqrt_d = 1.0f / __builtin_sqrtf((float)D);
+  const float rscale = (float)(1 << kRScaleLog2);
+
+  for (int64_t tile = (int64_t)blockIdx.x * kQWaves<D> + wave; tile < a.num_tiles; tile += (int64_t)gridDim.x * kQWaves<D>) {
+    const int64_t th = tile * 16 + row;
+    const bool valid = th < a.num_th;
+    const int64_t t = valid ? th / a.hkv : 0;
+    const int h = valid ? (int)(th - t * a.hkv) : 0;
+
+    // ---- key: norm, rotation, Lloyd-Max index, residual
+    float x[E];
+    if (valid) {
+      load_row_part<BF16>(a.k, th * D + part * E, x);
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) x[e] = 0.f;
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) ss = __builtin_fmaf(x[e], x[e], ss);
+    ss = group_sum<4>(ss);
+    const float n = __builtin_sqrtf(ss);
+    const bool zero = !(n > 0.f);
+#pragma unroll
+    for (int e = 0; e < E; ++e) x[e] = __uint_as_float(__float_as_uint(x[e]) ^ (((m1[e / 32] >> (e % 32)) & 1u) << 31));
+#pragma unroll
+    for (int hs = 1; hs < E; hs <<= 1) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        if ((e & hs) == 0) {
+          float p = x[e], q = x[e + hs];
+          x[e] = p + q;
+          x[e + hs] = p - q;
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 1; m <= 2; m <<= 1) {
+      const bool upper = (part & m) != 0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        float y = __shfl_xor(x[e], m, 64);
+        x[e] = upper ? (y - x[e]) : (x[e] + y);
+      }
+    }
+    const float inv = zero ? 0.f : inv_sqrt_d / n;
+    uint32_t idx[E];
+    float r2 = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      float u = __uint_as_float(__float_as_uint(x[e] * inv) ^ (((m2[e / 32] >> (e % 32)) & 1u) << 31));
+      uint32_t c = 0;
+#pragma unroll
+      for (int i = 0; i < L - 1; ++i) c += (u > thr[i]) ? 1u : 0u;
+      c = zero ? 0u : c;
+      float r = zero ? 0.f : u - s_c[c];
+      idx[e] = c;
+      r2 = __builtin_fmaf(r, r, r2);
+      x[e] = r;
+    }
+    const float gamma = __builtin_sqrtf(group_sum<4>(r2));
+
+    // ---- stage the scaled residual as fp16 hi/lo rows for the MFMA A operand
+#pragma unroll
+    for (int e = 0; e < E; e += 2) {
+      float v0 = x[e] * rscale, v1 = x[e + 1] * rscale;
+      uint16_t h0 = f32_to_f16_bits(v0), h1 = f32_to_f16_bits(v1);
+      uint16_t l0 = f32_to_f16_bits(v0 - f16_bits_to_f32(h0)), l1 = f32_to_f16_bits(v1 - f16_bits_to_f32(h1));
+      *reinterpret_cast<uint32_t*>(a_hi + row * RS + part * E + e) = (uint32_t)h0 | ((uint32_t)h1 << 16);
+      *reinterpret_cast<uint32_t*>(a_lo + row * RS + part * E + e) = (uint32_t)l0 | ((uint32_t)l1 << 16);
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done
+    __builtin_amdgcn_wave_barrier();
+    f16x8 ahi[KT], alo[KT];
+    {
+      const int arow = lane & 15, kq = lane >> 4;
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        ahi[kt] = *reinterpret_cast<const f16x8*>(a_hi + arow * RS + 32 * kt + 8 * kq);
+        alo[kt] = *reinterpret_cast<const f16x8*>(a_lo + arow * RS + 32 * kt + 8 * kq);
+      }
+    }
+    // ---- z = S r on the matrix cores; sign bits by ballot
+#pragma unroll 1
+    for (int nt = 0; nt < NT; ++nt) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        const size_t tb = (((size_t)nt * KT + kt) * 2) * 64 * 8;
+        f16x8 bhi, blo;
+        if constexpr (QLds<D>::kTilesInLds) {
+          bhi = *reinterpret_cast<const f16x8*>(s_tiles + tb + lane * 8);
+          blo = *reinterpret_cast<const f16x8*>(s_tiles + tb + 512 + lane * 8);
+        } else {
+          bhi = *reinterpret_cast<const f16x8*>(a.dev.s_tiles + tb + lane * 8);
+          blo = *reinterpret_cast<const f16x8*>(a.dev.s_tiles + tb + 512 + lane * 8);
+        }
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[kt], bhi, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[kt], blo, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[kt], bhi, acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        uint64_t b = __ballot(acc[r] >= 0.f);
+        if (lane == 0) ballots[nt * 4 + r] = b;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
+
+    // ---- pack and store the key record
+    const int32_t slot = valid ? a.slot_mapping[t] : -1;
+    const bool store = valid && slot >= 0 && (int64_t)slot < a.slots_total;
+    uint8_t* base = a.pool + ((int64_t)(slot >> 4) * a.hkv + h) * a.rec;
+    const int s = slot & 15;
+    {
+      constexpr int CW = E * KB / 32;  // code dwords per lane
+      uint32_t w[CW];
+#pragma unroll
+      for (int i = 0; i < CW; ++i) w[i] = 0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int bp = e * KB;
+        w[bp / 32] |= idx[e] << (bp % 32);
+        if ((bp % 32) + KB > 32) w[bp / 32 + 1] |= idx[e] >> (32 - bp % 32);
+      }
+      uint32_t qw[SW];
+#pragma unroll
+      for (int i = 0; i < SW; ++i) {
+        uint32_t lo16 = (uint32_t)(ballots[(part * E / 16 + 2 * i) * 4 + (row & 3)] >> (16 * (row >> 2))) & 0xFFFFu;
+        uint32_t hi16 = (uint32_t)(ballots[(part * E / 16 + 2 * i + 1) * 4 + (row & 3)] >> (16 * (row >> 2))) & 0xFFFFu;
+        qw[i] = zero ? 0u : (lo16 | (hi16 << 16));
+      }
+      if (store) {
+        uint32_t* kc = reinterpret_cast<uint32_t*>(base + a.lay.kcodes + s * (KB * D / 8) + part * (KB * E / 8));
+#pragma unroll
+        for (int i = 0; i < CW; ++i) kc[i] = w[i];
+        uint32_t* kq = reinterpret_cast<uint32_t*>(base + a.lay.kqjl + s * (D / 8) + part * (E / 8));
+#pragma unroll
+        for (int i = 0; i < SW; ++i) kq[i] = qw[i];
+        if (part == 0) {
+          uint32_t meta = (uint32_t)f32_to_f16_bits(zero ? 0.f : n) | ((uint32_t)f32_to_f16_bits(gamma) << 16);
+          *reinterpret_cast<uint32_t*>(base + a.lay.kmeta + s * 4) = meta;
+        }
+      }
+    }
+
+    // ---- value: min-max group quantisation of this lane's E channels
+    if (valid) {
+      load_row_part<BF16>(a.v, th * D + part * E, x);
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) x[e] = 0.f;
+    }
+    constexpr int GL = E / 32;  // groups per lane
+    constexpr float LV = (float)((1 << VB) - 1);
+#pragma unroll
+    for (int gl = 0; gl < GL; ++gl) {
+      float mn = x[32 * gl], mx = x[32 * gl];
+#pragma unroll
+      for (int e = 1; e < 32; ++e) {
+        mn = fminf(mn, x[32 * gl + e]);
+        mx = fmaxf(mx, x[32 * gl + e]);
+      }
+      const uint16_t s16 = f32_to_f16_bits((mx - mn) / LV);
+      const uint16_t z16 = f32_to_f16_bits(mn);
+      const float sc = f16_bits_to_f32(s16), zz = f16_bits_to_f32(z16);
+      uint32_t vw[VB];
+#pragma unroll
+      for (int i = 0; i < VB; ++i) vw[i] = 0;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) {
+        float q = __builtin_rintf((x[32 * gl + e] - zz) / sc);
+        q = fminf(fmaxf(q, 0.f), LV);
+        uint32_t qi = (sc != 0.f) ? (uint32_t)q : 0u;
+        vw[(e * VB) / 32] |= qi << ((e * VB) % 32);
+      }
+      if (store) {
+        const int g = part * GL + gl;
+#pragma unroll
+        for (int i = 0; i < VB; ++i)
+          *reinterpret_cast<uint32_t*>(base + a.lay.vcodes + ((g * VB + i) * 16 + s) * 4) = vw[i];
+        *reinterpret_cast<uint32_t*>(base + a.lay.vmeta + (g * 16 + s) * 4) = (uint32_t)s16 | ((uint32_t)z16 << 16);
+      }
+    }
+  }
+}
+
+template <int D, int KB, int VB, bool BF16>
+static hipError_t launch_q(const QArgs& a, hipStream_t stream) {
+  auto kern = quantize_kernel<D, KB, VB, BF16>;
+  const size_t lds = QLds<D>::total;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)lds);
+  if (e != hipSuccess) return e;
+  int dev = 0, cus = 256;
+  (void)hipGetDevice(&dev);
+  (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  // persistent waves: one workgroup per CU (the LDS footprint allows no more)
+  int64_t want = (a.num_tiles + kQWaves<D> - 1) / kQWaves<D>;
+  int grid = (int)std::min<int64_t>(want, (int64_t)cus);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kQWaves<D> * 64), lds, stream, a);
+  return hipGetLastError();
+}
+
+template <int D, int KB, bool BF16>
+static hipError_t dispatch_vb(const QArgs& a, int vb, hipStream_t s) {
+  return vb == 2 ? launch_q<D, KB, 2, BF16>(a, s) : launch_q<D, KB, 4, BF16>(a, s);
+}
+
+template <int D, bool BF16>
+static hipError_t dispatch_kb(const QArgs& a, int kb, int vb, hipStream_t s) {
+  switch (kb) {
+    case 2: return dispatch_vb<D, 2, BF16>(a, vb, s);
+    case 3: return dispatch_vb<D, 3, BF16>(a, vb, s);
+    default: return dispatch_vb<D, 4, BF16>(a, vb, s);
+  }
+}
+
+hipError_t launch_quantize(const tq_ctx* c, const void* k, const void* v, int in_dtype, int64_t num_tokens,
+                           int num_kv_heads, const int32_t* slot_mapping, void* pool, int64_t num_blocks,
+                           hipStream_t stream) {
+  QArgs a;
+  a.k = k;
+  a.v = v;
+  a.num_th = num_tokens * num_kv_heads;
+  a.hkv = num_kv_heads;
+  a.slot_mapping = slot_mapping;
+  a.slots_total = num_blocks * 16;
+  a.pool = reinterpret_cast<uint8_t*>(pool);
+  a.rec = c->lay.bytes;
+  a.lay = c->lay;
+  a.dev = c->dev;
+  a.num_tiles = (a.num_th + 15) / 16;
+  const bool bf = in_dtype == TQ_DTYPE_BF16;
+  if (c->d == 128) return bf ? dispatch_kb<128, true>(a, c->kb, c->vb, stream) : dispatch_kb<128, false>(a, c->kb, c->vb, stream);
+  return bf ? dispatch_kb<256, true>(a, c->kb, c->vb, stream) : dispatch_kb<256, false>(a, c->kb, c->vb, stream);
+}
+
+}  // namespace tq

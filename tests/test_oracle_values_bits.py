@@ -127,15 +127,18 @@ def test_layout_roundtrip_with_random_slots():
     assert not pool[:, :2].any()  # other heads untouched
 
 
-def test_value_bytes_are_stored_byte_major():
+def test_value_bytes_are_stored_in_dword_columns():
     d, bk, bv = 128, 3, 4
     lay = paged.layout(d, bk, bv)
     pool = paged.new_pool(1, 1, lay)
     q = np.zeros((16, d), np.int64)
     q[3, 0], q[3, 1] = 0x7, 0xA  # slot 3, channels 0 and 1 -> byte 0 = 0xA7
+    q[5, 12], q[5, 13] = 0x3, 0x1  # slot 5, channels 12, 13 -> byte 6 = 0x13 (dword 1, byte 2)
     venc = {"q": q, "s16": np.zeros((16, 4), np.uint16), "z16": np.zeros((16, 4), np.uint16)}
     kenc = {"idx": np.zeros((16, d), np.int64), "sign": np.zeros((16, d), np.uint8),
             "n16": np.zeros(16, np.uint16), "g16": np.zeros(16, np.uint16)}
     paged.write_tokens(pool, np.arange(16), 0, kenc, venc, lay)
     off, _ = lay["vcodes"]
-    assert pool[0, 0, off + 0 * 16 + 3] == 0xA7
+    assert pool[0, 0, off + (0 * 16 + 3) * 4 + 0] == 0xA7
+    assert pool[0, 0, off + (1 * 16 + 5) * 4 + 2] == 0x13
+    assert np.count_nonzero(pool[0, 0, off:off + lay["vcodes"][1]]) == 2
