@@ -13,8 +13,9 @@ a multiple of 16 bytes:
   Kcodes  [16][b_k*d/8]   slot-major: the LSB-first code stream of each slot
   Kqjl    [16][d/8]       slot-major: the QJL sign bits of each slot
   Kmeta   [16][2] fp16    (n, gamma) of each slot
-  Vcodes  [b_v*d/8][16]   byte-major: byte f of every slot's value-code
-                          stream, for f = 0, 1, ... (a 16-row transpose)
+  Vcodes  [b_v*d/32][16][4]  dword-column-major: dword w (bytes 4w..4w+3)
+                          of every slot's value-code stream together, i.e.
+                          byte f of slot s at ((f // 4) * 16 + s) * 4 + f % 4
   Vmeta   [d/32][16][2]   fp16 (scale, zero) per (group, slot)
 
 Token t of sequence s lives in block ``block_table[s][t // 16]``, slot
@@ -55,12 +56,13 @@ def new_pool(num_blocks: int, num_kv_heads: int, lay: dict) -> np.ndarray:
 
 def _region_index(lay: dict, name: str, slots, width: int, slot_major: bool):
     """Byte offsets inside a record of ``width`` bytes per slot for each slot:
-    slot-major regions hold a slot's bytes contiguously, byte-major regions
-    hold byte f of every slot contiguously."""
+    slot-major regions hold a slot's bytes contiguously; dword-column regions
+    hold dword w of every slot contiguously (byte f of slot s at
+    ((f // 4) * 16 + s) * 4 + f % 4)."""
     o, _ = lay[name]
     s = np.asarray(slots, dtype=np.int64)[:, None]
     f = np.arange(width, dtype=np.int64)[None, :]
-    return o + (s * width + f if slot_major else f * BLOCK + s)
+    return o + (s * width + f if slot_major else ((f // 4) * BLOCK + s) * 4 + f % 4)
 
 
 def write_tokens(pool, slot_mapping, head: int, kenc: dict, venc: dict, lay: dict) -> None:
