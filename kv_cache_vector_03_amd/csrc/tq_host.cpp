@@ -496,7 +496,8 @@ DecodePlan tq::plan_decode(const tq_decode_args* a) {
   p.off_qt = 0;
   p.off_p = up(p.off_qt + 4 * nq * p.d);
   p.off_part = up(p.off_p + 4 * nq * p.d);
-  p.bytes = up(p.off_part + 4 * nq * (size_t)p.num_splits_max * (p.d + 2));
+  p.off_work = up(p.off_part + 4 * nq * (size_t)p.num_splits_max * (p.d + 2));
+  p.bytes = up(p.off_work + 4 * 2 * ((size_t)a->batch + 1));
   return p;
 }
 

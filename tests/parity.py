@@ -77,3 +77,40 @@ def compare_pools(gpu, expected, mask, select=None):
     outside = np.unpackbits(diff & ~m).sum()
     inside = np.unpackbits(diff & m).sum()
     return int(outside), int(inside)
+
+
+def oracle_cache(prm, d, kb, vb, lengths, Hkv, block_table, pool, seed, p=0.0, factor=20.0, seqs=None, kv=None):
+    """Encode seeded keys/values of every (sequence, KV head) with the oracle
+    and write them into ``pool`` through ``block_table``.  ``kv(b, h, L)``
+    overrides the generator.  Returns the fields per sequence (list over KV
+    heads) for the oracle's decode."""
+    lay = paged.layout(d, kb, vb)
+    fields = {}
+    for b in (range(len(lengths)) if seqs is None else seqs):
+        L = int(lengths[b])
+        per_head = []
+        for h in range(Hkv):
+            K, V = kv(b, h, L) if kv is not None else synth.seq_kv(seed, b, h, L, d, p, factor)
+            ke = keys.encode_keys(K.astype(np.float64), prm["d1"], prm["d2"], prm["S"], prm["c32"], prm["t32"])
+            ve = values.encode_values(V, vb)
+            t = np.arange(L)
+            slots = block_table[b][t // 16].astype(np.int64) * 16 + t % 16
+            paged.write_tokens(pool, slots, h, ke, ve, lay)
+            per_head.append({"idx": ke["idx"], "sign": ke["sign"], "n16": ke["n16"], "g16": ke["g16"],
+                             "q": ve["q"], "s16": ve["s16"], "z16": ve["z16"]})
+        fields[b] = per_head
+    return fields
+
+
+def score_errors(got, ref):
+    """max |got - ref| / max(|ref|, rms(ref row)) over a [rows, T] pair."""
+    rms = np.sqrt(np.mean(ref ** 2, axis=-1, keepdims=True))
+    return float(np.max(np.abs(got - ref) / np.maximum(np.maximum(np.abs(ref), rms), 1e-30)))
+
+
+def output_errors(got, ref):
+    """max over rows of ||got - ref|| / ||ref|| (rows with a zero reference
+    compare absolutely)."""
+    num = np.linalg.norm(got - ref, axis=-1)
+    den = np.linalg.norm(ref, axis=-1)
+    return float(np.max(np.where(den > 0, num / np.where(den > 0, den, 1), num)))
