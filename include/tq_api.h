@@ -178,7 +178,7 @@ typedef struct {
   const int32_t* recent_lens;/* device int32 [batch] in [0, recent_window], NULL iff recent_k is NULL */
   int32_t recent_window;
   float sm_scale;            /* <= 0 selects 1/sqrt(head_dim) */
-  int32_t chunk_tokens;      /* tokens per split, a multiple of 32 (fixed at capture) */
+  int32_t chunk_tokens;      /* tokens per split, a multiple of 32 in [32, 4096] (fixed at capture) */
   int32_t max_seq_len;       /* largest seq_lens entry allowed (sizes the workspace) */
   void* workspace;           /* device, tq_decode_workspace_bytes(args) bytes, 256-byte aligned */
   size_t workspace_bytes;
@@ -186,6 +186,9 @@ typedef struct {
   float* scores_out;         /* device fp32 [batch][num_q_heads][scores_stride] or NULL:
                                 raw scores, cached tokens first then recent ones */
   int32_t scores_stride;     /* >= max_seq_len + recent_window when scores_out != NULL */
+  void* split_events[2];     /* optional hipEvent_t pair (or NULLs): recorded on `stream`
+                                right before and right after the split launch(es), so a
+                                caller can time the streaming kernel alone */
 } tq_decode_args;
 
 /* Workspace bytes the decode call needs for these arguments (only the shape

@@ -63,7 +63,7 @@ class tq_decode_args(ctypes.Structure):
         ("recent_lens", ctypes.c_void_p), ("recent_window", ctypes.c_int32), ("sm_scale", ctypes.c_float),
         ("chunk_tokens", ctypes.c_int32), ("max_seq_len", ctypes.c_int32), ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t), ("out", ctypes.c_void_p), ("scores_out", ctypes.c_void_p),
-        ("scores_stride", ctypes.c_int32),
+        ("scores_stride", ctypes.c_int32), ("split_events", ctypes.c_void_p * 2),
     ]
 
 
@@ -240,7 +240,7 @@ def tq_quantize_store(ctx: Context, k, v, slot_mapping, pool, stream=None) -> No
 
 def _decode_args(q, ctxs, pools, block_tables, seq_lens, out, workspace=None, seq_preset=None, recent_k=None,
                  recent_v=None, recent_lens=None, sm_scale=0.0, chunk_tokens=512, max_seq_len=None,
-                 scores_out=None):
+                 scores_out=None, split_events=None):
     B, Hq, d = q.shape
     a = tq_decode_args()
     a.q = _ptr(q)
@@ -266,6 +266,8 @@ def _decode_args(q, ctxs, pools, block_tables, seq_lens, out, workspace=None, se
     a.out = _ptr(out)
     a.scores_out = _ptr(scores_out)
     a.scores_stride = scores_out.shape[-1] if scores_out is not None else 0
+    if split_events is not None:
+        a.split_events[0], a.split_events[1] = split_events
     return a
 
 
@@ -283,6 +285,7 @@ def tq_decode_attention(q, ctxs, pools, block_tables, seq_lens, out, workspace, 
     workspace: device uint8 tensor of tq_decode_workspace_bytes(...) bytes.
     Keyword arguments: seq_preset (int8 [B]), recent_k / recent_v (bf16
     [B, Hkv, W, d]) with recent_lens (int32 [B]), sm_scale, chunk_tokens,
-    max_seq_len, scores_out (float32 [B, Hq, stride])."""
+    max_seq_len, scores_out (float32 [B, Hq, stride]), split_events (a pair of
+    raw hipEvent_t handles recorded around the split launch)."""
     a = _decode_args(q, ctxs, pools, block_tables, seq_lens, out, workspace, **kw)
     _check(load().tq_decode_attention(ctypes.byref(a), _stream(stream)), "tq_decode_attention")

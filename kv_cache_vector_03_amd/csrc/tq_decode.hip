@@ -28,6 +28,7 @@
 //            group are kept at the end.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 
 #include "tq_common.hip.h"
@@ -57,6 +58,7 @@ struct DArgs {
   const int32_t* rlens;
   int W;
   float logit_scale;  // sm_scale * log2(e)
+  float inv_logit_scale;
   float sm_scale;
   int chunk;
   int splits_cap;
@@ -88,16 +90,17 @@ __device__ __forceinline__ int seq_preset_of(const DArgs& a, int b) {
 }
 
 // ---------------------------------------------------------------------------
-// prep: one workgroup of 256 threads per (sequence, query head); the last
-// workgroup enumerates the work items (its scan is 256 wide).
+// prep: one workgroup of 256 threads per (sequence, KV head) rotates the G
+// query heads of that KV head and projects them (S is read once for all G);
+// the last workgroup enumerates the work items (its scan is 256 wide).
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void decode_prep_kernel(DArgs a) {
-  __shared__ float s_x[D];
+  __shared__ __attribute__((aligned(16))) float s_x[kMaxG * D];
   __shared__ int s_cnt[256];
   const int tid = threadIdx.x;
-  const int nq = a.B * a.Hq;
-  if ((int)blockIdx.x == nq) {
+  const int nkv = a.B * a.Hkv;
+  if ((int)blockIdx.x == nkv) {
     // exclusive prefix sums of work items per preset
     for (int pr = 0; pr < 2; ++pr) {
       int carry = 0;
@@ -123,222 +126,357 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(DArgs a) {
     }
     return;
   }
-  const int b = blockIdx.x / a.Hq;
+  const int b = blockIdx.x / a.Hkv, hk = blockIdx.x % a.Hkv;
+  const int G = a.G;
   const int pr = seq_preset_of(a, b);
   const DevTables& dv = a.dev[pr];
-  const int64_t qoff = (int64_t)blockIdx.x * D;
-  for (int j = tid; j < D; j += blockDim.x) {
-    float v = a.q_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(a.q)[qoff + j])
-                       : reinterpret_cast<const float*>(a.q)[qoff + j];
-    s_x[j] = v * dv.signs1[j];
+  const int64_t q0 = ((int64_t)b * a.Hq + (int64_t)hk * G) * D;  // first query row of this KV head
+  for (int i = tid; i < G * D; i += 256) {
+    const int j = i % D;
+    float v = a.q_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(a.q)[q0 + i])
+                       : reinterpret_cast<const float*>(a.q)[q0 + i];
+    s_x[i] = v * dv.signs1[j];
   }
   __syncthreads();
-  for (int h = 1; h < D; h <<= 1) {
-    float nv[D / 256 + 1];
-    int c = 0;
-    for (int j = tid; j < D; j += blockDim.x, ++c) {
-      float x = s_x[j], y = s_x[j ^ h];
-      nv[c] = (j & h) ? (y - x) : (x + y);
+  for (int hs = 1; hs < D; hs <<= 1) {
+    for (int pi = tid; pi < G * (D / 2); pi += 256) {
+      const int g = pi / (D / 2), i = pi % (D / 2);
+      const int j = (i / hs) * 2 * hs + (i % hs);
+      float x = s_x[g * D + j], y = s_x[g * D + j + hs];
+      s_x[g * D + j] = x + y;
+      s_x[g * D + j + hs] = x - y;
     }
-    __syncthreads();
-    c = 0;
-    for (int j = tid; j < D; j += blockDim.x, ++c) s_x[j] = nv[c];
     __syncthreads();
   }
   const float inv = 1.0f / __builtin_sqrtf((float)D);
-  for (int j = tid; j < D; j += blockDim.x) {
-    float v = s_x[j] * inv * dv.signs2[j];
-    a.qt[qoff + j] = v;
+  for (int i = tid; i < G * D; i += 256) {
+    float v = s_x[i] * inv * dv.signs2[i % D];
+    s_x[i] = v;
+    a.qt[q0 + i] = v;
   }
   __syncthreads();
-  for (int j = tid; j < D; j += blockDim.x) s_x[j] = s_x[j] * inv * dv.signs2[j];
-  __syncthreads();
-  for (int i = tid; i < D; i += blockDim.x) {
-    const float* row = dv.S + (int64_t)i * D;
-    float acc = 0.f;
-    for (int j = 0; j < D; ++j) acc = __builtin_fmaf(row[j], s_x[j], acc);
-    a.pq[qoff + i] = acc;
+  // p[g][r] = sum_j S[r][j] q~[g][j]; thread r owns row r of S
+  for (int r = tid; r < D; r += 256) {
+    const f32x4* row = reinterpret_cast<const f32x4*>(dv.S + (int64_t)r * D);
+    float acc[kMaxG];
+#pragma unroll
+    for (int g = 0; g < kMaxG; ++g) acc[g] = 0.f;
+#pragma unroll 4
+    for (int j4 = 0; j4 < D / 4; ++j4) {
+      const f32x4 w = row[j4];
+#pragma unroll
+      for (int g = 0; g < kMaxG; ++g) {
+        if (g < G) {
+          const f32x4 x = *reinterpret_cast<const f32x4*>(s_x + g * D + 4 * j4);
+          acc[g] = __builtin_fmaf(w[0], x[0], acc[g]);
+          acc[g] = __builtin_fmaf(w[1], x[1], acc[g]);
+          acc[g] = __builtin_fmaf(w[2], x[2], acc[g]);
+          acc[g] = __builtin_fmaf(w[3], x[3], acc[g]);
+        }
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < kMaxG; ++g)
+      if (g < G) a.pq[q0 + (int64_t)g * D + r] = acc[g];
   }
 }
 
 // ---------------------------------------------------------------------------
 // split
 // ---------------------------------------------------------------------------
-template <int D, int GP>
-struct SplitLds {
-  static constexpr int kPairBytes = 256 * 8;           // largest pair table (4-bit codes)
-  static constexpr int kSignBytes = 256 * 16;           // byte -> 8 bf16 of +-1
-  static constexpr int kPBytes = kWaves * GP * 32 * 4;  // per-wave softmax weights
-  static constexpr int kMergeBytes = kWaves * GP * D * 4;
-  static constexpr int kStatBytes = kWaves * GP * 2 * 4;
-  static constexpr int total = kPairBytes + kSignBytes + kPBytes + kMergeBytes + kStatBytes;
+constexpr int kMaxChunk = 4096;  // largest chunk_tokens (block ids of a chunk are staged in LDS)
+
+// Compile-time geometry of one (block, KV head) record (the same byte layout
+// the host computes) and of one 32-token step = two records.
+template <int D, int KB, int VB>
+struct Rec {
+  static constexpr int kcodes = 0;
+  static constexpr int kqjl = kcodes + 16 * (KB * D / 8);
+  static constexpr int kmeta = kqjl + 16 * (D / 8);
+  static constexpr int vcodes = kmeta + 64;
+  static constexpr int vmeta = vcodes + (VB * D / 8) * 16;
+  static constexpr int bytes = vmeta + (D / 32) * 64;
+  static constexpr int pieces = 2 * bytes / 16;       // 16-byte pieces of a step
+  static constexpr int dma = (pieces + 63) / 64;      // LDS-DMA instructions per step
+  static constexpr int slot = dma * 1024;             // LDS bytes of one ring slot
+  static constexpr int nslot = D == 128 ? 3 : 2;      // ring depth (steps in flight + 1)
 };
 
-__device__ __forceinline__ uint32_t bf16_pair_bits(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+template <int D, int GP, int KB, int VB>
+struct SplitLds {
+  static_assert(Rec<D, KB, VB>::bytes % 16 == 0, "record size");
+  static constexpr int kPBytes = kWaves * GP * 32 * 4;  // per-wave softmax weights
+  static constexpr int kStatBytes = kWaves * GP * 2 * 4;
+  static constexpr int kBlkBytes = (kMaxChunk / 16 + 16) * 4;
+  static constexpr int kRingBytes = kWaves * Rec<D, KB, VB>::nslot * Rec<D, KB, VB>::slot;
+  static constexpr int kMergeBytes = kWaves * GP * D * 4;  // overlays the ring after the stream
+  static constexpr int kMainBytes = kRingBytes > kMergeBytes ? kRingBytes : kMergeBytes;
+  static constexpr int kMainOffset = kPBytes + kStatBytes + kBlkBytes;
+  static_assert(kMainOffset % 16 == 0, "ring alignment");
+  static constexpr int total = kMainOffset + kMainBytes;
+};
+
+// Row-wide (16-lane) reductions with DPP row rotations.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_ror(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, false));
 }
+__device__ __forceinline__ float row_sum16(float x) {
+  x += dpp_ror<0x128>(x);  // row_ror:8
+  x += dpp_ror<0x124>(x);  // row_ror:4
+  x += dpp_ror<0x122>(x);  // row_ror:2
+  x += dpp_ror<0x121>(x);  // row_ror:1
+  return x;
+}
+// Max over each 16-lane row of four values at once; the four chains are
+// interleaved so every DPP read is 3 instructions after its producer.
+__device__ __forceinline__ void row_max16x4(float& a, float& b, float& c, float& d) {
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_max_f32_dpp %0, %0, %0 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %1, %1, %1 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %2, %2, %2 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %3, %3, %3 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %0, %0, %0 row_ror:4 row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %1, %1, %1 row_ror:4 row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %2, %2, %2 row_ror:4 row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %3, %3, %3 row_ror:4 row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %0, %0, %0 row_ror:2 row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %1, %1, %1 row_ror:2 row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %2, %2, %2 row_ror:2 row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %3, %3, %3 row_ror:2 row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %0, %0, %0 row_ror:1 row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %1, %1, %1 row_ror:1 row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %2, %2, %2 row_ror:1 row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %3, %3, %3 row_ror:1 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1"
+      : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+}
+__device__ __forceinline__ float lane_swap32_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float lane_swap16_sum(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+// Wave-uniform copy of a 32-bit value, zero-extended when widened (the
+// builtin returns a signed int, which would sign-extend the low half of an
+// address).
+__device__ __forceinline__ uint32_t uniform_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)x);
+}
+// Direct global -> LDS copy of 16 bytes per lane: lane l's bytes land at LDS
+// byte address m0 + 16 l.  Issued as inline assembly so that the compiler does
+// not fence every later LDS read on it; completion is awaited explicitly with
+// wait_vmcnt below.
+__device__ __forceinline__ void dma16(uint32_t lds_byte_addr, uint64_t sbase, uint32_t voff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %1"
+      :
+      : "s"(uniform_u32(lds_byte_addr)),
+        "s"(((uint64_t)uniform_u32((uint32_t)(sbase >> 32)) << 32) | (uint64_t)uniform_u32((uint32_t)sbase)),
+        "v"(voff)
+      : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+// (y & mask) | c.  `c` is kept opaque to the compiler (see opaque_u32) so
+// that it selects one v_and_or_b32 instead of two literal-operand VOP2 ops;
+// the instruction stays compiler-generated so MFMA operand hazards are seen.
+__device__ __forceinline__ uint32_t and_or(uint32_t y, uint32_t mask, uint32_t c) { return (y & mask) | c; }
+__device__ __forceinline__ uint32_t opaque_u32(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory"); }
 
 template <int D, int GP, int KB, int VB>
-__device__ void split_cached_chunk(const DArgs& a, int pr, int b, int h, int t0, int t1, const uint32_t* s_pair,
-                                   const u32x4* s_sign, float* s_p, float* s_merge, float* s_stat,
-                                   const bf16x8 (&A1)[D / 32], const bf16x8 (&A3)[D / 32], float* m_out,
-                                   float* l_out) {
+__device__ void split_cached_chunk(const DArgs& a, int pr, int h, int t0, int t1, const int32_t* s_blk,
+                                   const uint2* s_pair, const uint2* s_sgn, float* s_p, unsigned char* s_main,
+                                   float* s_stat, const bf16x8 (&A1)[D / 32][2], const bf16x8 (&A3)[D / 32],
+                                   float* m_out, float* l_out, int b) {
+  using R = Rec<D, KB, VB>;
   constexpr int KT = D / 32;
-  constexpr int CS = D / 128;        // value column sets
-  constexpr int RT = GP / 4;         // value row tiles per column set
-  constexpr int CT = 8;              // value channel tiles per column set
-  constexpr int QB = KB * D / 32;    // code bytes per lane quarter
-  constexpr int QW = (QB + 3) / 4;   // code dwords per lane quarter
+  constexpr int CS = D / 128;      // value column sets
+  constexpr int RT = GP / 4;       // value row tiles per column set
+  constexpr int CT = 8;            // value channel tiles per column set
+  constexpr int QB = KB * D / 32;  // code bytes per lane quarter
+  constexpr int QW = (QB + 3) / 4;
+  constexpr int PPR = R::bytes / 16;          // 16-byte pieces per record
+  constexpr int DPR = (PPR + 63) / 64;        // DMA instructions per record
+  constexpr int DPS = 2 * DPR;                // DMA instructions per step
+  static_assert((R::nslot - 1) * DPS < 64, "vmcnt range");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tok = lane & 15, kq = lane >> 4;
   const uint8_t* pool = a.pool[pr];
-  const Layout lay = a.lay[pr];
   const int64_t rec = a.rec[pr];
-  const int32_t* btrow = a.bt + (int64_t)b * a.max_blocks;
+  const int64_t pblocks = a.pool_blocks[pr];
   const float kappa = 1.2533141373155003f / (float)D;  // sqrt(pi/2) / d
   float* sp = s_p + wave * GP * 32;
+  unsigned char* ring = s_main + wave * R::nslot * R::slot;
+  const uint32_t ring_lds = lds_offset(ring);
 
-  f32x4 accv[CS][RT][CT];
+  // per-lane byte offsets inside a record
+  const int off_kc = R::kcodes + tok * (KB * D / 8) + kq * QB;
+  const int off_kj = R::kqjl + tok * (D / 8) + kq * (D / 32);
+  const int off_km = R::kmeta + tok * 4;
+  const int slot0 = (kq & 1) * 8;
+  const int vhalf = kq >> 1;
+  int off_vx[CS], off_vm[CS];
+#pragma unroll
+  for (int cs = 0; cs < CS; ++cs) {
+    constexpr int WPS = VB == 4 ? 16 : 8;  // dword columns per column set
+    const int wcol = cs * WPS + (VB == 4 ? (lane & 15) : (lane & 7));
+    off_vx[cs] = vhalf * R::bytes + R::vcodes + (wcol * 16 + slot0) * 4;
+    off_vm[cs] = vhalf * R::bytes + R::vmeta + ((4 * cs + ((lane & 15) >> 2)) * 16 + slot0) * 4;
+  }
+
+  // Stream the two records of step `st` into ring slot `sl`: record r's piece
+  // k (16 bytes) lands at slot + r * bytes + 16 k; one DMA instruction per 64
+  // pieces, with the record base in SGPRs and a constant per-lane offset.
+  auto issue = [&](int st, int sl) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int blk = __builtin_amdgcn_readfirstlane(s_blk[2 * st + half]);
+      const bool ok = blk >= 0 && (int64_t)blk < pblocks;
+      const uint64_t base = reinterpret_cast<uint64_t>(pool + ((int64_t)(ok ? blk : 0) * a.Hkv + h) * rec);
+      const uint32_t dst = ring_lds + sl * R::slot + half * R::bytes;
+#pragma unroll
+      for (int j = 0; j < DPR; ++j) {
+        if (64 * j + 64 <= PPR || lane < PPR - 64 * j) dma16(dst + 1024 * j, base, 16 * (64 * j + lane));
+      }
+    }
+  };
+
+  f32x4 accv[CS][RT][CT], accb[CS][RT];
 #pragma unroll
   for (int cs = 0; cs < CS; ++cs)
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+    for (int rt = 0; rt < RT; ++rt) {
+      accb[cs][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) accv[cs][rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
   float zacc[CS][RT];
 #pragma unroll
   for (int cs = 0; cs < CS; ++cs)
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) zacc[cs][rt] = 0.f;
-  float m_run[GP], l_run[GP];
+  float m_run[GP];
 #pragma unroll
-  for (int g = 0; g < GP; ++g) {
-    m_run[g] = -INFINITY;
-    l_run[g] = 0.f;
+  for (int g = 0; g < GP; ++g) m_run[g] = -INFINITY;
+  float lsum[4] = {0.f, 0.f, 0.f, 0.f};  // per-lane partial sums (rows of lanes 0..31)
+  const bool hi_heads = GP == 8 && (lane & 16);  // lanes 16-31 carry heads 4..7 when GP = 8
+  const bool row_lane = lane < (GP == 8 ? 32 : 16);
+  const uint32_t c1024 = opaque_u32(0x64006400u);  // two fp16 1024.0
+  const f16x8 k1024 = __builtin_bit_cast(f16x8, u32x4{c1024, c1024, c1024, c1024});
+  const int arow = lane & 15;
+  // VB = 2: lane column j takes bytes 2 (j >> 3) and 2 (j >> 3) + 1 of its dword column
+  uint32_t vsel[2];
+#pragma unroll
+  for (int bb = 0; bb < 2; ++bb) {
+    const uint32_t by = 2u * (uint32_t)((lane & 15) >> 3) + (uint32_t)bb;
+    vsel[bb] = by | ((4u + by) << 16);
   }
 
-  const int nsteps = (t1 - t0 + 31) / 32;
-  for (int st = wave; st < nsteps; st += kWaves) {
-    const int sbase = t0 + st * 32;
+  auto compute = [&](const unsigned char* sb, int st) {
+    const int base = t0 + 32 * st;
+    const int blk0 = s_blk[2 * st], blk1 = s_blk[2 * st + 1];
+    const bool ok0 = blk0 >= 0 && (int64_t)blk0 < pblocks;
+    const bool ok1 = blk1 >= 0 && (int64_t)blk1 < pblocks;
+    const bool full = ok0 && ok1 && base + 32 <= t1;  // every token of the step is live
+    float xl[2][4];
     // ------------------------------------------------------------ scores
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      const int blk_tok = sbase + half * 16;
-      const int my_tok = blk_tok + tok;
-      const bool blk_live = blk_tok < t1;
-      int blk = blk_live ? btrow[blk_tok >> 4] : -1;
-      const bool blk_ok = blk >= 0 && (int64_t)blk < a.pool_blocks[pr];
-      const uint8_t* rbase = pool + ((int64_t)(blk_ok ? blk : 0) * a.Hkv + h) * rec;
-      uint32_t cw[QW + 1];
-      uint32_t qw[D / 128];
-      uint32_t meta = 0;
-#pragma unroll
-      for (int i = 0; i <= QW; ++i) cw[i] = 0;
-#pragma unroll
-      for (int i = 0; i < D / 128; ++i) qw[i] = 0;
-      if (blk_ok) {
-        const uint32_t* cp = reinterpret_cast<const uint32_t*>(rbase + lay.kcodes + tok * (KB * D / 8) + kq * QB);
-#pragma unroll
-        for (int i = 0; i < QW; ++i) cw[i] = cp[i];
-        const uint32_t* qp = reinterpret_cast<const uint32_t*>(rbase + lay.kqjl + tok * (D / 8) + kq * (D / 32));
-#pragma unroll
-        for (int i = 0; i < D / 128; ++i) qw[i] = qp[i];
-        meta = *reinterpret_cast<const uint32_t*>(rbase + lay.kmeta + tok * 4);
-      }
+      const unsigned char* hb = sb + half * R::bytes;
       f32x4 am = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
+      uint32_t cw[QW + 1];
+#pragma unroll
+      for (int i = 0; i < QW; ++i) cw[i] = *reinterpret_cast<const uint32_t*>(hb + off_kc + 4 * i);
+      cw[QW] = 0;
+      uint32_t kj[D / 128];
+#pragma unroll
+      for (int i = 0; i < D / 128; ++i) kj[i] = *reinterpret_cast<const uint32_t*>(hb + off_kj + 4 * i);
+      const uint32_t km = *reinterpret_cast<const uint32_t*>(hb + off_km);
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) {
-        // 8 codes of this tile: bits [8 kt KB, 8 kt KB + 8 KB) of the quarter
         constexpr int TB = 8 * KB;
         const int bp = kt * TB;
-        uint32_t win = bp % 32 == 0 ? cw[bp / 32] : __builtin_amdgcn_alignbit(cw[bp / 32 + 1], cw[bp / 32], bp % 32);
-        u32x4 bh, bl;
+        const uint32_t win =
+            bp % 32 == 0 ? cw[bp / 32] : __builtin_amdgcn_alignbit(cw[bp / 32 + 1], cw[bp / 32], bp % 32);
+        // pair entries {hi, lo}: MFMA m takes pairs 2m, 2m+1 (coordinates 4m .. 4m+3)
+        uint2 pe[4];
 #pragma unroll
-        for (int pi = 0; pi < 4; ++pi) {
-          uint32_t pidx = (win >> (2 * KB * pi)) & ((1u << (2 * KB)) - 1u);
-          if (KB == 4 && pi == 3) pidx = win >> 24;
-          const uint32_t* e = s_pair + 2 * pidx;
-          bh[pi] = e[0];
-          bl[pi] = e[1];
-        }
-        am = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1[kt], __builtin_bit_cast(bf16x8, bh), am, 0, 0, 0);
-        am = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1[kt], __builtin_bit_cast(bf16x8, bl), am, 0, 0, 0);
-        const uint32_t sbyte = (qw[kt / 4] >> (8 * (kt % 4))) & 0xFFu;
-        u32x4 bq = s_sign[sbyte];
+        for (int pi = 0; pi < 4; ++pi) pe[pi] = s_pair[(win >> (2 * KB * pi)) & ((1u << (2 * KB)) - 1u)];
+        const u32x4 b0 = {pe[0].x, pe[0].y, pe[1].x, pe[1].y};
+        const u32x4 b1 = {pe[2].x, pe[2].y, pe[3].x, pe[3].y};
+        am = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1[kt][0], __builtin_bit_cast(bf16x8, b0), am, 0, 0, 0);
+        am = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1[kt][1], __builtin_bit_cast(bf16x8, b1), am, 0, 0, 0);
+        const uint32_t sbyte = kj[kt / 4] >> (8 * (kt % 4));
+        const uint2 s_lo_n = s_sgn[sbyte & 15u], s_hi_n = s_sgn[(sbyte >> 4) & 15u];
+        const u32x4 bq = {s_lo_n.x, s_lo_n.y, s_hi_n.x, s_hi_n.y};
         aq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A3[kt], __builtin_bit_cast(bf16x8, bq), aq, 0, 0, 0);
       }
-      // rows: GP hi rows then GP lo rows -> sum hi + lo
-      f32x4 sm, sq;
+      // logit = log2(e) sm_scale n (q~.c + kappa gamma p.sign); the hi and lo
+      // rows of a head sit 16 (GP = 4) or 32 (GP = 8) lanes apart
+      const float n = f16_bits_to_f32((uint16_t)(km & 0xFFFFu)) * a.logit_scale;
+      const float nk = n * kappa * f16_bits_to_f32((uint16_t)(km >> 16));
+      const int my_tok = base + 16 * half + tok;
+      const bool live = full || ((half ? ok1 : ok0) && my_tok < t1);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        if constexpr (GP == 4) {
-          auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(am[r]), __float_as_uint(am[r]), false, false);
-          auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(aq[r]), __float_as_uint(aq[r]), false, false);
-          sm[r] = __uint_as_float(x[0]) + __uint_as_float(x[1]);
-          sq[r] = __uint_as_float(y[0]) + __uint_as_float(y[1]);
-        } else {
-          auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(am[r]), __float_as_uint(am[r]), false, false);
-          auto y = __builtin_amdgcn_permlane32_swap(__float_as_uint(aq[r]), __float_as_uint(aq[r]), false, false);
-          sm[r] = __uint_as_float(x[0]) + __uint_as_float(x[1]);
-          sq[r] = __uint_as_float(y[0]) + __uint_as_float(y[1]);
+        const float v = __builtin_fmaf(nk, aq[r], n * am[r]);
+        const float lg = GP == 4 ? lane_swap16_sum(v) : lane_swap32_sum(v);
+        if (a.scores && row_lane && live) {
+          const int hh = (hi_heads ? 4 : 0) + r;
+          if (hh < a.G) a.scores[((int64_t)b * a.Hq + h * a.G + hh) * a.scores_stride + my_tok] = lg * a.inv_logit_scale;
         }
-      }
-      const float n = f16_bits_to_f32((uint16_t)(meta & 0xFFFFu));
-      const float gm = f16_bits_to_f32((uint16_t)(meta >> 16));
-      const bool live = blk_ok && my_tok < t1;
-      // lanes 0-15 hold heads 0..3 (and, for GP = 8, lanes 16-31 heads 4..7)
-      const int hbase = (GP == 8 && (lane & 16)) ? 4 : 0;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float est = n * (sm[r] + kappa * gm * sq[r]);
-        if (lane < (GP == 8 ? 32 : 16)) {
-          const int hh = hbase + r;
-          if (hh < a.G && live && a.scores)
-            a.scores[((int64_t)b * a.Hq + h * a.G + hh) * a.scores_stride + my_tok] = est;
-          sp[hh * 32 + half * 16 + tok] = live ? est * a.logit_scale : -INFINITY;
-        }
+        xl[half][r] = live ? lg : -INFINITY;
       }
     }
-    __builtin_amdgcn_s_waitcnt(0xc07f);
-    __builtin_amdgcn_wave_barrier();
     // ------------------------------------------------------------ softmax
-    constexpr int LPH = 64 / GP;   // lanes per head
-    constexpr int VPL = 32 / LPH;  // values per lane
-    const int mh = lane / LPH, ml = lane % LPH;
-    float xs[VPL];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      xs[i] = sp[mh * 32 + ml * VPL + i];
-      mx = fmaxf(mx, xs[i]);
-    }
-    mx = group_max<LPH>(mx);
-    float m_new[GP], alpha[GP];
+    float y0 = fmaxf(xl[0][0], xl[1][0]), y1 = fmaxf(xl[0][1], xl[1][1]);
+    float y2 = fmaxf(xl[0][2], xl[1][2]), y3 = fmaxf(xl[0][3], xl[1][3]);
+    row_max16x4(y0, y1, y2, y3);
+    const float ys[4] = {y0, y1, y2, y3};
+    float m_new[GP], alpha[GP], m_sub[GP];
     bool rescale = false;
 #pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      m_new[r] = fmaxf(m_run[r], __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ys[r]), 0)));
+      if constexpr (GP == 8)
+        m_new[4 + r] = fmaxf(m_run[4 + r], __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ys[r]), 16)));
+    }
+#pragma unroll
     for (int g = 0; g < GP; ++g) {
-      const float mg = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mx), g * LPH));
-      m_new[g] = fmaxf(m_run[g], mg);
-      // a head with no live token yet keeps scale 1 (never -inf - -inf)
+      // a head with no live token yet keeps scale 1 and subtracts 0 (never -inf - -inf)
       alpha[g] = (m_new[g] == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[g] - m_new[g]);
+      m_sub[g] = (m_new[g] == -INFINITY) ? 0.f : m_new[g];
       rescale |= alpha[g] != 1.f;
-    }
-    float mym = m_new[0];
-#pragma unroll
-    for (int g = 1; g < GP; ++g) mym = (mh == g) ? m_new[g] : mym;
-    float lsum = 0.f;
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      float p = (mym == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(xs[i] - mym);
-      lsum += p;
-      sp[mh * 32 + ml * VPL + i] = p;
-    }
-    lsum = group_sum<LPH>(lsum);
-#pragma unroll
-    for (int g = 0; g < GP; ++g) {
-      float lg = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lsum), g * LPH));
-      l_run[g] = l_run[g] * alpha[g] + lg;
       m_run[g] = m_new[g];
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float ml = hi_heads ? m_sub[(4 + r) % GP] : m_sub[r];
+      const float al = hi_heads ? alpha[(4 + r) % GP] : alpha[r];
+      const float p0 = __builtin_amdgcn_exp2f(xl[0][r] - ml);
+      const float p1 = __builtin_amdgcn_exp2f(xl[1][r] - ml);
+      lsum[r] = __builtin_fmaf(lsum[r], al, p0 + p1);
+      if (row_lane) {
+        const int hh = (hi_heads ? 4 : 0) + r;
+        sp[hh * 32 + tok] = p0;
+        sp[hh * 32 + 16 + tok] = p1;
+      }
     }
     if (rescale) {
 #pragma unroll
@@ -346,152 +484,164 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int b, int h, int t0,
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
 #pragma unroll
-          for (int ct = 0; ct < CT; ++ct)
+          for (int r = 0; r < 4; ++r) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) accv[cs][rt][ct][r] *= alpha[4 * rt + r];
-          // zacc of row (group, head = 4 rt + (lane & 3))
+            for (int ct = 0; ct < CT; ++ct) accv[cs][rt][ct][r] *= alpha[4 * rt + r];
+            accb[cs][rt][r] *= alpha[4 * rt + r];
+          }
           float az = alpha[4 * rt];
 #pragma unroll
           for (int r = 1; r < 4; ++r) az = ((lane & 3) == r) ? alpha[4 * rt + r] : az;
           zacc[cs][rt] *= az;
         }
     }
-    __builtin_amdgcn_s_waitcnt(0xc07f);
-    __builtin_amdgcn_wave_barrier();
+    wait_lgkm0();  // the weights are in LDS
     // ------------------------------------------------------------ values
-    {
-      // lane: A row = lane & 15 -> (group 4 cs + row / 4, head 4 rt + row % 4),
-      // tokens 8 kq .. 8 kq + 7 of the step (block kq / 2, slots 8 (kq & 1) ..)
-      const int vblk_tok = sbase + (kq >> 1) * 16;
-      const bool vlive = vblk_tok < t1;
-      int vb = vlive ? btrow[vblk_tok >> 4] : -1;
-      const bool vok = vb >= 0 && (int64_t)vb < a.pool_blocks[pr];
-      const uint8_t* vbase = pool + ((int64_t)(vok ? vb : 0) * a.Hkv + h) * rec;
-      const int slot0 = (kq & 1) * 8;
-      const int arow = lane & 15;
-      float pw[8];
+    // fp16 MFMA: A = p s as fp16 hi + lo, B = 1024 + sigma q exactly (code bits
+    // or-ed into mantissa bits 4..7 of 1024, so sigma = 16, or 64 for the upper
+    // 2-bit field); the 1024 sum_t A_t bias comes from one MFMA against a
+    // constant 1024 tile.  Keeping the codes in the upper mantissa bits keeps
+    // the bias within a factor ~10 of the signal it is subtracted from.
+    const bool vblk_ok = vhalf ? ok1 : ok0;
+    const int vtok0 = base + 8 * kq;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pw[e] = 0.f;
+    for (int cs = 0; cs < CS; ++cs) {
+      const u32x4 x0 = *reinterpret_cast<const u32x4*>(sb + off_vx[cs]);
+      const u32x4 x1 = *reinterpret_cast<const u32x4*>(sb + off_vx[cs] + 16);
+      const u32x4 m0 = *reinterpret_cast<const u32x4*>(sb + off_vm[cs]);
+      const u32x4 m1 = *reinterpret_cast<const u32x4*>(sb + off_vm[cs] + 16);
+      const uint32_t xv[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+      uint32_t sz[8] = {m0[0], m0[1], m0[2], m0[3], m1[0], m1[1], m1[2], m1[3]};
+      if (!full) {
 #pragma unroll
-      for (int cs = 0; cs < CS; ++cs) {
-        // value code dwords of this lane's column for 8 slots
-        constexpr int WPS = VB == 4 ? 16 : 8;  // dword columns per column set
-        const int wcol = cs * WPS + (VB == 4 ? (lane & 15) : (lane & 7));
-        uint32_t xv[8];
-        if (vok) {
-          const u32x4* vp = reinterpret_cast<const u32x4*>(vbase + lay.vcodes + ((int64_t)wcol * 16 + slot0) * 4);
-          u32x4 v0 = vp[0], v1 = vp[1];
-          xv[0] = v0[0]; xv[1] = v0[1]; xv[2] = v0[2]; xv[3] = v0[3];
-          xv[4] = v1[0]; xv[5] = v1[1]; xv[6] = v1[2]; xv[7] = v1[3];
+        for (int e = 0; e < 8; ++e) sz[e] = (vblk_ok && (vtok0 + e) < t1) ? sz[e] : 0u;
+      }
+      // B tiles: byte-gather two tokens' code bytes into the halves of a dword
+      u32x4 bv[CT];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (VB == 4) {
+#pragma unroll
+          for (int bi = 0; bi < 4; ++bi) {
+            const uint32_t y = __builtin_amdgcn_perm(xv[2 * i + 1], xv[2 * i], (uint32_t)bi | ((uint32_t)(4 + bi) << 16));
+            bv[2 * bi][i] = and_or(y << 4, 0x00F000F0u, c1024);
+            bv[2 * bi + 1][i] = and_or(y, 0x00F000F0u, c1024);
+          }
         } else {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) xv[e] = 0;
-        }
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-          const int grp = 4 * cs + (arow >> 2);
-          const int hd = 4 * rt + (arow & 3);
-          uint32_t sz[8];
-          if (vok) {
-            const u32x4* mp = reinterpret_cast<const u32x4*>(vbase + lay.vmeta + ((int64_t)grp * 16 + slot0) * 4);
-            u32x4 m0 = mp[0], m1 = mp[1];
-            sz[0] = m0[0]; sz[1] = m0[1]; sz[2] = m0[2]; sz[3] = m0[3];
-            sz[4] = m1[0]; sz[5] = m1[1]; sz[6] = m1[2]; sz[7] = m1[3];
-          } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) sz[e] = 0;
-          }
-          const float* prow = sp + hd * 32 + 8 * kq;
-          u32x4 ah, al;
-#pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            float p0 = prow[e], p1 = prow[e + 1];
-            float s0 = f16_bits_to_f32((uint16_t)(sz[e] & 0xFFFFu)), z0 = f16_bits_to_f32((uint16_t)(sz[e] >> 16));
-            float s1 = f16_bits_to_f32((uint16_t)(sz[e + 1] & 0xFFFFu)), z1 = f16_bits_to_f32((uint16_t)(sz[e + 1] >> 16));
-            float w0 = p0 * s0, w1 = p1 * s1;
-            uint32_t h0 = f32_to_bf16_bits(w0), h1 = f32_to_bf16_bits(w1);
-            uint32_t l0 = f32_to_bf16_bits(w0 - __uint_as_float(h0 << 16));
-            uint32_t l1 = f32_to_bf16_bits(w1 - __uint_as_float(h1 << 16));
-            ah[e / 2] = h0 | (h1 << 16);
-            al[e / 2] = l0 | (l1 << 16);
-            // zero-points, minus exactly the +128 bias the MFMA adds with the
-            // split weights (hi + lo is exact in fp32)
-            const float a0 = __uint_as_float(h0 << 16) + __uint_as_float(l0 << 16);
-            const float a1 = __uint_as_float(h1 << 16) + __uint_as_float(l1 << 16);
-            zacc[cs][rt] = __builtin_fmaf(p0, z0, __builtin_fmaf(-128.f, a0, zacc[cs][rt]));
-            zacc[cs][rt] = __builtin_fmaf(p1, z1, __builtin_fmaf(-128.f, a1, zacc[cs][rt]));
-          }
-          const bf16x8 Ah = __builtin_bit_cast(bf16x8, ah), Al = __builtin_bit_cast(bf16x8, al);
-#pragma unroll
-          for (int ct = 0; ct < CT; ++ct) {
-            u32x4 bv;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              if constexpr (VB == 4) {
-                const int byte = ct >> 1, par = ct & 1;
-                uint32_t y = __builtin_amdgcn_perm(xv[2 * i + 1], xv[2 * i], 0x0C000C00u | (uint32_t)byte | ((uint32_t)(4 + byte) << 16));
-                bv[i] = ((par ? (y >> 4) : y) & 0x000F000Fu) | 0x43004300u;
-              } else {
-                const int bsel = 2 * ((lane & 15) >> 3) + (ct >> 2), sub = ct & 3;
-                uint32_t y = __builtin_amdgcn_perm(xv[2 * i + 1], xv[2 * i], 0x0C000C00u | (uint32_t)bsel | ((uint32_t)(4 + bsel) << 16));
-                bv[i] = ((y >> (2 * sub)) & 0x00030003u) | 0x43004300u;
-              }
-            }
-            const bf16x8 Bv = __builtin_bit_cast(bf16x8, bv);
-            accv[cs][rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ah, Bv, accv[cs][rt][ct], 0, 0, 0);
-            accv[cs][rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Al, Bv, accv[cs][rt][ct], 0, 0, 0);
+          for (int bb = 0; bb < 2; ++bb) {
+            const uint32_t y = __builtin_amdgcn_perm(xv[2 * i + 1], xv[2 * i], vsel[bb]);
+            bv[4 * bb + 0][i] = and_or(y << 4, 0x00300030u, c1024);
+            bv[4 * bb + 1][i] = and_or(y << 4, 0x00C000C0u, c1024);
+            bv[4 * bb + 2][i] = and_or(y, 0x00300030u, c1024);
+            bv[4 * bb + 3][i] = and_or(y, 0x00C000C0u, c1024);
           }
         }
       }
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const int hd = 4 * rt + (arow & 3);
+        const f32x4 pa = *reinterpret_cast<const f32x4*>(sp + hd * 32 + 8 * kq);
+        const f32x4 pb = *reinterpret_cast<const f32x4*>(sp + hd * 32 + 8 * kq + 4);
+        const float pw[8] = {pa[0], pa[1], pa[2], pa[3], pb[0], pb[1], pb[2], pb[3]};
+        f16x8 Ah, Al;
+        float z = zacc[cs][rt];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float sv = f16_bits_to_f32((uint16_t)(sz[e] & 0xFFFFu));
+          const _Float16 hv = (_Float16)(pw[e] * sv);
+          Ah[e] = hv;
+          Al[e] = (_Float16)__builtin_fmaf(pw[e], sv, -(float)hv);
+          z = __builtin_fmaf(pw[e], f16_bits_to_f32((uint16_t)(sz[e] >> 16)), z);
+        }
+        zacc[cs][rt] = z;
+        accb[cs][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, k1024, accb[cs][rt], 0, 0, 0);
+        accb[cs][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Al, k1024, accb[cs][rt], 0, 0, 0);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          const f16x8 B = __builtin_bit_cast(f16x8, bv[ct]);
+          accv[cs][rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, B, accv[cs][rt][ct], 0, 0, 0);
+          accv[cs][rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Al, B, accv[cs][rt][ct], 0, 0, 0);
+        }
+      }
     }
-    __builtin_amdgcn_s_waitcnt(0xc07f);
-    __builtin_amdgcn_wave_barrier();
+  };
+
+  // ---- the stream: this wave takes steps wave, wave + 4, ...; ring depth R::nslot
+  const int nsteps = (t1 - t0 + 31) / 32;
+  const int mine = wave < nsteps ? (nsteps - wave + kWaves - 1) / kWaves : 0;
+  const bool exact_wait = a.scores == nullptr;  // score stores also count in vmcnt
+#pragma unroll
+  for (int it = 0; it < R::nslot - 1; ++it)
+    if (it < mine) issue(wave + kWaves * it, it);
+  for (int it = 0; it < mine; ++it) {
+    const int ahead = min(R::nslot - 1, mine - 1 - it);  // steps already issued after this one
+    if (it + R::nslot - 1 < mine) {
+      wait_lgkm0();  // ring slot reuse: the reads of the step that used it are complete
+      issue(wave + kWaves * (it + R::nslot - 1), (it + R::nslot - 1) % R::nslot);
+    }
+    if (!exact_wait || ahead == 0)
+      wait_vmcnt<0>();
+    else if (ahead == 1)
+      wait_vmcnt<DPS>();
+    else
+      wait_vmcnt<(R::nslot - 1) * DPS>();
+    compute(ring + (it % R::nslot) * R::slot, wave + kWaves * it);
   }
+  wait_vmcnt<0>();
+  __syncthreads();  // every wave is done with the ring before it becomes the merge area
 
   // ---------------------------------------------------------------- merge
+  float* s_merge = reinterpret_cast<float*>(s_main);
   // zacc: sum the four token quarters (lanes l, l^16, l^32, l^48)
 #pragma unroll
   for (int cs = 0; cs < CS; ++cs)
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      float z = zacc[cs][rt];
-      z += __shfl_xor(z, 16, 64);
-      z += __shfl_xor(z, 32, 64);
-      zacc[cs][rt] = z;
-    }
+    for (int rt = 0; rt < RT; ++rt) zacc[cs][rt] = lane_swap16_sum(lane_swap32_sum(zacc[cs][rt]));
   float* mw = s_merge + wave * GP * D;
   // each wave writes its own un-normalised acc[head][channel]: output row
-  // (group l/16, head 4 rt + r) of column j is kept where the column's channel
-  // belongs to that group
+  // (group lane/16, head 4 rt + r) of column j is kept where the column's
+  // channel belongs to that group
+  const int j = lane & 15, gl = lane >> 4;
 #pragma unroll
   for (int cs = 0; cs < CS; ++cs)
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
+      for (int r = 0; r < 4; ++r) {
+        // zero-point term of row (group gl, head 4 rt + r) sits in A row 4 gl + r;
+        // the bias row-sum sits in this lane's own output row
+        const float zv = __shfl(zacc[cs][rt], 4 * gl + r, 64);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int j = lane & 15, gl = lane >> 4;
+        for (int ct = 0; ct < CT; ++ct) {
           int ch;
-          if constexpr (VB == 4)
+          float inv;  // 1 / sigma of the tile's field position
+          if constexpr (VB == 4) {
             ch = 128 * cs + 8 * j + 2 * (ct >> 1) + (ct & 1);
-          else
+            inv = 0.0625f;
+          } else {
             ch = 128 * cs + 16 * (j & 7) + 4 * (2 * (j >> 3) + (ct >> 2)) + (ct & 3);
-          const int grp_local = (ch >> 5) - 4 * cs;
-          // zero-point / bias term of row (group, head) sits in the lanes whose
-          // A row is 4 grp_local + r
-          const float zz = __shfl(zacc[cs][rt], 4 * grp_local + r, 64);
-          if (grp_local == gl) mw[(4 * rt + r) * D + ch] = accv[cs][rt][ct][r] + zz;
+            inv = (ct & 1) ? 0.015625f : 0.0625f;
+          }
+          if ((ch >> 5) - 4 * cs == gl)
+            mw[(4 * rt + r) * D + ch] = __builtin_fmaf(accv[cs][rt][ct][r] - accb[cs][rt][r], inv, zv);
         }
+      }
+  float lw[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) lw[r] = row_sum16(lsum[r]);
   if (lane == 0) {
 #pragma unroll
-    for (int g = 0; g < GP; ++g) {
-      s_stat[(wave * GP + g) * 2] = m_run[g];
-      s_stat[(wave * GP + g) * 2 + 1] = l_run[g];
-    }
+    for (int g = 0; g < GP; ++g) s_stat[(wave * GP + g) * 2] = m_run[g];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s_stat[(wave * GP + r) * 2 + 1] = lw[r];
+  }
+  if (GP == 8 && lane == 16) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s_stat[(wave * GP + 4 + r) * 2 + 1] = lw[r];
   }
   __syncthreads();
-  // combine the four waves; results for head g in m_out[g], l_out[g] and s_merge[0][g][:]
+  // combine the four waves; results for head g in m_out[g], l_out[g] and s_merge[g][:]
   const int tid = threadIdx.x;
   for (int idx = tid; idx < GP * D; idx += kWaves * 64) {
     const int g = idx / D;
@@ -501,11 +651,11 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int b, int h, int t0,
     float acc = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      float lw = s_stat[(w * GP + g) * 2 + 1];
-      float f = lw > 0.f ? __builtin_amdgcn_exp2f(s_stat[(w * GP + g) * 2] - M) : 0.f;
+      const float lwv = s_stat[(w * GP + g) * 2 + 1];
+      const float f = lwv > 0.f ? __builtin_amdgcn_exp2f(s_stat[(w * GP + g) * 2] - M) : 0.f;
       acc += f * s_merge[w * GP * D + idx];
     }
-    s_merge[idx] = acc;  // wave 0's slot is consumed in place (read above before write by this thread only)
+    s_merge[idx] = acc;  // each idx is read and written by this thread only
   }
   if (tid < GP) {
     float M = -INFINITY;
@@ -514,8 +664,8 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int b, int h, int t0,
     float L = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      float lw = s_stat[(w * GP + tid) * 2 + 1];
-      L += lw > 0.f ? lw * __builtin_amdgcn_exp2f(s_stat[(w * GP + tid) * 2] - M) : 0.f;
+      const float lwv = s_stat[(w * GP + tid) * 2 + 1];
+      L += lwv > 0.f ? lwv * __builtin_amdgcn_exp2f(s_stat[(w * GP + tid) * 2] - M) : 0.f;
     }
     m_out[tid] = L > 0.f ? M : -INFINITY;
     l_out[tid] = L;
@@ -577,26 +727,25 @@ template <int D, int GP, int KB, int VB>
 __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DArgs a, int pr) {
   constexpr int KT = D / 32;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-  uint32_t* s_pair = reinterpret_cast<uint32_t*>(lds);
-  u32x4* s_sign = reinterpret_cast<u32x4*>(lds + SplitLds<D, GP>::kPairBytes);
-  float* s_p = reinterpret_cast<float*>(lds + SplitLds<D, GP>::kPairBytes + SplitLds<D, GP>::kSignBytes);
-  float* s_merge = s_p + kWaves * GP * 32;
-  float* s_stat = s_merge + kWaves * GP * D;
+  using SL = SplitLds<D, GP, KB, VB>;
+  float* s_p = reinterpret_cast<float*>(lds);
+  float* s_stat = s_p + kWaves * GP * 32;
+  int32_t* s_blk = reinterpret_cast<int32_t*>(s_stat + kWaves * GP * 2);
+  unsigned char* s_main = lds + SL::kMainOffset;
+  float* s_merge = reinterpret_cast<float*>(s_main);
+  __shared__ uint2 s_pair[256];  // centroid pair -> {bf16 hi parts, bf16 lo parts}
+  __shared__ uint2 s_sgn[16];                // nibble -> 4 bf16 of +-1
   __shared__ float s_m[kMaxG], s_l[kMaxG];
   const int tid = threadIdx.x, lane = tid & 63;
 
-  // tables: centroid pairs of this preset, +-1 patterns of sign bytes
+  // tables: centroid pairs of this preset, +-1 patterns of sign nibbles
   const DevTables& dv = a.dev[pr];
-  for (int i = tid; i < (1 << (2 * KB)) * 2; i += kWaves * 64) s_pair[i] = dv.pair_lut[i];
-  for (int v = tid; v < 256; v += kWaves * 64) {
-    u32x4 w;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t lo = ((v >> (2 * i)) & 1) ? 0x3F80u : 0xBF80u;
-      uint32_t hi = ((v >> (2 * i + 1)) & 1) ? 0x3F80u : 0xBF80u;
-      w[i] = lo | (hi << 16);
-    }
-    s_sign[v] = w;
+  for (int i = tid; i < (1 << (2 * KB)); i += kWaves * 64) s_pair[i] = make_uint2(dv.pair_lut[2 * i], dv.pair_lut[2 * i + 1]);
+  if (tid < 16) {
+    uint2 w;
+    w.x = ((tid & 1) ? 0x3F80u : 0xBF80u) | (((tid & 2) ? 0x3F80u : 0xBF80u) << 16);
+    w.y = ((tid & 4) ? 0x3F80u : 0xBF80u) | (((tid & 8) ? 0x3F80u : 0xBF80u) << 16);
+    s_sgn[tid] = w;
   }
   __syncthreads();
 
@@ -618,40 +767,54 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DArgs a, int 
     const int nq_chunks = (Lc + a.chunk - 1) / a.chunk;
 
     if (c < nq_chunks) {
-      // A operands: rows 0..GP-1 = hi parts of head rows, GP..2GP-1 = lo parts
-      bf16x8 A1[KT], A3[KT];
+      const int t0 = c * a.chunk;
+      const int t1 = min(t0 + a.chunk, Lc);
+      // stage the chunk's block ids (-1 past its end)
+      {
+        const int nblk = (t1 - t0 + 15) >> 4;
+        const int32_t* btrow = a.bt + (int64_t)b * a.max_blocks + (t0 >> 4);
+        for (int i = tid; i < (a.chunk >> 4) + 2; i += kWaves * 64) s_blk[i] = i < nblk ? btrow[i] : -1;
+      }
+      // A operands: rows 0..GP-1 = hi parts of head rows, GP..2GP-1 = lo parts.
+      // A1[kt][m] slot e holds coordinate 8 kt + 4 m + {0,1,0,1,2,3,2,3}[e] of
+      // the lane quarter, matching the {hi pair, lo pair} B dwords; A3[kt] slot e
+      // holds coordinate 8 kt + e (sign bits in order).
+      bf16x8 A1[KT][2], A3[KT];
       {
         const int arow = lane & 15, kq = lane >> 4;
         const int g = arow % GP;
         const bool is_lo = arow >= GP;
         const bool used = arow < 2 * GP && g < a.G;
         const int64_t qo = ((int64_t)b * a.Hq + h * a.G + (used ? g : 0)) * D;
+        auto split = [&](float x) -> uint32_t {
+          const float v = used ? x : 0.f;
+          const uint32_t hb = f32_to_bf16_bits(v);
+          return is_lo ? f32_to_bf16_bits(v - __uint_as_float(hb << 16)) : hb;
+        };
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt) {
-          u32x4 w1, w3;
+          const int j0 = kq * (D / 4) + 8 * kt;
+          const f32x4 xa = *reinterpret_cast<const f32x4*>(a.qt + qo + j0);
+          const f32x4 xb = *reinterpret_cast<const f32x4*>(a.qt + qo + j0 + 4);
+          const f32x4 ya = *reinterpret_cast<const f32x4*>(a.pq + qo + j0);
+          const f32x4 yb = *reinterpret_cast<const f32x4*>(a.pq + qo + j0 + 4);
+          const float xs[8] = {xa[0], xa[1], xa[2], xa[3], xb[0], xb[1], xb[2], xb[3]};
+          const float ys[8] = {ya[0], ya[1], ya[2], ya[3], yb[0], yb[1], yb[2], yb[3]};
+          u32x4 w3;
 #pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            const int j = kq * (D / 4) + 8 * kt + e;
-            float x0 = used ? a.qt[qo + j] : 0.f, x1 = used ? a.qt[qo + j + 1] : 0.f;
-            float y0 = used ? a.pq[qo + j] : 0.f, y1 = used ? a.pq[qo + j + 1] : 0.f;
-            uint32_t hx0 = f32_to_bf16_bits(x0), hx1 = f32_to_bf16_bits(x1);
-            uint32_t hy0 = f32_to_bf16_bits(y0), hy1 = f32_to_bf16_bits(y1);
-            if (is_lo) {
-              hx0 = f32_to_bf16_bits(x0 - __uint_as_float(hx0 << 16));
-              hx1 = f32_to_bf16_bits(x1 - __uint_as_float(hx1 << 16));
-              hy0 = f32_to_bf16_bits(y0 - __uint_as_float(hy0 << 16));
-              hy1 = f32_to_bf16_bits(y1 - __uint_as_float(hy1 << 16));
-            }
-            w1[e / 2] = hx0 | (hx1 << 16);
-            w3[e / 2] = hy0 | (hy1 << 16);
-          }
-          A1[kt] = __builtin_bit_cast(bf16x8, w1);
+          for (int e = 0; e < 8; e += 2) w3[e / 2] = split(ys[e]) | (split(ys[e + 1]) << 16);
           A3[kt] = __builtin_bit_cast(bf16x8, w3);
+#pragma unroll
+          for (int m = 0; m < 2; ++m) {
+            const uint32_t c01 = split(xs[4 * m]) | (split(xs[4 * m + 1]) << 16);
+            const uint32_t c23 = split(xs[4 * m + 2]) | (split(xs[4 * m + 3]) << 16);
+            A1[kt][m] = __builtin_bit_cast(bf16x8, u32x4{c01, c01, c23, c23});
+          }
         }
       }
-      const int t0 = c * a.chunk;
-      const int t1 = min(t0 + a.chunk, Lc);
-      split_cached_chunk<D, GP, KB, VB>(a, pr, b, h, t0, t1, s_pair, s_sign, s_p, s_merge, s_stat, A1, A3, s_m, s_l);
+      __syncthreads();
+      split_cached_chunk<D, GP, KB, VB>(a, pr, h, t0, t1, s_blk, s_pair, s_sgn, s_p, s_main, s_stat, A1, A3,
+                                        s_m, s_l, b);
     } else {
       split_recent<D, GP>(a, b, h, seq_recent(a, b), s_p, s_merge, s_m, s_l);
     }
@@ -666,29 +829,53 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DArgs a, int 
 }
 
 // ---------------------------------------------------------------------------
-// combine: one workgroup of D threads per (sequence, query head)
+// combine: one workgroup per (sequence, query head).  Split weights
+// 2^(m_s - M) are formed once in LDS (splits with l = 0 are empty and weigh 0),
+// then each thread merges its channels.
 // ---------------------------------------------------------------------------
+constexpr int kCombineThreads = 128;
+constexpr int kCombineMaxSplits = 1024;
+
 template <int D>
-__global__ __launch_bounds__(256) void decode_combine_kernel(DArgs a) {
-  const int bh = blockIdx.x;
+__global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DArgs a) {
+  __shared__ float s_w[kCombineMaxSplits];
+  __shared__ float s_red[kCombineThreads];
+  const int bh = blockIdx.x, tid = threadIdx.x;
   const int b = bh / a.Hq;
-  const int ns = seq_splits(a, b);
+  const int ns = min(seq_splits(a, b), kCombineMaxSplits);
   const float* pp = a.part + (int64_t)bh * a.splits_cap * (D + 2);
-  float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) {
-    if (pp[s * (D + 2) + 1] > 0.f) M = fmaxf(M, pp[s * (D + 2)]);
+  float mx = -INFINITY;
+  for (int s = tid; s < ns; s += kCombineThreads) {
+    const float l = pp[(int64_t)s * (D + 2) + 1];
+    const float m = pp[(int64_t)s * (D + 2)];
+    if (l > 0.f) mx = fmaxf(mx, m);
   }
-  float L = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    float l = pp[s * (D + 2) + 1];
-    if (l > 0.f) L += l * __builtin_amdgcn_exp2f(pp[s * (D + 2)] - M);
+  s_red[tid] = mx;
+  __syncthreads();
+  for (int off = kCombineThreads / 2; off > 0; off >>= 1) {
+    if (tid < off) s_red[tid] = fmaxf(s_red[tid], s_red[tid + off]);
+    __syncthreads();
   }
-  for (int c = threadIdx.x; c < D; c += blockDim.x) {
+  const float M = s_red[0];
+  __syncthreads();
+  float lsum = 0.f;
+  for (int s = tid; s < ns; s += kCombineThreads) {
+    const float l = pp[(int64_t)s * (D + 2) + 1];
+    const float w = l > 0.f ? __builtin_amdgcn_exp2f(pp[(int64_t)s * (D + 2)] - M) : 0.f;
+    s_w[s] = w;
+    lsum = __builtin_fmaf(w, l, lsum);
+  }
+  s_red[tid] = lsum;
+  __syncthreads();
+  for (int off = kCombineThreads / 2; off > 0; off >>= 1) {
+    if (tid < off) s_red[tid] += s_red[tid + off];
+    __syncthreads();
+  }
+  const float L = s_red[0];
+  for (int c = tid; c < D; c += kCombineThreads) {
     float acc = 0.f;
-    for (int s = 0; s < ns; ++s) {
-      float l = pp[s * (D + 2) + 1];
-      if (l > 0.f) acc += __builtin_amdgcn_exp2f(pp[s * (D + 2)] - M) * pp[s * (D + 2) + 2 + c];
-    }
+#pragma unroll 4
+    for (int s = 0; s < ns; ++s) acc = __builtin_fmaf(s_w[s], pp[(int64_t)s * (D + 2) + 2 + c], acc);
     a.out[(int64_t)bh * D + c] = L > 0.f ? acc / L : 0.f;
   }
 }
@@ -697,9 +884,9 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DArgs a) {
 template <int D, int GP, int KB, int VB>
 static hipError_t launch_split(const DArgs& a, int pr, hipStream_t s) {
   auto kern = decode_split_kernel<D, GP, KB, VB>;
-  size_t lds = SplitLds<D, GP>::total;
-  size_t recent_need = (size_t)(GP * a.W + GP * D) * 4 + SplitLds<D, GP>::kPairBytes + SplitLds<D, GP>::kSignBytes +
-                       SplitLds<D, GP>::kPBytes + SplitLds<D, GP>::kStatBytes;
+  using SL = SplitLds<D, GP, KB, VB>;
+  size_t lds = SL::total;
+  const size_t recent_need = SL::kMainOffset + (size_t)(GP * a.W + GP * D) * 4;
   if (recent_need > lds) lds = recent_need;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);
@@ -707,7 +894,9 @@ static hipError_t launch_split(const DArgs& a, int pr, hipStream_t s) {
   int dev = 0, cus = 256;
   (void)hipGetDevice(&dev);
   (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  hipLaunchKernelGGL(kern, dim3(cus * 8), dim3(kWaves * 64), lds, s, a, pr);
+  // persistent workgroups: as many as fit on the chip at once (LDS bounds it)
+  const int per_cu = std::max(1, std::min(8, (int)((160 * 1024) / lds)));
+  hipLaunchKernelGGL(kern, dim3(cus * per_cu), dim3(kWaves * 64), lds, s, a, pr);
   return hipGetLastError();
 }
 
@@ -720,15 +909,17 @@ static hipError_t dispatch_preset(const DArgs& a, int pr, int kb, int vb, hipStr
 
 template <int D>
 static hipError_t launch_all(const DArgs& a, const tq_decode_args* args, hipStream_t s) {
-  hipLaunchKernelGGL(decode_prep_kernel<D>, dim3(a.B * a.Hq + 1), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(decode_prep_kernel<D>, dim3(a.B * a.Hkv + 1), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (args->split_events[0] && (e = hipEventRecord((hipEvent_t)args->split_events[0], s)) != hipSuccess) return e;
   for (int pr = 0; pr < args->num_presets; ++pr) {
     const tq_ctx* c = args->ctx[pr];
     e = a.G <= 4 ? dispatch_preset<D, 4>(a, pr, c->kb, c->vb, s) : dispatch_preset<D, 8>(a, pr, c->kb, c->vb, s);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(decode_combine_kernel<D>, dim3(a.B * a.Hq), dim3(D < 256 ? D : 256), 0, s, a);
+  if (args->split_events[1] && (e = hipEventRecord((hipEvent_t)args->split_events[1], s)) != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_combine_kernel<D>, dim3(a.B * a.Hq), dim3(kCombineThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -759,6 +950,7 @@ hipError_t launch_decode(const tq_decode_args* args, const DecodePlan& plan, hip
   a.W = args->recent_k ? args->recent_window : 0;
   a.sm_scale = args->sm_scale > 0.f ? args->sm_scale : 1.0f / std::sqrt((float)plan.d);
   a.logit_scale = a.sm_scale * 1.4426950408889634f;
+  a.inv_logit_scale = 1.f / a.logit_scale;
   a.chunk = args->chunk_tokens;
   a.splits_cap = plan.num_splits_max;
   char* ws = reinterpret_cast<char*>(args->workspace);

@@ -464,12 +464,17 @@ int check_decode_shape(const tq_decode_args* a) {
     set_error("decode: query heads per KV head %d > 8 is not supported", G);
     return TQ_EUNSUPPORTED;
   }
-  if (a->chunk_tokens < 32 || a->chunk_tokens % 32 || a->chunk_tokens > (1 << 20)) {
-    set_error("decode: chunk_tokens %d must be a positive multiple of 32", a->chunk_tokens);
+  if (a->chunk_tokens < 32 || a->chunk_tokens % 32 || a->chunk_tokens > 4096) {
+    set_error("decode: chunk_tokens %d must be a multiple of 32 in [32, 4096]", a->chunk_tokens);
     return TQ_EINVAL;
   }
   if (a->max_seq_len < 0 || a->max_blocks_per_seq < 0 || (int64_t)a->max_seq_len > 16ll * a->max_blocks_per_seq) {
     set_error("decode: max_seq_len %d exceeds 16 * max_blocks_per_seq %d", a->max_seq_len, a->max_blocks_per_seq);
+    return TQ_EINVAL;
+  }
+  if ((int64_t)(a->max_seq_len + a->chunk_tokens - 1) / a->chunk_tokens + 1 > 1024) {
+    set_error("decode: max_seq_len %d / chunk_tokens %d gives more than 1023 splits per sequence", a->max_seq_len,
+              a->chunk_tokens);
     return TQ_EINVAL;
   }
   if ((a->recent_k == nullptr) != (a->recent_v == nullptr) || (a->recent_k == nullptr) != (a->recent_lens == nullptr)) {

@@ -126,3 +126,17 @@ CONFIGS = {
     5: dict(name="decode-ragged-b64-hq32-hkv8-d128-k3v2|k4v4-recent128", d=128, Hq=32, Hkv=8, B=64,
             presets=((3, 2), (4, 4)), recent=128, seed=5, p=0.005, factor=20.0),
 }
+
+
+def torch_normal_bf16(shape, seed: int, device="cuda", p: float = 0.0, factor: float = 20.0):
+    """Seeded N(0, 1) bf16 tensor generated on the device (for the bench's
+    large inputs), each element scaled by ``factor`` with probability ``p``."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    if p > 0:
+        mask = torch.rand(shape, generator=g, device=device) < p
+        x = torch.where(mask, x * factor, x)
+    return x.to(torch.bfloat16)
