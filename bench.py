@@ -170,7 +170,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--chunk", type=int, default=512, help="tokens per decode split (fixed grid)")
+    ap.add_argument("--chunk", type=int, default=4096, help="tokens per decode split (fixed grid)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path shards by KV head or "
@@ -190,21 +190,30 @@ def main():
         decode_step(tq, s, i)
     torch.cuda.synchronize()
 
-    # timed region: K steps, split kernel bracketed by its own events each step
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    for a, b in evs:  # create the underlying HIP events
-        a.record()
-        b.record()
-    torch.cuda.synchronize()
+    # timed region: K steps of the whole path (store + decode), nothing else
+    # on the stream.
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
     for i in range(args.steps):
-        decode_step(tq, s, i, events=(evs[i][0].cuda_event, evs[i][1].cuda_event))
+        decode_step(tq, s, i)
     stop.record()
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(stop) / args.steps
+
+    # the same K steps again with the split (streaming) kernel bracketed by
+    # HIP events on its own stream each step, for its average launch duration
+    # (kept out of the step timing: an event record between launches adds a
+    # few microseconds of idle time to the step).
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in evs:  # create the underlying HIP events
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        decode_step(tq, s, i, events=(evs[i][0].cuda_event, evs[i][1].cuda_event))
+    torch.cuda.synchronize()
     split_ms = sorted(a.elapsed_time(b) for a, b in evs)
     split_avg = sum(split_ms) / len(split_ms)
     value = s["kv_bytes"] / (ms_step * 1e-3) / 1e12

@@ -149,35 +149,60 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(DArgs a) {
     __syncthreads();
   }
   const float inv = 1.0f / __builtin_sqrtf((float)D);
+  __shared__ uint32_t s_amax[kMaxG];
+  if (tid < kMaxG) s_amax[tid] = 0u;
+  __syncthreads();
   for (int i = tid; i < G * D; i += 256) {
     float v = s_x[i] * inv * dv.signs2[i % D];
     s_x[i] = v;
     a.qt[q0 + i] = v;
+    atomicMax(&s_amax[i / D], __float_as_uint(fabsf(v)));  // |v| bits order like the values
   }
   __syncthreads();
-  // p[g][r] = sum_j S[r][j] q~[g][j]; thread r owns row r of S
-  for (int r = tid; r < D; r += 256) {
-    const f32x4* row = reinterpret_cast<const f32x4*>(dv.S + (int64_t)r * D);
-    float acc[kMaxG];
+  // p[g][i] = sum_j S[i][j] q~[g][j] on the matrix cores: A rows = heads (fp16
+  // hi/lo of q~ 2^-e_g, with 2^e_g above the head's largest |q~_j| so fp16
+  // cannot overflow), B = the 16 S tiles of the context (fp16 hi/lo), three
+  // products per tile; each wave takes every fourth column tile.
+  {
+    constexpr int KT = D / 32, NT = D / 16;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int arow = lane & 15, kq = lane >> 4;
+    // power-of-two exponent per head: max |q~| < 2^e
+    auto head_exp = [&](int g) -> int {
+      const uint32_t m = s_amax[g];
+      return m == 0u ? 0 : (int)((m >> 23) & 0xFFu) - 126;
+    };
+    const float ascale = arow < G ? __builtin_ldexpf(1.0f, -head_exp(arow)) : 0.f;
+    f16x8 ahi[KT], alo[KT];
 #pragma unroll
-    for (int g = 0; g < kMaxG; ++g) acc[g] = 0.f;
-#pragma unroll 4
-    for (int j4 = 0; j4 < D / 4; ++j4) {
-      const f32x4 w = row[j4];
+    for (int kt = 0; kt < KT; ++kt) {
 #pragma unroll
-      for (int g = 0; g < kMaxG; ++g) {
-        if (g < G) {
-          const f32x4 x = *reinterpret_cast<const f32x4*>(s_x + g * D + 4 * j4);
-          acc[g] = __builtin_fmaf(w[0], x[0], acc[g]);
-          acc[g] = __builtin_fmaf(w[1], x[1], acc[g]);
-          acc[g] = __builtin_fmaf(w[2], x[2], acc[g]);
-          acc[g] = __builtin_fmaf(w[3], x[3], acc[g]);
-        }
+      for (int e = 0; e < 8; ++e) {
+        const float v = arow < G ? s_x[arow * D + 32 * kt + 8 * kq + e] * ascale : 0.f;
+        const _Float16 hv = (_Float16)v;
+        ahi[kt][e] = hv;
+        alo[kt][e] = (_Float16)(v - (float)hv);
       }
     }
+    const float unscale = 1.0f / (float)(1 << kSScaleLog2);
+    for (int nt = wave; nt < NT; nt += 4) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int g = 0; g < kMaxG; ++g)
-      if (g < G) a.pq[q0 + (int64_t)g * D + r] = acc[g];
+      for (int kt = 0; kt < KT; ++kt) {
+        const size_t tb = (((size_t)nt * KT + kt) * 2) * 64 * 8;
+        const f16x8 bhi = *reinterpret_cast<const f16x8*>(dv.s_tiles + tb + lane * 8);
+        const f16x8 blo = *reinterpret_cast<const f16x8*>(dv.s_tiles + tb + 512 + lane * 8);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[kt], bhi, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[kt], blo, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[kt], bhi, acc, 0, 0, 0);
+      }
+      // result row 4 (lane / 16) + r (a head), column lane % 16
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int g = 4 * kq + r;
+        if (g < G) a.pq[q0 + (int64_t)g * D + 16 * nt + arow] = __builtin_ldexpf(acc[r] * unscale, head_exp(g));
+      }
+    }
   }
 }
 

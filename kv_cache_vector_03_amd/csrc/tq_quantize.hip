@@ -301,6 +301,225 @@ __global__ __launch_bounds__(kQWaves<D> * 64) void quantize_kernel(QArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Small batches (a decode step stores one token per sequence): one wave per
+// token-head, lane l holding coordinates [P l, P l + P), P = d / 64, so every
+// elementwise stage is a few instructions per lane instead of d / 4.  The QJL
+// projection uses the same fp16 hi/lo operands, tiles and MFMA order as the
+// tiled kernel with the residual in row 0 of the A operand, so its sign bits
+// are identical to the tiled path's.
+// ---------------------------------------------------------------------------
+constexpr int kRowWaves = 4;
+constexpr int64_t kRowPathMaxTokenHeads = 2048;
+
+// P (2 or 4) consecutive elements of a bf16 or fp32 row.
+template <bool BF16, int P>
+__device__ __forceinline__ void load_few(const void* base, int64_t elem_off, float (&x)[P]) {
+  static_assert(P == 2 || P == 4, "row slice");
+  if constexpr (BF16) {
+    const uint16_t* p = reinterpret_cast<const uint16_t*>(base) + elem_off;
+    if constexpr (P == 2) {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
+      x[0] = __uint_as_float(w << 16);
+      x[1] = __uint_as_float(w & 0xFFFF0000u);
+    } else {
+      const uint2 w = *reinterpret_cast<const uint2*>(p);
+      x[0] = __uint_as_float(w.x << 16);
+      x[1] = __uint_as_float(w.x & 0xFFFF0000u);
+      x[2] = __uint_as_float(w.y << 16);
+      x[3] = __uint_as_float(w.y & 0xFFFF0000u);
+    }
+  } else {
+    const float* p = reinterpret_cast<const float*>(base) + elem_off;
+#pragma unroll
+    for (int e = 0; e < P; ++e) x[e] = p[e];
+  }
+}
+
+template <int D>
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m, 64);
+  return x;
+}
+
+template <int D, int KB, int VB, bool BF16>
+__global__ __launch_bounds__(kRowWaves * 64) void quantize_rows_kernel(QArgs a) {
+  constexpr int P = D / 64;
+  constexpr int L = 1 << KB;
+  constexpr int KT = D / 32, NT = D / 16;
+  constexpr float LV = (float)((1 << VB) - 1);
+  __shared__ float s_r[kRowWaves][D];
+  __shared__ uint8_t s_code[kRowWaves][D];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t th = (int64_t)blockIdx.x * kRowWaves + wave;
+  if (th >= a.num_th) return;  // whole wave
+  const int64_t t = th / a.hkv;
+  const int h = (int)(th - t * a.hkv);
+  const int j0 = lane * P;
+
+  // ---- key: norm, D1, Walsh-Hadamard, 1/sqrt(d) n, D2, Lloyd-Max index, residual
+  float x[P];
+  load_few<BF16, P>(a.k, th * D + j0, x);
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < P; ++e) ss = __builtin_fmaf(x[e], x[e], ss);
+  const float n = __builtin_sqrtf(wave_sum<D>(ss));
+  const bool zero = !(n > 0.f);
+#pragma unroll
+  for (int e = 0; e < P; ++e) x[e] *= a.dev.signs1[j0 + e];
+#pragma unroll
+  for (int hs = 1; hs < P; hs <<= 1) {
+#pragma unroll
+    for (int e = 0; e < P; ++e) {
+      if ((e & hs) == 0) {
+        const float p = x[e], q = x[e + hs];
+        x[e] = p + q;
+        x[e + hs] = p - q;
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const bool upper = (lane & m) != 0;
+#pragma unroll
+    for (int e = 0; e < P; ++e) {
+      const float y = __shfl_xor(x[e], m, 64);
+      x[e] = upper ? (y - x[e]) : (x[e] + y);
+    }
+  }
+  const float inv = zero ? 0.f : (1.0f / __builtin_sqrtf((float)D)) / n;
+  float r2 = 0.f;
+#pragma unroll
+  for (int e = 0; e < P; ++e) {
+    const float u = x[e] * inv * a.dev.signs2[j0 + e];
+    uint32_t c = 0;
+#pragma unroll
+    for (int i = 0; i < L - 1; ++i) c += (u > a.dev.thresholds[i]) ? 1u : 0u;
+    c = zero ? 0u : c;
+    const float r = zero ? 0.f : u - a.dev.centroids[c];
+    r2 = __builtin_fmaf(r, r, r2);
+    s_r[wave][j0 + e] = r * (float)(1 << kRScaleLog2);
+    s_code[wave][j0 + e] = (uint8_t)c;
+  }
+  const float gamma = __builtin_sqrtf(wave_sum<D>(r2));
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
+  __builtin_amdgcn_wave_barrier();
+
+  // ---- z = S r: row 0 of the A operand carries the scaled residual
+  f16x8 ahi[KT], alo[KT];
+  {
+    const bool row0 = (lane & 15) == 0;
+    const int kq = lane >> 4;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = row0 ? s_r[wave][32 * kt + 8 * kq + e] : 0.f;
+        const uint16_t hb = f32_to_f16_bits(v);
+        const uint16_t lb = f32_to_f16_bits(v - f16_bits_to_f32(hb));
+        ahi[kt][e] = __builtin_bit_cast(_Float16, hb);
+        alo[kt][e] = __builtin_bit_cast(_Float16, lb);
+      }
+    }
+  }
+  uint32_t qjl[D / 32];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+      const size_t tb = (((size_t)nt * KT + kt) * 2) * 64 * 8;
+      const f16x8 bhi = *reinterpret_cast<const f16x8*>(a.dev.s_tiles + tb + lane * 8);
+      const f16x8 blo = *reinterpret_cast<const f16x8*>(a.dev.s_tiles + tb + 512 + lane * 8);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[kt], bhi, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[kt], blo, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[kt], bhi, acc, 0, 0, 0);
+    }
+    // row 0 of the result sits in register 0 of lanes 0..15 (column = lane)
+    const uint32_t bits = (uint32_t)__ballot(acc[0] >= 0.f) & 0xFFFFu;
+    if (nt % 2 == 0)
+      qjl[nt / 2] = bits;
+    else
+      qjl[nt / 2] |= bits << 16;
+  }
+
+  // ---- store the key record
+  const int32_t slot = a.slot_mapping[t];
+  const bool store = slot >= 0 && (int64_t)slot < a.slots_total;
+  uint8_t* base = a.pool + ((int64_t)(slot >> 4) * a.hkv + h) * a.rec;
+  const int sl = slot & 15;
+  if (store) {
+    constexpr int CW = D * KB / 32;  // code dwords of the token
+    if (lane < CW) {
+      // dword `lane` holds bits [32 lane, 32 lane + 32) of the LSB-first code stream
+      uint32_t w = 0;
+      const int b0 = 32 * lane;
+      for (int j = b0 / KB; j * KB < b0 + 32; ++j) {
+        const int bp = j * KB - b0;
+        const uint32_t c = s_code[wave][j];
+        w |= bp >= 0 ? (c << bp) : (c >> (-bp));
+      }
+      *reinterpret_cast<uint32_t*>(base + a.lay.kcodes + sl * (KB * D / 8) + 4 * lane) = w;
+    }
+    if (lane < D / 32) {
+      uint32_t q = 0;
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i) q = (lane == i) ? qjl[i] : q;
+      *reinterpret_cast<uint32_t*>(base + a.lay.kqjl + sl * (D / 8) + 4 * lane) = zero ? 0u : q;
+    }
+    if (lane == 0) {
+      const uint32_t meta = (uint32_t)f32_to_f16_bits(zero ? 0.f : n) | ((uint32_t)f32_to_f16_bits(gamma) << 16);
+      *reinterpret_cast<uint32_t*>(base + a.lay.kmeta + sl * 4) = meta;
+    }
+  }
+
+  // ---- value: min-max quantisation of 32-channel groups (32 / P lanes each)
+  load_few<BF16, P>(a.v, th * D + j0, x);
+  constexpr int GLN = 32 / P;  // lanes per group
+  float mn = x[0], mx = x[0];
+#pragma unroll
+  for (int e = 1; e < P; ++e) {
+    mn = fminf(mn, x[e]);
+    mx = fmaxf(mx, x[e]);
+  }
+#pragma unroll
+  for (int m = 1; m < GLN; m <<= 1) {
+    mn = fminf(mn, __shfl_xor(mn, m, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, m, 64));
+  }
+  const uint16_t s16 = f32_to_f16_bits((mx - mn) / LV);
+  const uint16_t z16 = f32_to_f16_bits(mn);
+  const float sc = f16_bits_to_f32(s16), zz = f16_bits_to_f32(z16);
+  // this lane's codes placed at their bit positions inside their dword
+  constexpr int CPD = 32 / VB;  // codes per dword
+  uint32_t part = 0;
+#pragma unroll
+  for (int e = 0; e < P; ++e) {
+    float q = __builtin_rintf((x[e] - zz) / sc);
+    q = fminf(fmaxf(q, 0.f), LV);
+    const uint32_t qi = (sc != 0.f) ? (uint32_t)q : 0u;
+    part |= qi << (((j0 + e) % CPD) * VB);
+  }
+#pragma unroll
+  for (int m = 1; m < CPD / P; m <<= 1) part |= __shfl_xor(part, m, 64);
+  if (store) {
+    const int g = j0 / 32;             // group
+    const int i = (j0 % 32) / CPD;     // dword of the group
+    if ((j0 % CPD) == 0)
+      *reinterpret_cast<uint32_t*>(base + a.lay.vcodes + ((g * VB + i) * 16 + sl) * 4) = part;
+    if ((j0 % 32) == 0)
+      *reinterpret_cast<uint32_t*>(base + a.lay.vmeta + (g * 16 + sl) * 4) = (uint32_t)s16 | ((uint32_t)z16 << 16);
+  }
+}
+
+template <int D, int KB, int VB, bool BF16>
+static hipError_t launch_rows(const QArgs& a, hipStream_t stream) {
+  const int64_t grid = (a.num_th + kRowWaves - 1) / kRowWaves;
+  hipLaunchKernelGGL((quantize_rows_kernel<D, KB, VB, BF16>), dim3((unsigned)grid), dim3(kRowWaves * 64), 0, stream, a);
+  return hipGetLastError();
+}
+
 template <int D, int KB, int VB, bool BF16>
 static hipError_t launch_q(const QArgs& a, hipStream_t stream) {
   auto kern = quantize_kernel<D, KB, VB, BF16>;
@@ -320,6 +539,8 @@ static hipError_t launch_q(const QArgs& a, hipStream_t stream) {
 
 template <int D, int KB, bool BF16>
 static hipError_t dispatch_vb(const QArgs& a, int vb, hipStream_t s) {
+  if (a.num_th <= kRowPathMaxTokenHeads)
+    return vb == 2 ? launch_rows<D, KB, 2, BF16>(a, s) : launch_rows<D, KB, 4, BF16>(a, s);
   return vb == 2 ? launch_q<D, KB, 2, BF16>(a, s) : launch_q<D, KB, 4, BF16>(a, s);
 }
 

@@ -66,13 +66,35 @@ def test_bf16_d128_random_slots_ragged(kb, vb):
 
 @pytest.mark.parametrize("kb,vb", [(4, 4), (3, 2)])
 def test_bf16_d256(kb, vb):
-    T, Hkv, d = 301, 4, 256
+    T, Hkv, d = 601, 4, 256  # 2404 token-heads: the tiled kernel
     rng = np.random.default_rng([4, kb])
     K = synth.normal_with_outliers(rng, (T, Hkv, d), 0.005, 20.0)
     V = synth.normal_with_outliers(rng, (T, Hkv, d), 0.005, 20.0)
     nb = 40
     slots = rng.permutation(nb * 16)[:T]
     _check(K, V, d, kb, vb, slots, nb, torch.bfloat16, seed=4, label=f"d256 k{kb}v{vb}")
+
+
+# Small batches (up to 2048 token-heads) take the one-wave-per-token-head
+# kernel: a decode step's store of one token per sequence, and a few tokens.
+@pytest.mark.parametrize("d,kb,vb,T,Hkv,dtype", [
+    (128, 3, 4, 1, 8, torch.bfloat16),
+    (128, 3, 2, 32, 8, torch.bfloat16),
+    (128, 4, 4, 3, 8, torch.float32),
+    (128, 2, 2, 17, 2, torch.bfloat16),
+    (128, 4, 2, 256, 8, torch.bfloat16),
+    (256, 4, 4, 8, 4, torch.bfloat16),
+    (256, 3, 2, 5, 4, torch.float32),
+])
+def test_small_batch_store(d, kb, vb, T, Hkv, dtype):
+    rng = np.random.default_rng([11, d, kb, vb, T])
+    K = synth.normal_with_outliers(rng, (T, Hkv, d), 0.005, 20.0)
+    V = synth.normal_with_outliers(rng, (T, Hkv, d), 0.005, 20.0)
+    nb = max(2, (T + 15) // 16 * 2)
+    slots = rng.permutation(nb * 16)[:T].astype(np.int64)
+    if T > 2:
+        slots[1] = -1  # a skipped token
+    _check(K, V, d, kb, vb, slots, nb, dtype, seed=kb * 10 + vb, label=f"small d{d} k{kb}v{vb} T={T}x{Hkv}")
 
 
 def test_edge_rows_zero_keys_constant_groups_skipped_slots():
