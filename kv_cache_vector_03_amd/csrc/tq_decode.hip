@@ -131,48 +131,67 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(DArgs a) {
   const int pr = seq_preset_of(a, b);
   const DevTables& dv = a.dev[pr];
   const int64_t q0 = ((int64_t)b * a.Hq + (int64_t)hk * G) * D;  // first query row of this KV head
-  for (int i = tid; i < G * D; i += 256) {
-    const int j = i % D;
-    float v = a.q_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(a.q)[q0 + i])
-                       : reinterpret_cast<const float*>(a.q)[q0 + i];
-    s_x[i] = v * dv.signs1[j];
-  }
-  __syncthreads();
-  for (int hs = 1; hs < D; hs <<= 1) {
-    for (int pi = tid; pi < G * (D / 2); pi += 256) {
-      const int g = pi / (D / 2), i = pi % (D / 2);
-      const int j = (i / hs) * 2 * hs + (i % hs);
-      float x = s_x[g * D + j], y = s_x[g * D + j + hs];
-      s_x[g * D + j] = x + y;
-      s_x[g * D + j + hs] = x - y;
+  const int wave = tid >> 6, lane = tid & 63;
+  constexpr int P = D / 64;  // coordinates per lane: [P lane, P lane + P)
+  __shared__ int s_exp[kMaxG];
+
+  // q~ = D2 H D1 q / sqrt(d): wave w rotates heads w, w + 4 in registers
+  // (butterflies within a lane for the low index bits, across lanes by
+  // shuffles for the others).
+  for (int g = wave; g < G; g += 4) {
+    float x[P];
+#pragma unroll
+    for (int e = 0; e < P; ++e) {
+      const int j = P * lane + e;
+      const float v = a.q_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(a.q)[q0 + g * D + j])
+                               : reinterpret_cast<const float*>(a.q)[q0 + g * D + j];
+      x[e] = v * dv.signs1[j];
     }
-    __syncthreads();
+#pragma unroll
+    for (int hs = 1; hs < P; hs <<= 1) {
+#pragma unroll
+      for (int e = 0; e < P; ++e) {
+        if ((e & hs) == 0) {
+          const float p = x[e], q = x[e + hs];
+          x[e] = p + q;
+          x[e + hs] = p - q;
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      const bool upper = (lane & m) != 0;
+#pragma unroll
+      for (int e = 0; e < P; ++e) {
+        const float y = __shfl_xor(x[e], m, 64);
+        x[e] = upper ? (y - x[e]) : (x[e] + y);
+      }
+    }
+    const float inv = 1.0f / __builtin_sqrtf((float)D);
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < P; ++e) {
+      const int j = P * lane + e;
+      const float v = x[e] * inv * dv.signs2[j];
+      s_x[g * D + j] = v;
+      a.qt[q0 + g * D + j] = v;
+      amax = fmaxf(amax, fabsf(v));
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+    // power-of-two exponent with max |q~| < 2^e (0 for an all-zero head)
+    if (lane == 0) s_exp[g] = amax > 0.f ? (int)((__float_as_uint(amax) >> 23) & 0xFFu) - 126 : 0;
   }
-  const float inv = 1.0f / __builtin_sqrtf((float)D);
-  __shared__ uint32_t s_amax[kMaxG];
-  if (tid < kMaxG) s_amax[tid] = 0u;
   __syncthreads();
-  for (int i = tid; i < G * D; i += 256) {
-    float v = s_x[i] * inv * dv.signs2[i % D];
-    s_x[i] = v;
-    a.qt[q0 + i] = v;
-    atomicMax(&s_amax[i / D], __float_as_uint(fabsf(v)));  // |v| bits order like the values
-  }
-  __syncthreads();
+
   // p[g][i] = sum_j S[i][j] q~[g][j] on the matrix cores: A rows = heads (fp16
-  // hi/lo of q~ 2^-e_g, with 2^e_g above the head's largest |q~_j| so fp16
-  // cannot overflow), B = the 16 S tiles of the context (fp16 hi/lo), three
-  // products per tile; each wave takes every fourth column tile.
+  // hi/lo of q~ 2^-e_g so fp16 cannot overflow), B = the 16 S tiles of the
+  // context (fp16 hi/lo), three products per tile; wave w takes column tiles
+  // w, w + 4, ... with all its B tiles loaded up front.
   {
-    constexpr int KT = D / 32, NT = D / 16;
-    const int wave = tid >> 6, lane = tid & 63;
+    constexpr int KT = D / 32, NT = D / 16, NTW = NT / 4;
     const int arow = lane & 15, kq = lane >> 4;
-    // power-of-two exponent per head: max |q~| < 2^e
-    auto head_exp = [&](int g) -> int {
-      const uint32_t m = s_amax[g];
-      return m == 0u ? 0 : (int)((m >> 23) & 0xFFu) - 126;
-    };
-    const float ascale = arow < G ? __builtin_ldexpf(1.0f, -head_exp(arow)) : 0.f;
+    const float ascale = arow < G ? __builtin_ldexpf(1.0f, -s_exp[arow]) : 0.f;
     f16x8 ahi[KT], alo[KT];
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
@@ -184,23 +203,32 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(DArgs a) {
         alo[kt][e] = (_Float16)(v - (float)hv);
       }
     }
+    f16x8 bhi[NTW][KT], blo[NTW][KT];
+#pragma unroll
+    for (int i = 0; i < NTW; ++i) {
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        const size_t tb = ((((size_t)(wave + 4 * i)) * KT + kt) * 2) * 64 * 8;
+        bhi[i][kt] = *reinterpret_cast<const f16x8*>(dv.s_tiles + tb + lane * 8);
+        blo[i][kt] = *reinterpret_cast<const f16x8*>(dv.s_tiles + tb + 512 + lane * 8);
+      }
+    }
     const float unscale = 1.0f / (float)(1 << kSScaleLog2);
-    for (int nt = wave; nt < NT; nt += 4) {
+#pragma unroll
+    for (int i = 0; i < NTW; ++i) {
+      const int nt = wave + 4 * i;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) {
-        const size_t tb = (((size_t)nt * KT + kt) * 2) * 64 * 8;
-        const f16x8 bhi = *reinterpret_cast<const f16x8*>(dv.s_tiles + tb + lane * 8);
-        const f16x8 blo = *reinterpret_cast<const f16x8*>(dv.s_tiles + tb + 512 + lane * 8);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[kt], bhi, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[kt], blo, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[kt], bhi, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[kt], bhi[i][kt], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[kt], blo[i][kt], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[kt], bhi[i][kt], acc, 0, 0, 0);
       }
       // result row 4 (lane / 16) + r (a head), column lane % 16
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int g = 4 * kq + r;
-        if (g < G) a.pq[q0 + (int64_t)g * D + 16 * nt + arow] = __builtin_ldexpf(acc[r] * unscale, head_exp(g));
+        if (g < G) a.pq[q0 + (int64_t)g * D + 16 * nt + arow] = __builtin_ldexpf(acc[r] * unscale, s_exp[g]);
       }
     }
   }
@@ -326,7 +354,7 @@ __device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0
 
 template <int D, int GP, int KB, int VB>
 __device__ void split_cached_chunk(const DArgs& a, int pr, int h, int t0, int t1, const int32_t* s_blk,
-                                   const uint2* s_pair, const uint2* s_sgn, float* s_p, unsigned char* s_main,
+                                   const uint2* s_pair, const u32x4* s_sgn, float* s_p, unsigned char* s_main,
                                    float* s_stat, const bf16x8 (&A1)[D / 32][2], const bf16x8 (&A3)[D / 32],
                                    float* m_out, float* l_out, int b) {
   using R = Rec<D, KB, VB>;
@@ -345,7 +373,6 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h, int t0, int t1
   const uint8_t* pool = a.pool[pr];
   const int64_t rec = a.rec[pr];
   const int64_t pblocks = a.pool_blocks[pr];
-  const float kappa = 1.2533141373155003f / (float)D;  // sqrt(pi/2) / d
   float* sp = s_p + wave * GP * 32;
   unsigned char* ring = s_main + wave * R::nslot * R::slot;
   const uint32_t ring_lds = lds_offset(ring);
@@ -447,15 +474,15 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h, int t0, int t1
         const u32x4 b1 = {pe[2].x, pe[2].y, pe[3].x, pe[3].y};
         am = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1[kt][0], __builtin_bit_cast(bf16x8, b0), am, 0, 0, 0);
         am = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1[kt][1], __builtin_bit_cast(bf16x8, b1), am, 0, 0, 0);
-        const uint32_t sbyte = kj[kt / 4] >> (8 * (kt % 4));
-        const uint2 s_lo_n = s_sgn[sbyte & 15u], s_hi_n = s_sgn[(sbyte >> 4) & 15u];
-        const u32x4 bq = {s_lo_n.x, s_lo_n.y, s_hi_n.x, s_hi_n.y};
+        const u32x4 bq = s_sgn[(kj[kt / 4] >> (8 * (kt % 4))) & 0xFFu];
         aq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A3[kt], __builtin_bit_cast(bf16x8, bq), aq, 0, 0, 0);
       }
-      // logit = log2(e) sm_scale n (q~.c + kappa gamma p.sign); the hi and lo
-      // rows of a head sit 16 (GP = 4) or 32 (GP = 8) lanes apart
-      const float n = f16_bits_to_f32((uint16_t)(km & 0xFFFFu)) * a.logit_scale;
-      const float nk = n * kappa * f16_bits_to_f32((uint16_t)(km >> 16));
+      // logit = log2(e) sm_scale n (q~.c + kappa gamma p.sign), with
+      // log2(e) sm_scale folded into q~ and kappa log2(e) sm_scale into p (the
+      // A operands); the hi and lo rows of a head sit 16 (GP = 4) or 32
+      // (GP = 8) lanes apart
+      const float n = f16_bits_to_f32((uint16_t)(km & 0xFFFFu));
+      const float nk = n * f16_bits_to_f32((uint16_t)(km >> 16));
       const int my_tok = base + 16 * half + tok;
       const bool live = full || ((half ? ok1 : ok0) && my_tok < t1);
 #pragma unroll
@@ -470,40 +497,42 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h, int t0, int t1
       }
     }
     // ------------------------------------------------------------ softmax
-    float y0 = fmaxf(xl[0][0], xl[1][0]), y1 = fmaxf(xl[0][1], xl[1][1]);
-    float y2 = fmaxf(xl[0][2], xl[1][2]), y3 = fmaxf(xl[0][3], xl[1][3]);
+    // Each lane takes four distinct (head, token) logits: GP = 4: lanes 0-15
+    // the first 16 tokens, lanes 16-31 the second 16 (the swap-sum left every
+    // head row in both lane groups), lanes 32-63 idle; GP = 8: lanes 0-31 the
+    // first 16 tokens (heads 0-3 | 4-7), lanes 32-63 the second 16.
+    const int sh = GP == 4 ? ((lane >> 4) & 1) : (lane >> 5);
+    const bool act = GP == 8 || lane < 32;
+    float x[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) x[r] = act ? (sh ? xl[1][r] : xl[0][r]) : -INFINITY;
+    float y0 = x[0], y1 = x[1], y2 = x[2], y3 = x[3];
     row_max16x4(y0, y1, y2, y3);
     const float ys[4] = {y0, y1, y2, y3};
-    float m_new[GP], alpha[GP], m_sub[GP];
-    bool rescale = false;
+    float mt[GP];
+    bool grow = false;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      m_new[r] = fmaxf(m_run[r], __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ys[r]), 0)));
-      if constexpr (GP == 8)
-        m_new[4 + r] = fmaxf(m_run[4 + r], __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ys[r]), 16)));
-    }
-#pragma unroll
-    for (int g = 0; g < GP; ++g) {
-      // a head with no live token yet keeps scale 1 and subtracts 0 (never -inf - -inf)
-      alpha[g] = (m_new[g] == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[g] - m_new[g]);
-      m_sub[g] = (m_new[g] == -INFINITY) ? 0.f : m_new[g];
-      rescale |= alpha[g] != 1.f;
-      m_run[g] = m_new[g];
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float ml = hi_heads ? m_sub[(4 + r) % GP] : m_sub[r];
-      const float al = hi_heads ? alpha[(4 + r) % GP] : alpha[r];
-      const float p0 = __builtin_amdgcn_exp2f(xl[0][r] - ml);
-      const float p1 = __builtin_amdgcn_exp2f(xl[1][r] - ml);
-      lsum[r] = __builtin_fmaf(lsum[r], al, p0 + p1);
-      if (row_lane) {
-        const int hh = (hi_heads ? 4 : 0) + r;
-        sp[hh * 32 + tok] = p0;
-        sp[hh * 32 + 16 + tok] = p1;
+      const int yr = __float_as_int(ys[r]);
+      if constexpr (GP == 4) {
+        mt[r] = fmaxf(__int_as_float(__builtin_amdgcn_readlane(yr, 0)), __int_as_float(__builtin_amdgcn_readlane(yr, 16)));
+      } else {
+        mt[r] = fmaxf(__int_as_float(__builtin_amdgcn_readlane(yr, 0)), __int_as_float(__builtin_amdgcn_readlane(yr, 32)));
+        mt[4 + r] = fmaxf(__int_as_float(__builtin_amdgcn_readlane(yr, 16)), __int_as_float(__builtin_amdgcn_readlane(yr, 48)));
       }
     }
-    if (rescale) {
+#pragma unroll
+    for (int g = 0; g < GP; ++g) grow |= mt[g] > m_run[g];
+    if (grow) {  // uniform: some head's running max grew; rescale what was accumulated
+      float alpha[GP];
+#pragma unroll
+      for (int g = 0; g < GP; ++g) {
+        const float mn = fmaxf(m_run[g], mt[g]);
+        alpha[g] = __builtin_amdgcn_exp2f(m_run[g] - mn);  // 0 while m_run is -inf, 1 if unchanged
+        m_run[g] = mn;
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) lsum[r] *= hi_heads ? alpha[(4 + r) % GP] : alpha[r];
 #pragma unroll
       for (int cs = 0; cs < CS; ++cs)
 #pragma unroll
@@ -519,6 +548,16 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h, int t0, int t1
           for (int r = 1; r < 4; ++r) az = ((lane & 3) == r) ? alpha[4 * rt + r] : az;
           zacc[cs][rt] *= az;
         }
+    }
+    {
+      const int tokw = (lane & 15) + 16 * sh;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float mr = hi_heads ? m_run[(4 + r) % GP] : m_run[r];
+        const float p = __builtin_amdgcn_exp2f(x[r] - (mr == -INFINITY ? 0.f : mr));
+        lsum[r] += p;
+        if (act) sp[((hi_heads ? 4 : 0) + r) * 32 + tokw] = p;
+      }
     }
     wait_lgkm0();  // the weights are in LDS
     // ------------------------------------------------------------ values
@@ -574,7 +613,7 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h, int t0, int t1
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float sv = f16_bits_to_f32((uint16_t)(sz[e] & 0xFFFFu));
-          const _Float16 hv = (_Float16)(pw[e] * sv);
+          const _Float16 hv = (_Float16)__builtin_fmaf(pw[e], sv, 0.f);
           Ah[e] = hv;
           Al[e] = (_Float16)__builtin_fmaf(pw[e], sv, -(float)hv);
           z = __builtin_fmaf(pw[e], f16_bits_to_f32((uint16_t)(sz[e] >> 16)), z);
@@ -652,18 +691,24 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h, int t0, int t1
             mw[(4 * rt + r) * D + ch] = __builtin_fmaf(accv[cs][rt][ct][r] - accb[cs][rt][r], inv, zv);
         }
       }
-  float lw[4];
+  // l per head: row sums of the lane groups that held the head's two token halves
+  float lh[GP];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) lw[r] = row_sum16(lsum[r]);
+  for (int r = 0; r < 4; ++r) {
+    const int lw = __float_as_int(row_sum16(lsum[r]));
+    if constexpr (GP == 4) {
+      lh[r] = __int_as_float(__builtin_amdgcn_readlane(lw, 0)) + __int_as_float(__builtin_amdgcn_readlane(lw, 16));
+    } else {
+      lh[r] = __int_as_float(__builtin_amdgcn_readlane(lw, 0)) + __int_as_float(__builtin_amdgcn_readlane(lw, 32));
+      lh[4 + r] = __int_as_float(__builtin_amdgcn_readlane(lw, 16)) + __int_as_float(__builtin_amdgcn_readlane(lw, 48));
+    }
+  }
   if (lane == 0) {
 #pragma unroll
-    for (int g = 0; g < GP; ++g) s_stat[(wave * GP + g) * 2] = m_run[g];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) s_stat[(wave * GP + r) * 2 + 1] = lw[r];
-  }
-  if (GP == 8 && lane == 16) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) s_stat[(wave * GP + 4 + r) * 2 + 1] = lw[r];
+    for (int g = 0; g < GP; ++g) {
+      s_stat[(wave * GP + g) * 2] = m_run[g];
+      s_stat[(wave * GP + g) * 2 + 1] = lh[g];
+    }
   }
   __syncthreads();
   // combine the four waves; results for head g in m_out[g], l_out[g] and s_merge[g][:]
@@ -759,18 +804,19 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DArgs a, int 
   unsigned char* s_main = lds + SL::kMainOffset;
   float* s_merge = reinterpret_cast<float*>(s_main);
   __shared__ uint2 s_pair[256];  // centroid pair -> {bf16 hi parts, bf16 lo parts}
-  __shared__ uint2 s_sgn[16];                // nibble -> 4 bf16 of +-1
+  __shared__ u32x4 s_sgn[256];               // sign byte -> 8 bf16 of +-1 (bit i -> element i)
   __shared__ float s_m[kMaxG], s_l[kMaxG];
   const int tid = threadIdx.x, lane = tid & 63;
 
   // tables: centroid pairs of this preset, +-1 patterns of sign nibbles
   const DevTables& dv = a.dev[pr];
   for (int i = tid; i < (1 << (2 * KB)); i += kWaves * 64) s_pair[i] = make_uint2(dv.pair_lut[2 * i], dv.pair_lut[2 * i + 1]);
-  if (tid < 16) {
-    uint2 w;
-    w.x = ((tid & 1) ? 0x3F80u : 0xBF80u) | (((tid & 2) ? 0x3F80u : 0xBF80u) << 16);
-    w.y = ((tid & 4) ? 0x3F80u : 0xBF80u) | (((tid & 8) ? 0x3F80u : 0xBF80u) << 16);
-    s_sgn[tid] = w;
+  {
+    u32x4 w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = (((tid >> (2 * e)) & 1) ? 0x3F80u : 0xBF80u) | ((((tid >> (2 * e + 1)) & 1) ? 0x3F80u : 0xBF80u) << 16);
+    s_sgn[tid] = w;  // 256 threads, one entry each
   }
   __syncthreads();
 
@@ -811,6 +857,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DArgs a, int 
         const bool is_lo = arow >= GP;
         const bool used = arow < 2 * GP && g < a.G;
         const int64_t qo = ((int64_t)b * a.Hq + h * a.G + (used ? g : 0)) * D;
+        const float kappa = 1.2533141373155003f / (float)D;  // sqrt(pi/2) / d
         auto split = [&](float x) -> uint32_t {
           const float v = used ? x : 0.f;
           const uint32_t hb = f32_to_bf16_bits(v);
@@ -827,12 +874,14 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DArgs a, int 
           const float ys[8] = {ya[0], ya[1], ya[2], ya[3], yb[0], yb[1], yb[2], yb[3]};
           u32x4 w3;
 #pragma unroll
-          for (int e = 0; e < 8; e += 2) w3[e / 2] = split(ys[e]) | (split(ys[e + 1]) << 16);
+          for (int e = 0; e < 8; e += 2)
+            w3[e / 2] = split(ys[e] * (kappa * a.logit_scale)) | (split(ys[e + 1] * (kappa * a.logit_scale)) << 16);
           A3[kt] = __builtin_bit_cast(bf16x8, w3);
 #pragma unroll
           for (int m = 0; m < 2; ++m) {
-            const uint32_t c01 = split(xs[4 * m]) | (split(xs[4 * m + 1]) << 16);
-            const uint32_t c23 = split(xs[4 * m + 2]) | (split(xs[4 * m + 3]) << 16);
+            const float ls = a.logit_scale;
+            const uint32_t c01 = split(xs[4 * m] * ls) | (split(xs[4 * m + 1] * ls) << 16);
+            const uint32_t c23 = split(xs[4 * m + 2] * ls) | (split(xs[4 * m + 3] * ls) << 16);
             A1[kt][m] = __builtin_bit_cast(bf16x8, u32x4{c01, c01, c23, c23});
           }
         }

@@ -305,9 +305,10 @@ __global__ __launch_bounds__(kQWaves<D> * 64) void quantize_kernel(QArgs a) {
 // Small batches (a decode step stores one token per sequence): one wave per
 // token-head, lane l holding coordinates [P l, P l + P), P = d / 64, so every
 // elementwise stage is a few instructions per lane instead of d / 4.  The QJL
-// projection uses the same fp16 hi/lo operands, tiles and MFMA order as the
-// tiled kernel with the residual in row 0 of the A operand, so its sign bits
-// are identical to the tiled path's.
+// projection of a workgroup's four token-heads is one [4 x d] x [d x d]
+// product (A rows 0..3) whose column tiles are shared out over the four
+// waves; it uses the same fp16 hi/lo operands, tiles and MFMA order as the
+// tiled kernel, so its sign bits are identical to the tiled path's.
 // ---------------------------------------------------------------------------
 constexpr int kRowWaves = 4;
 constexpr int64_t kRowPathMaxTokenHeads = 2048;
@@ -351,23 +352,43 @@ __global__ __launch_bounds__(kRowWaves * 64) void quantize_rows_kernel(QArgs a) 
   constexpr float LV = (float)((1 << VB) - 1);
   __shared__ float s_r[kRowWaves][D];
   __shared__ uint8_t s_code[kRowWaves][D];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ uint32_t s_qjl[kRowWaves][D / 32];
+  __shared__ float s_cent[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t th = (int64_t)blockIdx.x * kRowWaves + wave;
-  if (th >= a.num_th) return;  // whole wave
-  const int64_t t = th / a.hkv;
-  const int h = (int)(th - t * a.hkv);
+  const bool valid = th < a.num_th;  // invalid waves still take part in the barriers
+  const int64_t t = valid ? th / a.hkv : 0;
+  const int h = valid ? (int)(th - t * a.hkv) : 0;
   const int j0 = lane * P;
 
+  // issue every independent load first
+  float x[P], vx[P], sg1[P], sg2[P], thr[L - 1];
+  int32_t slot = -1;
+  if (valid) {
+    load_few<BF16, P>(a.k, th * D + j0, x);
+    load_few<BF16, P>(a.v, th * D + j0, vx);
+    slot = a.slot_mapping[t];
+  } else {
+#pragma unroll
+    for (int e = 0; e < P; ++e) x[e] = vx[e] = 0.f;
+  }
+#pragma unroll
+  for (int e = 0; e < P; ++e) {
+    sg1[e] = a.dev.signs1[j0 + e];
+    sg2[e] = a.dev.signs2[j0 + e];
+  }
+#pragma unroll
+  for (int i = 0; i < L - 1; ++i) thr[i] = a.dev.thresholds[i];
+  if (tid < L) s_cent[tid] = a.dev.centroids[tid];
+
   // ---- key: norm, D1, Walsh-Hadamard, 1/sqrt(d) n, D2, Lloyd-Max index, residual
-  float x[P];
-  load_few<BF16, P>(a.k, th * D + j0, x);
   float ss = 0.f;
 #pragma unroll
   for (int e = 0; e < P; ++e) ss = __builtin_fmaf(x[e], x[e], ss);
   const float n = __builtin_sqrtf(wave_sum<D>(ss));
   const bool zero = !(n > 0.f);
 #pragma unroll
-  for (int e = 0; e < P; ++e) x[e] *= a.dev.signs1[j0 + e];
+  for (int e = 0; e < P; ++e) x[e] *= sg1[e];
 #pragma unroll
   for (int hs = 1; hs < P; hs <<= 1) {
 #pragma unroll
@@ -388,65 +409,73 @@ __global__ __launch_bounds__(kRowWaves * 64) void quantize_rows_kernel(QArgs a) 
       x[e] = upper ? (y - x[e]) : (x[e] + y);
     }
   }
+  __syncthreads();  // s_cent
   const float inv = zero ? 0.f : (1.0f / __builtin_sqrtf((float)D)) / n;
   float r2 = 0.f;
 #pragma unroll
   for (int e = 0; e < P; ++e) {
-    const float u = x[e] * inv * a.dev.signs2[j0 + e];
+    const float u = x[e] * inv * sg2[e];
     uint32_t c = 0;
 #pragma unroll
-    for (int i = 0; i < L - 1; ++i) c += (u > a.dev.thresholds[i]) ? 1u : 0u;
+    for (int i = 0; i < L - 1; ++i) c += (u > thr[i]) ? 1u : 0u;
     c = zero ? 0u : c;
-    const float r = zero ? 0.f : u - a.dev.centroids[c];
+    const float r = zero ? 0.f : u - s_cent[c];
     r2 = __builtin_fmaf(r, r, r2);
     s_r[wave][j0 + e] = r * (float)(1 << kRScaleLog2);
     s_code[wave][j0 + e] = (uint8_t)c;
   }
   const float gamma = __builtin_sqrtf(wave_sum<D>(r2));
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
-  __builtin_amdgcn_wave_barrier();
+  __syncthreads();  // every wave's residual is in LDS
 
-  // ---- z = S r: row 0 of the A operand carries the scaled residual
-  f16x8 ahi[KT], alo[KT];
+  // ---- z = S r for the workgroup's token-heads (A rows 0..3); wave w takes
+  // column tiles w, w + 4, ...
   {
-    const bool row0 = (lane & 15) == 0;
-    const int kq = lane >> 4;
+    const int arow = lane & 15, kq = lane >> 4;
+    f16x8 ahi[KT], alo[KT];
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float v = row0 ? s_r[wave][32 * kt + 8 * kq + e] : 0.f;
+        const float v = arow < kRowWaves ? s_r[arow][32 * kt + 8 * kq + e] : 0.f;
         const uint16_t hb = f32_to_f16_bits(v);
         const uint16_t lb = f32_to_f16_bits(v - f16_bits_to_f32(hb));
         ahi[kt][e] = __builtin_bit_cast(_Float16, hb);
         alo[kt][e] = __builtin_bit_cast(_Float16, lb);
       }
     }
-  }
-  uint32_t qjl[D / 32];
+    constexpr int NTW = NT / kRowWaves;
+    f16x8 bhi[NTW][KT], blo[NTW][KT];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < NTW; ++i) {
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
-      const size_t tb = (((size_t)nt * KT + kt) * 2) * 64 * 8;
-      const f16x8 bhi = *reinterpret_cast<const f16x8*>(a.dev.s_tiles + tb + lane * 8);
-      const f16x8 blo = *reinterpret_cast<const f16x8*>(a.dev.s_tiles + tb + 512 + lane * 8);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[kt], bhi, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[kt], blo, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[kt], bhi, acc, 0, 0, 0);
+      for (int kt = 0; kt < KT; ++kt) {
+        const size_t tb = ((((size_t)(wave + kRowWaves * i)) * KT + kt) * 2) * 64 * 8;
+        bhi[i][kt] = *reinterpret_cast<const f16x8*>(a.dev.s_tiles + tb + lane * 8);
+        blo[i][kt] = *reinterpret_cast<const f16x8*>(a.dev.s_tiles + tb + 512 + lane * 8);
+      }
     }
-    // row 0 of the result sits in register 0 of lanes 0..15 (column = lane)
-    const uint32_t bits = (uint32_t)__ballot(acc[0] >= 0.f) & 0xFFFFu;
-    if (nt % 2 == 0)
-      qjl[nt / 2] = bits;
-    else
-      qjl[nt / 2] |= bits << 16;
+#pragma unroll
+    for (int i = 0; i < NTW; ++i) {
+      const int nt = wave + kRowWaves * i;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[kt], bhi[i][kt], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[kt], blo[i][kt], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[kt], bhi[i][kt], acc, 0, 0, 0);
+      }
+      // result row r (token-head r of the group) sits in register r of lanes 0..15
+#pragma unroll
+      for (int r = 0; r < kRowWaves; ++r) {
+        const uint32_t bits = (uint32_t)__ballot(acc[r] >= 0.f) & 0xFFFFu;
+        if (lane == 0) reinterpret_cast<uint16_t*>(&s_qjl[r][0])[nt] = (uint16_t)bits;
+      }
+    }
   }
+  __syncthreads();
 
   // ---- store the key record
-  const int32_t slot = a.slot_mapping[t];
-  const bool store = slot >= 0 && (int64_t)slot < a.slots_total;
+  const bool store = valid && slot >= 0 && (int64_t)slot < a.slots_total;
   uint8_t* base = a.pool + ((int64_t)(slot >> 4) * a.hkv + h) * a.rec;
   const int sl = slot & 15;
   if (store) {
@@ -462,12 +491,8 @@ __global__ __launch_bounds__(kRowWaves * 64) void quantize_rows_kernel(QArgs a) 
       }
       *reinterpret_cast<uint32_t*>(base + a.lay.kcodes + sl * (KB * D / 8) + 4 * lane) = w;
     }
-    if (lane < D / 32) {
-      uint32_t q = 0;
-#pragma unroll
-      for (int i = 0; i < D / 32; ++i) q = (lane == i) ? qjl[i] : q;
-      *reinterpret_cast<uint32_t*>(base + a.lay.kqjl + sl * (D / 8) + 4 * lane) = zero ? 0u : q;
-    }
+    if (lane < D / 32)
+      *reinterpret_cast<uint32_t*>(base + a.lay.kqjl + sl * (D / 8) + 4 * lane) = zero ? 0u : s_qjl[wave][lane];
     if (lane == 0) {
       const uint32_t meta = (uint32_t)f32_to_f16_bits(zero ? 0.f : n) | ((uint32_t)f32_to_f16_bits(gamma) << 16);
       *reinterpret_cast<uint32_t*>(base + a.lay.kmeta + sl * 4) = meta;
@@ -475,13 +500,12 @@ __global__ __launch_bounds__(kRowWaves * 64) void quantize_rows_kernel(QArgs a) 
   }
 
   // ---- value: min-max quantisation of 32-channel groups (32 / P lanes each)
-  load_few<BF16, P>(a.v, th * D + j0, x);
   constexpr int GLN = 32 / P;  // lanes per group
-  float mn = x[0], mx = x[0];
+  float mn = vx[0], mx = vx[0];
 #pragma unroll
   for (int e = 1; e < P; ++e) {
-    mn = fminf(mn, x[e]);
-    mx = fmaxf(mx, x[e]);
+    mn = fminf(mn, vx[e]);
+    mx = fmaxf(mx, vx[e]);
   }
 #pragma unroll
   for (int m = 1; m < GLN; m <<= 1) {
@@ -496,7 +520,7 @@ __global__ __launch_bounds__(kRowWaves * 64) void quantize_rows_kernel(QArgs a) 
   uint32_t part = 0;
 #pragma unroll
   for (int e = 0; e < P; ++e) {
-    float q = __builtin_rintf((x[e] - zz) / sc);
+    float q = __builtin_rintf((vx[e] - zz) / sc);
     q = fminf(fmaxf(q, 0.f), LV);
     const uint32_t qi = (sc != 0.f) ? (uint32_t)q : 0u;
     part |= qi << (((j0 + e) % CPD) * VB);
