@@ -161,7 +161,7 @@ int tq_quantize_store(const tq_ctx* ctx, const void* k, const void* v, int32_t i
 typedef struct {
   const void* q;             /* device [batch][num_q_heads][head_dim], q_dtype */
   int32_t q_dtype;           /* TQ_DTYPE_BF16 or TQ_DTYPE_F32 */
-  int32_t batch;
+  int32_t batch;             /* 0 .. 8192 */
   int32_t num_q_heads;
   int32_t num_kv_heads;      /* num_q_heads % num_kv_heads == 0, G <= 8 */
   int32_t num_presets;       /* 1 or 2 */

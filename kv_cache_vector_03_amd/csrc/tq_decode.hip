@@ -31,6 +31,8 @@
 #include <algorithm>
 #include <cmath>
 
+#include <type_traits>
+
 #include "tq_common.hip.h"
 #include "tq_internal.h"
 
@@ -62,10 +64,7 @@ struct DArgs {
   float sm_scale;
   int chunk;
   int splits_cap;
-  float* qt;     // [B][Hq][D]
-  float* pq;     // [B][Hq][D]
   float* part;   // [B][Hq][splits_cap][D + 2]
-  int32_t* work; // [2][B + 1]
   float* out;
   float* scores;
   int scores_stride;
@@ -87,151 +86,6 @@ __device__ __forceinline__ int seq_splits(const DArgs& a, int b) {
 }
 __device__ __forceinline__ int seq_preset_of(const DArgs& a, int b) {
   return a.seq_preset ? (a.seq_preset[b] != 0 ? 1 : 0) : 0;
-}
-
-// ---------------------------------------------------------------------------
-// prep: one workgroup of 256 threads per (sequence, KV head) rotates the G
-// query heads of that KV head and projects them (S is read once for all G);
-// the last workgroup enumerates the work items (its scan is 256 wide).
-// ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void decode_prep_kernel(DArgs a) {
-  __shared__ __attribute__((aligned(16))) float s_x[kMaxG * D];
-  __shared__ int s_cnt[256];
-  const int tid = threadIdx.x;
-  const int nkv = a.B * a.Hkv;
-  if ((int)blockIdx.x == nkv) {
-    // exclusive prefix sums of work items per preset
-    for (int pr = 0; pr < 2; ++pr) {
-      int carry = 0;
-      for (int base = 0; base < a.B; base += 256) {
-        int b = base + tid;
-        int items = 0;
-        if (b < a.B && seq_preset_of(a, b) == pr) items = a.Hkv * seq_splits(a, b);
-        s_cnt[tid] = items;
-        __syncthreads();
-        for (int off = 1; off < 256; off <<= 1) {
-          int v = tid >= off ? s_cnt[tid - off] : 0;
-          __syncthreads();
-          s_cnt[tid] += v;
-          __syncthreads();
-        }
-        if (b < a.B) a.work[pr * (a.B + 1) + b] = carry + s_cnt[tid] - items;
-        int tot = s_cnt[255];
-        __syncthreads();
-        carry += tot;
-      }
-      if (tid == 0) a.work[pr * (a.B + 1) + a.B] = carry;
-      __syncthreads();
-    }
-    return;
-  }
-  const int b = blockIdx.x / a.Hkv, hk = blockIdx.x % a.Hkv;
-  const int G = a.G;
-  const int pr = seq_preset_of(a, b);
-  const DevTables& dv = a.dev[pr];
-  const int64_t q0 = ((int64_t)b * a.Hq + (int64_t)hk * G) * D;  // first query row of this KV head
-  const int wave = tid >> 6, lane = tid & 63;
-  constexpr int P = D / 64;  // coordinates per lane: [P lane, P lane + P)
-  __shared__ int s_exp[kMaxG];
-
-  // q~ = D2 H D1 q / sqrt(d): wave w rotates heads w, w + 4 in registers
-  // (butterflies within a lane for the low index bits, across lanes by
-  // shuffles for the others).
-  for (int g = wave; g < G; g += 4) {
-    float x[P];
-#pragma unroll
-    for (int e = 0; e < P; ++e) {
-      const int j = P * lane + e;
-      const float v = a.q_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(a.q)[q0 + g * D + j])
-                               : reinterpret_cast<const float*>(a.q)[q0 + g * D + j];
-      x[e] = v * dv.signs1[j];
-    }
-#pragma unroll
-    for (int hs = 1; hs < P; hs <<= 1) {
-#pragma unroll
-      for (int e = 0; e < P; ++e) {
-        if ((e & hs) == 0) {
-          const float p = x[e], q = x[e + hs];
-          x[e] = p + q;
-          x[e + hs] = p - q;
-        }
-      }
-    }
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-      const bool upper = (lane & m) != 0;
-#pragma unroll
-      for (int e = 0; e < P; ++e) {
-        const float y = __shfl_xor(x[e], m, 64);
-        x[e] = upper ? (y - x[e]) : (x[e] + y);
-      }
-    }
-    const float inv = 1.0f / __builtin_sqrtf((float)D);
-    float amax = 0.f;
-#pragma unroll
-    for (int e = 0; e < P; ++e) {
-      const int j = P * lane + e;
-      const float v = x[e] * inv * dv.signs2[j];
-      s_x[g * D + j] = v;
-      a.qt[q0 + g * D + j] = v;
-      amax = fmaxf(amax, fabsf(v));
-    }
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
-    // power-of-two exponent with max |q~| < 2^e (0 for an all-zero head)
-    if (lane == 0) s_exp[g] = amax > 0.f ? (int)((__float_as_uint(amax) >> 23) & 0xFFu) - 126 : 0;
-  }
-  __syncthreads();
-
-  // p[g][i] = sum_j S[i][j] q~[g][j] on the matrix cores: A rows = heads (fp16
-  // hi/lo of q~ 2^-e_g so fp16 cannot overflow), B = the 16 S tiles of the
-  // context (fp16 hi/lo), three products per tile; wave w takes column tiles
-  // w, w + 4, ... with all its B tiles loaded up front.
-  {
-    constexpr int KT = D / 32, NT = D / 16, NTW = NT / 4;
-    const int arow = lane & 15, kq = lane >> 4;
-    const float ascale = arow < G ? __builtin_ldexpf(1.0f, -s_exp[arow]) : 0.f;
-    f16x8 ahi[KT], alo[KT];
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float v = arow < G ? s_x[arow * D + 32 * kt + 8 * kq + e] * ascale : 0.f;
-        const _Float16 hv = (_Float16)v;
-        ahi[kt][e] = hv;
-        alo[kt][e] = (_Float16)(v - (float)hv);
-      }
-    }
-    f16x8 bhi[NTW][KT], blo[NTW][KT];
-#pragma unroll
-    for (int i = 0; i < NTW; ++i) {
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-        const size_t tb = ((((size_t)(wave + 4 * i)) * KT + kt) * 2) * 64 * 8;
-        bhi[i][kt] = *reinterpret_cast<const f16x8*>(dv.s_tiles + tb + lane * 8);
-        blo[i][kt] = *reinterpret_cast<const f16x8*>(dv.s_tiles + tb + 512 + lane * 8);
-      }
-    }
-    const float unscale = 1.0f / (float)(1 << kSScaleLog2);
-#pragma unroll
-    for (int i = 0; i < NTW; ++i) {
-      const int nt = wave + 4 * i;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[kt], bhi[i][kt], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[kt], blo[i][kt], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[kt], bhi[i][kt], acc, 0, 0, 0);
-      }
-      // result row 4 (lane / 16) + r (a head), column lane % 16
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int g = 4 * kq + r;
-        if (g < G) a.pq[q0 + (int64_t)g * D + 16 * nt + arow] = __builtin_ldexpf(acc[r] * unscale, s_exp[g]);
-      }
-    }
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -352,11 +206,11 @@ __device__ __forceinline__ uint32_t opaque_u32(uint32_t x) {
 }
 __device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory"); }
 
-template <int D, int GP, int KB, int VB>
+template <int D, int GP, int KB, int VB, class Setup>
 __device__ void split_cached_chunk(const DArgs& a, int pr, int h, int t0, int t1, const int32_t* s_blk,
                                    const uint2* s_pair, const u32x4* s_sgn, float* s_p, unsigned char* s_main,
-                                   float* s_stat, const bf16x8 (&A1)[D / 32][2], const bf16x8 (&A3)[D / 32],
-                                   float* m_out, float* l_out, int b) {
+                                   float* s_stat, bf16x8 (&A1)[D / 32][2], bf16x8 (&A3)[D / 32],
+                                   float* m_out, float* l_out, int b, Setup&& setup) {
   using R = Rec<D, KB, VB>;
   constexpr int KT = D / 32;
   constexpr int CS = D / 128;      // value column sets
@@ -399,7 +253,7 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h, int t0, int t1
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const int blk = __builtin_amdgcn_readfirstlane(s_blk[2 * st + half]);
-      const bool ok = blk >= 0 && (int64_t)blk < pblocks;
+      const bool ok = blk >= 0;  // validated at staging
       const uint64_t base = reinterpret_cast<uint64_t>(pool + ((int64_t)(ok ? blk : 0) * a.Hkv + h) * rec);
       const uint32_t dst = ring_lds + sl * R::slot + half * R::bytes;
 #pragma unroll
@@ -442,10 +296,10 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h, int t0, int t1
 
   auto compute = [&](const unsigned char* sb, int st) {
     const int base = t0 + 32 * st;
-    const int blk0 = s_blk[2 * st], blk1 = s_blk[2 * st + 1];
-    const bool ok0 = blk0 >= 0 && (int64_t)blk0 < pblocks;
-    const bool ok1 = blk1 >= 0 && (int64_t)blk1 < pblocks;
-    const bool full = ok0 && ok1 && base + 32 <= t1;  // every token of the step is live
+    // block ids were validated at staging: -1 marks a block outside the pool
+    const bool ok0 = __builtin_amdgcn_readfirstlane(s_blk[2 * st]) >= 0;
+    const bool ok1 = __builtin_amdgcn_readfirstlane(s_blk[2 * st + 1]) >= 0;
+    const bool full = ok0 && ok1 && base + 32 <= t1;  // every token of the step is live (uniform)
     float xl[2][4];
     // ------------------------------------------------------------ scores
 #pragma unroll
@@ -483,17 +337,30 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h, int t0, int t1
       // (GP = 8) lanes apart
       const float n = f16_bits_to_f32((uint16_t)(km & 0xFFFFu));
       const float nk = n * f16_bits_to_f32((uint16_t)(km >> 16));
-      const int my_tok = base + 16 * half + tok;
-      const bool live = full || ((half ? ok1 : ok0) && my_tok < t1);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float v = __builtin_fmaf(nk, aq[r], n * am[r]);
-        const float lg = GP == 4 ? lane_swap16_sum(v) : lane_swap32_sum(v);
-        if (a.scores && row_lane && live) {
+        xl[half][r] = GP == 4 ? lane_swap16_sum(v) : lane_swap32_sum(v);
+      }
+    }
+    if (!full) {  // uniform: dead tokens of a partial step get -inf
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const bool live = (half ? ok1 : ok0) && base + 16 * half + tok < t1;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) xl[half][r] = live ? xl[half][r] : -INFINITY;
+      }
+    }
+    if (a.scores) {  // uniform: estimated q.k of the live tokens
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int my_tok = base + 16 * half + tok;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
           const int hh = (hi_heads ? 4 : 0) + r;
-          if (hh < a.G) a.scores[((int64_t)b * a.Hq + h * a.G + hh) * a.scores_stride + my_tok] = lg * a.inv_logit_scale;
+          if (row_lane && hh < a.G && xl[half][r] != -INFINITY)
+            a.scores[((int64_t)b * a.Hq + h * a.G + hh) * a.scores_stride + my_tok] = xl[half][r] * a.inv_logit_scale;
         }
-        xl[half][r] = live ? lg : -INFINITY;
       }
     }
     // ------------------------------------------------------------ softmax
@@ -638,11 +505,14 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h, int t0, int t1
 #pragma unroll
   for (int it = 0; it < R::nslot - 1; ++it)
     if (it < mine) issue(wave + kWaves * it, it);
-  for (int it = 0; it < mine; ++it) {
+  setup(A1, A3);  // per-item work that needs no cache data runs while the first steps stream in
+  // one ring lap per outer iteration, so every slot offset is a constant
+  auto stream_step = [&](int it, auto slot_c) {
+    constexpr int SL = decltype(slot_c)::value;
     const int ahead = min(R::nslot - 1, mine - 1 - it);  // steps already issued after this one
     if (it + R::nslot - 1 < mine) {
       wait_lgkm0();  // ring slot reuse: the reads of the step that used it are complete
-      issue(wave + kWaves * (it + R::nslot - 1), (it + R::nslot - 1) % R::nslot);
+      issue(wave + kWaves * (it + R::nslot - 1), (SL + R::nslot - 1) % R::nslot);
     }
     if (!exact_wait || ahead == 0)
       wait_vmcnt<0>();
@@ -650,7 +520,13 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h, int t0, int t1
       wait_vmcnt<DPS>();
     else
       wait_vmcnt<(R::nslot - 1) * DPS>();
-    compute(ring + (it % R::nslot) * R::slot, wave + kWaves * it);
+    compute(ring + SL * R::slot, wave + kWaves * it);
+  };
+  for (int it = 0; it < mine; it += R::nslot) {
+    stream_step(it, std::integral_constant<int, 0>{});
+    if (it + 1 < mine) stream_step(it + 1, std::integral_constant<int, 1>{});
+    if constexpr (R::nslot == 3)
+      if (it + 2 < mine) stream_step(it + 2, std::integral_constant<int, 2>{});
   }
   wait_vmcnt<0>();
   __syncthreads();  // every wave is done with the ring before it becomes the merge area
@@ -793,6 +669,114 @@ __device__ void split_recent(const DArgs& a, int b, int h, int R, float* s_p, fl
   __syncthreads();
 }
 
+// q~ = D2 H D1 q / sqrt(d) of the G query heads of (b, h) into s_q (wave w
+// rotates heads w, w + 4 in registers: butterflies within a lane for the low
+// index bits, shuffles for the others), then p = S q~ on the matrix cores into
+// s_pq: A rows = heads (fp16 hi/lo of q~ 2^-e_g, with 2^e_g above the head's
+// largest |q~_j| so fp16 cannot overflow), B = the 16 S tiles of the context,
+// three products per tile; wave w takes column tiles w, w + 4, ...
+template <int D>
+__device__ __forceinline__ void rotate_project(const DArgs& a, const DevTables& dv, int b, int h, float* s_q, float* s_pq,
+                               int* s_exp) {
+  constexpr int P = D / 64;
+  constexpr int KT = D / 32, NT = D / 16, NTW = NT / kWaves;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int G = a.G;
+  const int64_t q0 = ((int64_t)b * a.Hq + (int64_t)h * G) * D;
+  // the S tiles do not depend on q: load them first
+  f16x8 bhi[NTW][KT], blo[NTW][KT];
+#pragma unroll
+  for (int i = 0; i < NTW; ++i) {
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+      const size_t tb = ((((size_t)(wave + kWaves * i)) * KT + kt) * 2) * 64 * 8;
+      bhi[i][kt] = *reinterpret_cast<const f16x8*>(dv.s_tiles + tb + lane * 8);
+      blo[i][kt] = *reinterpret_cast<const f16x8*>(dv.s_tiles + tb + 512 + lane * 8);
+    }
+  }
+  for (int g = wave; g < G; g += kWaves) {
+    float x[P];
+#pragma unroll
+    for (int e = 0; e < P; ++e) {
+      const int j = P * lane + e;
+      const float v = a.q_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(a.q)[q0 + g * D + j])
+                               : reinterpret_cast<const float*>(a.q)[q0 + g * D + j];
+      x[e] = v * dv.signs1[j];
+    }
+#pragma unroll
+    for (int hs = 1; hs < P; hs <<= 1) {
+#pragma unroll
+      for (int e = 0; e < P; ++e) {
+        if ((e & hs) == 0) {
+          const float p = x[e], q = x[e + hs];
+          x[e] = p + q;
+          x[e + hs] = p - q;
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      const bool upper = (lane & m) != 0;
+#pragma unroll
+      for (int e = 0; e < P; ++e) {
+        const float y = __shfl_xor(x[e], m, 64);
+        x[e] = upper ? (y - x[e]) : (x[e] + y);
+      }
+    }
+    const float inv = 1.0f / __builtin_sqrtf((float)D);
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < P; ++e) {
+      const int j = P * lane + e;
+      const float v = x[e] * inv * dv.signs2[j];
+      s_q[g * D + j] = v;
+      amax = fmaxf(amax, fabsf(v));
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+    if (lane == 0) s_exp[g] = amax > 0.f ? (int)((__float_as_uint(amax) >> 23) & 0xFFu) - 126 : 0;
+  }
+  __syncthreads();
+  const int arow = lane & 15, kq = lane >> 4;
+  const float ascale = arow < G ? __builtin_ldexpf(1.0f, -s_exp[arow]) : 0.f;
+  f16x8 ahi[KT], alo[KT];
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float v = arow < G ? s_q[arow * D + 32 * kt + 8 * kq + e] * ascale : 0.f;
+      const _Float16 hv = (_Float16)v;
+      ahi[kt][e] = hv;
+      alo[kt][e] = (_Float16)(v - (float)hv);
+    }
+  }
+  const float unscale = 1.0f / (float)(1 << kSScaleLog2);
+#pragma unroll
+  for (int i = 0; i < NTW; ++i) {
+    const int nt = wave + kWaves * i;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[kt], bhi[i][kt], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[kt], blo[i][kt], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[kt], bhi[i][kt], acc, 0, 0, 0);
+    }
+    // result row 4 (lane / 16) + r (a head), column lane % 16
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int g = 4 * kq + r;
+      if (g < G) s_pq[g * D + 16 * nt + arow] = __builtin_ldexpf(acc[r] * unscale, s_exp[g]);
+    }
+  }
+  __syncthreads();
+}
+
+// One workgroup of four waves per work item (b, h, c): chunk c of the cached
+// tokens of (sequence b, KV head h), or the recent window when c is the last
+// split.  The items of this preset are enumerated in (b, h, c) order by a scan
+// every workgroup runs at start-up; workgroup w takes the contiguous range
+// [w total / grid, (w + 1) total / grid), so consecutive items mostly share
+// (b, h) and reuse its rotated query operands.
 template <int D, int GP, int KB, int VB>
 __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DArgs a, int pr) {
   constexpr int KT = D / 32;
@@ -804,11 +788,14 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DArgs a, int 
   unsigned char* s_main = lds + SL::kMainOffset;
   float* s_merge = reinterpret_cast<float*>(s_main);
   __shared__ uint2 s_pair[256];  // centroid pair -> {bf16 hi parts, bf16 lo parts}
-  __shared__ u32x4 s_sgn[256];               // sign byte -> 8 bf16 of +-1 (bit i -> element i)
+  __shared__ u32x4 s_sgn[256];   // sign byte -> 8 bf16 of +-1 (bit i -> element i)
   __shared__ float s_m[kMaxG], s_l[kMaxG];
+  __shared__ __attribute__((aligned(16))) float s_q[GP * D];
+  __shared__ __attribute__((aligned(16))) float s_pq[GP * D];
+  __shared__ int s_exp[GP];
   const int tid = threadIdx.x, lane = tid & 63;
 
-  // tables: centroid pairs of this preset, +-1 patterns of sign nibbles
+  // tables: centroid pairs of this preset, +-1 patterns of sign bytes
   const DevTables& dv = a.dev[pr];
   for (int i = tid; i < (1 << (2 * KB)); i += kWaves * 64) s_pair[i] = make_uint2(dv.pair_lut[2 * i], dv.pair_lut[2 * i + 1]);
   {
@@ -818,21 +805,62 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DArgs a, int 
       w[e] = (((tid >> (2 * e)) & 1) ? 0x3F80u : 0xBF80u) | ((((tid >> (2 * e + 1)) & 1) ? 0x3F80u : 0xBF80u) << 16);
     s_sgn[tid] = w;  // 256 threads, one entry each
   }
-  __syncthreads();
 
-  const int32_t* cum = a.work + pr * (a.B + 1);
-  const int total = cum[a.B];  // written by the prep launch on the same stream
-  for (int item = blockIdx.x; item < total; item += gridDim.x) {
-    // find the sequence: largest b with cum[b] <= item
-    int lo = 0, hi = a.B - 1;
-    while (lo < hi) {
-      int mid = (lo + hi + 1) >> 1;
-      if (cum[mid] <= item) lo = mid; else hi = mid - 1;
+  // work list: exclusive prefix over sequences of Hkv * splits(b) for the
+  // sequences of this preset, in the (still unused) ring area
+  int* s_scan = reinterpret_cast<int*>(s_main);
+  {
+    int carry = 0;
+    for (int base = 0; base < a.B; base += kWaves * 64) {
+      const int bb = base + tid;
+      const int items = (bb < a.B && seq_preset_of(a, bb) == pr) ? a.Hkv * seq_splits(a, bb) : 0;
+      int* sc = s_scan + base;
+      if (bb < a.B) sc[tid] = items;
+      __syncthreads();
+      // Hillis-Steele inclusive scan of this block of 256 entries, in place
+      for (int off = 1; off < kWaves * 64; off <<= 1) {
+        const int v = (bb < a.B && tid >= off) ? sc[tid - off] : 0;
+        __syncthreads();
+        if (bb < a.B) sc[tid] += v;
+        __syncthreads();
+      }
+      const int last = min(kWaves * 64, a.B - base) - 1;
+      const int tot = sc[last];
+      __syncthreads();
+      if (bb < a.B) sc[tid] = carry + sc[tid] - items;  // exclusive
+      carry += tot;
+      __syncthreads();
     }
-    const int b = lo;
-    const int local = item - cum[b];
+    if (tid == 0) s_scan[a.B] = carry;
+    __syncthreads();
+  }
+  const int total = s_scan[a.B];
+  const int i0 = (int)((int64_t)blockIdx.x * total / gridDim.x);
+  const int i1 = (int)((int64_t)(blockIdx.x + 1) * total / gridDim.x);
+  int b = 0, cur_base = 0;
+  if (i0 < i1) {
+    int lo = 0, hi = a.B - 1;  // largest b with s_scan[b] <= i0
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_scan[mid] <= i0) lo = mid; else hi = mid - 1;
+    }
+    b = lo;
+    cur_base = s_scan[b];
+  }
+  __syncthreads();  // the ring area is free again
+
+  bf16x8 A1[KT][2], A3[KT];
+  int ready_bh = -1;  // (b, h) whose query operands A1 / A3 hold
+  for (int item = i0; item < i1; ++item) {
+    // advance to the sequence holding this item (sequences of the other
+    // preset, or with no splits, hold none)
+    while (b < a.B && item - cur_base >= (seq_preset_of(a, b) == pr ? a.Hkv * seq_splits(a, b) : 0)) {
+      cur_base += seq_preset_of(a, b) == pr ? a.Hkv * seq_splits(a, b) : 0;
+      ++b;
+    }
+    if (b >= a.B) break;  // inconsistent with the scan: stop
+    const int local = item - cur_base;
     const int nsp = seq_splits(a, b);
-    if (nsp <= 0 || local < 0 || local >= nsp * a.Hkv) break;  // inconsistent work list: stop
     const int h = local / nsp, c = local % nsp;
     const int Lc = seq_cached(a, b);
     const int nq_chunks = (Lc + a.chunk - 1) / a.chunk;
@@ -844,51 +872,61 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DArgs a, int 
       {
         const int nblk = (t1 - t0 + 15) >> 4;
         const int32_t* btrow = a.bt + (int64_t)b * a.max_blocks + (t0 >> 4);
-        for (int i = tid; i < (a.chunk >> 4) + 2; i += kWaves * 64) s_blk[i] = i < nblk ? btrow[i] : -1;
+        const int64_t pblocks = a.pool_blocks[pr];
+        for (int i = tid; i < (a.chunk >> 4) + 2; i += kWaves * 64) {
+          const int blk = i < nblk ? btrow[i] : -1;
+          s_blk[i] = (blk >= 0 && (int64_t)blk < pblocks) ? blk : -1;
+        }
       }
-      // A operands: rows 0..GP-1 = hi parts of head rows, GP..2GP-1 = lo parts.
-      // A1[kt][m] slot e holds coordinate 8 kt + 4 m + {0,1,0,1,2,3,2,3}[e] of
-      // the lane quarter, matching the {hi pair, lo pair} B dwords; A3[kt] slot e
-      // holds coordinate 8 kt + e (sign bits in order).
-      bf16x8 A1[KT][2], A3[KT];
-      {
+      __syncthreads();
+      // A operands (built while the first steps stream in): rows 0..GP-1 =
+      // hi parts of head rows, GP..2GP-1 = lo parts.  A1[kt][m] slot e holds
+      // coordinate 8 kt + 4 m + {0,1,0,1,2,3,2,3}[e] of the lane quarter,
+      // matching the {hi pair, lo pair} B dwords; A3[kt] slot e holds
+      // coordinate 8 kt + e (sign bits in order).  log2(e) sm_scale is folded
+      // into q~, sqrt(pi/2) / d log2(e) sm_scale into p.
+      auto setup = [&](bf16x8 (&A1r)[KT][2], bf16x8 (&A3r)[KT]) {
+        const int bh = b * a.Hkv + h;
+        if (bh == ready_bh) return;
+        rotate_project<D>(a, dv, b, h, s_q, s_pq, s_exp);
         const int arow = lane & 15, kq = lane >> 4;
         const int g = arow % GP;
         const bool is_lo = arow >= GP;
         const bool used = arow < 2 * GP && g < a.G;
-        const int64_t qo = ((int64_t)b * a.Hq + h * a.G + (used ? g : 0)) * D;
         const float kappa = 1.2533141373155003f / (float)D;  // sqrt(pi/2) / d
         auto split = [&](float x) -> uint32_t {
           const float v = used ? x : 0.f;
           const uint32_t hb = f32_to_bf16_bits(v);
           return is_lo ? f32_to_bf16_bits(v - __uint_as_float(hb << 16)) : hb;
         };
+        const float* xq = s_q + (used ? g : 0) * D;
+        const float* yq = s_pq + (used ? g : 0) * D;
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt) {
           const int j0 = kq * (D / 4) + 8 * kt;
-          const f32x4 xa = *reinterpret_cast<const f32x4*>(a.qt + qo + j0);
-          const f32x4 xb = *reinterpret_cast<const f32x4*>(a.qt + qo + j0 + 4);
-          const f32x4 ya = *reinterpret_cast<const f32x4*>(a.pq + qo + j0);
-          const f32x4 yb = *reinterpret_cast<const f32x4*>(a.pq + qo + j0 + 4);
+          const f32x4 xa = *reinterpret_cast<const f32x4*>(xq + j0);
+          const f32x4 xb = *reinterpret_cast<const f32x4*>(xq + j0 + 4);
+          const f32x4 ya = *reinterpret_cast<const f32x4*>(yq + j0);
+          const f32x4 yb = *reinterpret_cast<const f32x4*>(yq + j0 + 4);
           const float xs[8] = {xa[0], xa[1], xa[2], xa[3], xb[0], xb[1], xb[2], xb[3]};
           const float ys[8] = {ya[0], ya[1], ya[2], ya[3], yb[0], yb[1], yb[2], yb[3]};
           u32x4 w3;
 #pragma unroll
           for (int e = 0; e < 8; e += 2)
             w3[e / 2] = split(ys[e] * (kappa * a.logit_scale)) | (split(ys[e + 1] * (kappa * a.logit_scale)) << 16);
-          A3[kt] = __builtin_bit_cast(bf16x8, w3);
+          A3r[kt] = __builtin_bit_cast(bf16x8, w3);
 #pragma unroll
           for (int m = 0; m < 2; ++m) {
             const float ls = a.logit_scale;
             const uint32_t c01 = split(xs[4 * m] * ls) | (split(xs[4 * m + 1] * ls) << 16);
             const uint32_t c23 = split(xs[4 * m + 2] * ls) | (split(xs[4 * m + 3] * ls) << 16);
-            A1[kt][m] = __builtin_bit_cast(bf16x8, u32x4{c01, c01, c23, c23});
+            A1r[kt][m] = __builtin_bit_cast(bf16x8, u32x4{c01, c01, c23, c23});
           }
         }
-      }
-      __syncthreads();
+        ready_bh = bh;
+      };
       split_cached_chunk<D, GP, KB, VB>(a, pr, h, t0, t1, s_blk, s_pair, s_sgn, s_p, s_main, s_stat, A1, A3,
-                                        s_m, s_l, b);
+                                        s_m, s_l, b, setup);
     } else {
       split_recent<D, GP>(a, b, h, seq_recent(a, b), s_p, s_merge, s_m, s_l);
     }
@@ -983,9 +1021,7 @@ static hipError_t dispatch_preset(const DArgs& a, int pr, int kb, int vb, hipStr
 
 template <int D>
 static hipError_t launch_all(const DArgs& a, const tq_decode_args* args, hipStream_t s) {
-  hipLaunchKernelGGL(decode_prep_kernel<D>, dim3(a.B * a.Hkv + 1), dim3(256), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
   if (args->split_events[0] && (e = hipEventRecord((hipEvent_t)args->split_events[0], s)) != hipSuccess) return e;
   for (int pr = 0; pr < args->num_presets; ++pr) {
     const tq_ctx* c = args->ctx[pr];
@@ -1028,10 +1064,7 @@ hipError_t launch_decode(const tq_decode_args* args, const DecodePlan& plan, hip
   a.chunk = args->chunk_tokens;
   a.splits_cap = plan.num_splits_max;
   char* ws = reinterpret_cast<char*>(args->workspace);
-  a.qt = reinterpret_cast<float*>(ws + plan.off_qt);
-  a.pq = reinterpret_cast<float*>(ws + plan.off_p);
   a.part = reinterpret_cast<float*>(ws + plan.off_part);
-  a.work = reinterpret_cast<int32_t*>(ws + plan.off_work);
   a.out = args->out;
   a.scores = args->scores_out;
   a.scores_stride = args->scores_stride;

@@ -454,7 +454,8 @@ int check_decode_shape(const tq_decode_args* a) {
     set_error("decode: both presets must share head_dim");
     return TQ_EINVAL;
   }
-  if (a->batch < 0 || a->num_q_heads <= 0 || a->num_kv_heads <= 0 || a->num_q_heads % a->num_kv_heads) {
+  if (a->batch < 0 || a->batch > 8192 || a->num_q_heads <= 0 || a->num_kv_heads <= 0 ||
+      a->num_q_heads % a->num_kv_heads) {
     set_error("decode: batch %d, num_q_heads %d, num_kv_heads %d invalid", a->batch, a->num_q_heads,
               a->num_kv_heads);
     return TQ_EINVAL;
@@ -498,11 +499,8 @@ DecodePlan tq::plan_decode(const tq_decode_args* a) {
   if (p.num_splits_max < 1) p.num_splits_max = 1;
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   size_t nq = (size_t)a->batch * a->num_q_heads;
-  p.off_qt = 0;
-  p.off_p = up(p.off_qt + 4 * nq * p.d);
-  p.off_part = up(p.off_p + 4 * nq * p.d);
-  p.off_work = up(p.off_part + 4 * nq * (size_t)p.num_splits_max * (p.d + 2));
-  p.bytes = up(p.off_work + 4 * 2 * ((size_t)a->batch + 1));
+  p.off_part = 0;
+  p.bytes = up(p.off_part + 4 * nq * (size_t)p.num_splits_max * (p.d + 2));
   return p;
 }
 

@@ -62,7 +62,7 @@ hipError_t launch_quantize(const tq_ctx* c, const void* k, const void* v, int in
 
 struct DecodePlan {
   int d, G, num_splits_max, chunk;
-  size_t off_qt, off_p, off_part, off_work, bytes;
+  size_t off_part, bytes;
 };
 DecodePlan plan_decode(const tq_decode_args* a);
 hipError_t launch_decode(const tq_decode_args* a, const DecodePlan& plan, hipStream_t stream);
