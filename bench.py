@@ -171,6 +171,9 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--chunk", type=int, default=4096, help="tokens per decode split (fixed grid)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="finish with three 256 MiB device-to-device copies (the reference kernel for "
+                         "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path shards by KV head or "
@@ -258,6 +261,12 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+    if args.copy_calibration:
+        x = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
 
 
 if __name__ == "__main__":
