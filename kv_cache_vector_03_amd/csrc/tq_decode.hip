@@ -112,7 +112,10 @@ struct Rec {
 template <int D, int GP, int KB, int VB>
 struct SplitLds {
   static_assert(Rec<D, KB, VB>::bytes % 16 == 0, "record size");
-  static constexpr int kPBytes = kWaves * GP * 32 * 4;  // per-wave softmax weights
+  // per-wave softmax weights [GP][32]; with GP = 4 the idle lanes 32-63 store
+  // theirs to a second, never-read copy so that the store needs no lane mask
+  static constexpr int kPWave = GP * 32 * (GP == 4 ? 2 : 1);
+  static constexpr int kPBytes = kWaves * kPWave * 4;
   static constexpr int kStatBytes = kWaves * GP * 2 * 4;
   static constexpr int kBlkBytes = (kMaxChunk / 16 + 16) * 4;
   static constexpr int kRingBytes = kWaves * Rec<D, KB, VB>::nslot * Rec<D, KB, VB>::slot;
@@ -222,12 +225,13 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h, int t0, int t1
   constexpr int DPR = (PPR + 63) / 64;        // DMA instructions per record
   constexpr int DPS = 2 * DPR;                // DMA instructions per step
   static_assert((R::nslot - 1) * DPS < 64, "vmcnt range");
+  static_assert(PPR >= 64, "a record spans at least one full DMA window");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tok = lane & 15, kq = lane >> 4;
   const uint8_t* pool = a.pool[pr];
   const int64_t rec = a.rec[pr];
   const int64_t pblocks = a.pool_blocks[pr];
-  float* sp = s_p + wave * GP * 32;
+  float* sp = s_p + wave * SplitLds<D, GP, KB, VB>::kPWave;
   unsigned char* ring = s_main + wave * R::nslot * R::slot;
   const uint32_t ring_lds = lds_offset(ring);
 
@@ -247,8 +251,11 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h, int t0, int t1
   }
 
   // Stream the two records of step `st` into ring slot `sl`: record r's piece
-  // k (16 bytes) lands at slot + r * bytes + 16 k; one DMA instruction per 64
-  // pieces, with the record base in SGPRs and a constant per-lane offset.
+  // k (16 bytes) lands at slot + r * bytes + 16 k; one DMA instruction per
+  // window of 64 pieces, with the record base in SGPRs and a constant
+  // per-lane offset.  The last window ends at the record's last piece and
+  // overlaps the one before it (those pieces are written twice with the same
+  // bytes), so every DMA runs on all 64 lanes and needs no lane mask.
   auto issue = [&](int st, int sl) {
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
@@ -258,7 +265,8 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h, int t0, int t1
       const uint32_t dst = ring_lds + sl * R::slot + half * R::bytes;
 #pragma unroll
       for (int j = 0; j < DPR; ++j) {
-        if (64 * j + 64 <= PPR || lane < PPR - 64 * j) dma16(dst + 1024 * j, base, 16 * (64 * j + lane));
+        const int p0 = j == DPR - 1 ? PPR - 64 : 64 * j;  // first piece of window j
+        dma16(dst + 16 * p0, base, 16 * (p0 + lane));
       }
     }
   };
@@ -281,8 +289,6 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h, int t0, int t1
 #pragma unroll
   for (int g = 0; g < GP; ++g) m_run[g] = -INFINITY;
   float lsum[4] = {0.f, 0.f, 0.f, 0.f};  // per-lane partial sums (rows of lanes 0..31)
-  const bool hi_heads = GP == 8 && (lane & 16);  // lanes 16-31 carry heads 4..7 when GP = 8
-  const bool row_lane = lane < (GP == 8 ? 32 : 16);
   const uint32_t c1024 = opaque_u32(0x64006400u);  // two fp16 1024.0
   const f16x8 k1024 = __builtin_bit_cast(f16x8, u32x4{c1024, c1024, c1024, c1024});
   const int arow = lane & 15;
@@ -300,8 +306,11 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h, int t0, int t1
     const bool ok0 = __builtin_amdgcn_readfirstlane(s_blk[2 * st]) >= 0;
     const bool ok1 = __builtin_amdgcn_readfirstlane(s_blk[2 * st + 1]) >= 0;
     const bool full = ok0 && ok1 && base + 32 <= t1;  // every token of the step is live (uniform)
-    float xl[2][4];
     // ------------------------------------------------------------ scores
+    // v[half][r]: MFMA output row 4 (lane / 16) + r of the half's 16 tokens
+    // (column = token); rows 0..GP-1 carry the hi parts of the heads, rows
+    // GP..2GP-1 the lo parts.
+    float v[2][4];
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const unsigned char* hb = sb + half * R::bytes;
@@ -333,46 +342,42 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h, int t0, int t1
       }
       // logit = log2(e) sm_scale n (q~.c + kappa gamma p.sign), with
       // log2(e) sm_scale folded into q~ and kappa log2(e) sm_scale into p (the
-      // A operands); the hi and lo rows of a head sit 16 (GP = 4) or 32
-      // (GP = 8) lanes apart
+      // A operands)
       const float n = f16_bits_to_f32((uint16_t)(km & 0xFFFFu));
       const float nk = n * f16_bits_to_f32((uint16_t)(km >> 16));
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float v = __builtin_fmaf(nk, aq[r], n * am[r]);
-        xl[half][r] = GP == 4 ? lane_swap16_sum(v) : lane_swap32_sum(v);
-      }
+      for (int r = 0; r < 4; ++r) v[half][r] = __builtin_fmaf(nk, aq[r], n * am[r]);
     }
+    // x[r]: hi + lo of head row r, one swap per row.  GP = 4: the hi and lo
+    // rows sit 16 lanes apart; after the swap lanes 0-15 hold the first 16
+    // tokens, lanes 16-31 the second 16 (lanes 32-63 hold zero rows and are
+    // never read back).  GP = 8: rows 32 lanes apart; lanes 0-31 take the
+    // first 16 tokens (heads 0-3 | 4-7 by lane bit 4), lanes 32-63 the second.
+    const int sh = GP == 4 ? ((lane >> 4) & 1) : (lane >> 5);
+    float x[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      auto sw = GP == 4 ? __builtin_amdgcn_permlane16_swap(__float_as_uint(v[0][r]), __float_as_uint(v[1][r]), false, false)
+                        : __builtin_amdgcn_permlane32_swap(__float_as_uint(v[0][r]), __float_as_uint(v[1][r]), false, false);
+      x[r] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
+    const int my_tok = base + 16 * sh + tok;
     if (!full) {  // uniform: dead tokens of a partial step get -inf
+      const bool live = (sh ? ok1 : ok0) && my_tok < t1;
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const bool live = (half ? ok1 : ok0) && base + 16 * half + tok < t1;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) xl[half][r] = live ? xl[half][r] : -INFINITY;
-      }
+      for (int r = 0; r < 4; ++r) x[r] = live ? x[r] : -INFINITY;
     }
     if (a.scores) {  // uniform: estimated q.k of the live tokens
+      const int ln = (int)opaque_u32((uint32_t)lane);  // recomputed here, not kept live across the loop
+      const int hh0 = GP == 8 && (ln & 16) ? 4 : 0;
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int my_tok = base + 16 * half + tok;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int hh = (hi_heads ? 4 : 0) + r;
-          if (row_lane && hh < a.G && xl[half][r] != -INFINITY)
-            a.scores[((int64_t)b * a.Hq + h * a.G + hh) * a.scores_stride + my_tok] = xl[half][r] * a.inv_logit_scale;
-        }
+      for (int r = 0; r < 4; ++r) {
+        if ((GP == 8 || ln < 32) && hh0 + r < a.G && x[r] != -INFINITY)
+          a.scores[((int64_t)b * a.Hq + h * a.G + hh0 + r) * a.scores_stride + my_tok] = x[r] * a.inv_logit_scale;
       }
     }
     // ------------------------------------------------------------ softmax
-    // Each lane takes four distinct (head, token) logits: GP = 4: lanes 0-15
-    // the first 16 tokens, lanes 16-31 the second 16 (the swap-sum left every
-    // head row in both lane groups), lanes 32-63 idle; GP = 8: lanes 0-31 the
-    // first 16 tokens (heads 0-3 | 4-7), lanes 32-63 the second 16.
-    const int sh = GP == 4 ? ((lane >> 4) & 1) : (lane >> 5);
-    const bool act = GP == 8 || lane < 32;
-    float x[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) x[r] = act ? (sh ? xl[1][r] : xl[0][r]) : -INFINITY;
+    // Each lane holds four distinct (head, token) logits (see x above).
     float y0 = x[0], y1 = x[1], y2 = x[2], y3 = x[3];
     row_max16x4(y0, y1, y2, y3);
     const float ys[4] = {y0, y1, y2, y3};
@@ -391,6 +396,7 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h, int t0, int t1
 #pragma unroll
     for (int g = 0; g < GP; ++g) grow |= mt[g] > m_run[g];
     if (grow) {  // uniform: some head's running max grew; rescale what was accumulated
+      const int ln = (int)opaque_u32((uint32_t)lane);  // lane predicates are formed here, not kept live
       float alpha[GP];
 #pragma unroll
       for (int g = 0; g < GP; ++g) {
@@ -399,7 +405,7 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h, int t0, int t1
         m_run[g] = mn;
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) lsum[r] *= hi_heads ? alpha[(4 + r) % GP] : alpha[r];
+      for (int r = 0; r < 4; ++r) lsum[r] *= (GP == 8 && (ln & 16)) ? alpha[(4 + r) % GP] : alpha[r];
 #pragma unroll
       for (int cs = 0; cs < CS; ++cs)
 #pragma unroll
@@ -412,18 +418,22 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h, int t0, int t1
           }
           float az = alpha[4 * rt];
 #pragma unroll
-          for (int r = 1; r < 4; ++r) az = ((lane & 3) == r) ? alpha[4 * rt + r] : az;
+          for (int r = 1; r < 4; ++r) az = ((ln & 3) == r) ? alpha[4 * rt + r] : az;
           zacc[cs][rt] *= az;
         }
     }
     {
-      const int tokw = (lane & 15) + 16 * sh;
+      // weight of (head hh0 + r, token tokw); with GP = 4 lanes 32-63 write
+      // the unread second copy (address arithmetic instead of a lane mask)
+      const int ln = (int)opaque_u32((uint32_t)lane);
+      const int hh0 = GP == 8 ? ((ln >> 4) & 1) * 4 : 0;
+      float* spw = sp + (ln & 15) + 16 * sh + (GP == 4 ? (ln >> 5) * (GP * 32) : 0);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float mr = hi_heads ? m_run[(4 + r) % GP] : m_run[r];
+        const float mr = (GP == 8 && hh0) ? m_run[(4 + r) % GP] : m_run[r];
         const float p = __builtin_amdgcn_exp2f(x[r] - (mr == -INFINITY ? 0.f : mr));
         lsum[r] += p;
-        if (act) sp[((hi_heads ? 4 : 0) + r) * 32 + tokw] = p;
+        spw[(hh0 + r) * 32] = p;
       }
     }
     wait_lgkm0();  // the weights are in LDS
@@ -783,7 +793,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DArgs a, int 
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   using SL = SplitLds<D, GP, KB, VB>;
   float* s_p = reinterpret_cast<float*>(lds);
-  float* s_stat = s_p + kWaves * GP * 32;
+  float* s_stat = s_p + kWaves * SL::kPWave;
   int32_t* s_blk = reinterpret_cast<int32_t*>(s_stat + kWaves * GP * 2);
   unsigned char* s_main = lds + SL::kMainOffset;
   float* s_merge = reinterpret_cast<float*>(s_main);
