@@ -170,7 +170,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--chunk", type=int, default=4096, help="tokens per decode split (fixed grid)")
+    ap.add_argument("--chunk", type=int, default=8192, help="tokens per decode split (fixed grid)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="finish with three 256 MiB device-to-device copies (the reference kernel for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes)")

@@ -178,7 +178,10 @@ typedef struct {
   const int32_t* recent_lens;/* device int32 [batch] in [0, recent_window], NULL iff recent_k is NULL */
   int32_t recent_window;
   float sm_scale;            /* <= 0 selects 1/sqrt(head_dim) */
-  int32_t chunk_tokens;      /* tokens per split, a multiple of 32 in [32, 4096] (fixed at capture) */
+  int32_t chunk_tokens;      /* tokens per split, a multiple of 32 in [32, 8192] (fixed at capture);
+                                with no recent window and max_seq_len <= chunk_tokens each
+                                sequence is a single split and the output is written by the
+                                split launch itself (no separate combine launch) */
   int32_t max_seq_len;       /* largest seq_lens entry allowed (sizes the workspace) */
   void* workspace;           /* device, tq_decode_workspace_bytes(args) bytes, 256-byte aligned */
   size_t workspace_bytes;

@@ -38,8 +38,14 @@
 
 namespace tq {
 
-constexpr int kWaves = 4;
 constexpr int kMaxG = 8;
+// Waves per split workgroup.  d = 128 with up to 4 query heads per KV head
+// fits two waves per SIMD (<= 256 VGPRs), so one 8-wave workgroup fills a CU
+// and its waves share one item; the wider variants run one wave per SIMD.
+template <int D, int GP>
+constexpr int split_waves() {
+  return (D == 128 && GP == 4) ? 8 : 4;
+}
 
 struct DArgs {
   const void* q;
@@ -68,6 +74,7 @@ struct DArgs {
   float* out;
   float* scores;
   int scores_stride;
+  int direct;  // every sequence has at most one split: write the normalised output, no partials
 };
 
 __device__ __forceinline__ int seq_cached(const DArgs& a, int b) {
@@ -91,7 +98,15 @@ __device__ __forceinline__ int seq_preset_of(const DArgs& a, int b) {
 // ---------------------------------------------------------------------------
 // split
 // ---------------------------------------------------------------------------
-constexpr int kMaxChunk = 4096;  // largest chunk_tokens (block ids of a chunk are staged in LDS)
+constexpr int kMaxChunk = 8192;  // largest chunk_tokens (block ids of a chunk are staged in LDS)
+// Online softmax with a lazily moved reference: a head's reference m (kept
+// in m_run) only moves when a block's max exceeds m + kLazyMax, and weights
+// are exp2(x - m - kLazyMax) <= 1.  Every weight, l and acc of the stream
+// carries the same 2^-kLazyMax factor, which cancels in acc / l and in the
+// merge of partials (a partial reports m + kLazyMax as its reference, like
+// the exact-max partials of the recent window); the rescale of the
+// accumulators becomes rare.
+constexpr float kLazyMax = 2.0f;
 
 // Compile-time geometry of one (block, KV head) record (the same byte layout
 // the host computes) and of one 32-token step = two records.
@@ -103,9 +118,7 @@ struct Rec {
   static constexpr int vcodes = kmeta + 64;
   static constexpr int vmeta = vcodes + (VB * D / 8) * 16;
   static constexpr int bytes = vmeta + (D / 32) * 64;
-  static constexpr int pieces = 2 * bytes / 16;       // 16-byte pieces of a step
-  static constexpr int dma = (pieces + 63) / 64;      // LDS-DMA instructions per step
-  static constexpr int slot = dma * 1024;             // LDS bytes of one ring slot
+  static constexpr int slot = 2 * bytes;              // LDS bytes of one ring slot (one step)
   static constexpr int nslot = D == 128 ? 3 : 2;      // ring depth (steps in flight + 1)
 };
 
@@ -115,15 +128,18 @@ struct SplitLds {
   // per-wave softmax weights [GP][32]; with GP = 4 the idle lanes 32-63 store
   // theirs to a second, never-read copy so that the store needs no lane mask
   static constexpr int kPWave = GP * 32 * (GP == 4 ? 2 : 1);
-  static constexpr int kPBytes = kWaves * kPWave * 4;
-  static constexpr int kStatBytes = kWaves * GP * 2 * 4;
+  static constexpr int NW = split_waves<D, GP>();
+  static constexpr int kPBytes = NW * kPWave * 4;
+  static constexpr int kStatBytes = NW * GP * 2 * 4;
   static constexpr int kBlkBytes = (kMaxChunk / 16 + 16) * 4;
-  static constexpr int kRingBytes = kWaves * Rec<D, KB, VB>::nslot * Rec<D, KB, VB>::slot;
-  static constexpr int kMergeBytes = kWaves * GP * D * 4;  // overlays the ring after the stream
+  static constexpr int kRingBytes = NW * Rec<D, KB, VB>::nslot * Rec<D, KB, VB>::slot;
+  static constexpr int kMergeBytes = NW * GP * D * 4;  // overlays the ring after the stream
   static constexpr int kMainBytes = kRingBytes > kMergeBytes ? kRingBytes : kMergeBytes;
   static constexpr int kMainOffset = kPBytes + kStatBytes + kBlkBytes;
   static_assert(kMainOffset % 16 == 0, "ring alignment");
   static constexpr int total = kMainOffset + kMainBytes;
+  // with the static tables (< 16 KB) the workgroup must fit a CU's 160 KB
+  static_assert(total <= (160 - 16) * 1024, "split workgroup LDS");
 };
 
 // Row-wide (16-lane) reductions with DPP row rotations.
@@ -207,14 +223,17 @@ __device__ __forceinline__ uint32_t opaque_u32(uint32_t x) {
   asm volatile("" : "+v"(x));
   return x;
 }
+// s_waitcnt immediate for vmcnt(0) alone (expcnt and lgkmcnt at their maxima)
+constexpr int kWaitVm0 = 0x0F70;
 __device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory"); }
 
 template <int D, int GP, int KB, int VB, class Setup>
 __device__ void split_cached_chunk(const DArgs& a, int pr, int h, int t0, int t1, const int32_t* s_blk,
                                    const uint2* s_pair, const u32x4* s_sgn, float* s_p, unsigned char* s_main,
                                    float* s_stat, bf16x8 (&A1)[D / 32][2], bf16x8 (&A3)[D / 32],
-                                   float* m_out, float* l_out, int b, Setup&& setup) {
+                                   float* m_out, float* l_out, int b, int* s_claim, Setup&& setup) {
   using R = Rec<D, KB, VB>;
+  constexpr int NW = split_waves<D, GP>();
   constexpr int KT = D / 32;
   constexpr int CS = D / 128;      // value column sets
   constexpr int RT = GP / 4;       // value row tiles per column set
@@ -306,6 +325,16 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h, int t0, int t1
     const bool ok0 = __builtin_amdgcn_readfirstlane(s_blk[2 * st]) >= 0;
     const bool ok1 = __builtin_amdgcn_readfirstlane(s_blk[2 * st + 1]) >= 0;
     const bool full = ok0 && ok1 && base + 32 <= t1;  // every token of the step is live (uniform)
+    // value codes and scales of the step, read first so that their LDS latency
+    // hides under the score phase (the weight stores below could alias them)
+    u32x4 vx0[CS], vx1[CS], vm0[CS], vm1[CS];
+#pragma unroll
+    for (int cs = 0; cs < CS; ++cs) {
+      vx0[cs] = *reinterpret_cast<const u32x4*>(sb + off_vx[cs]);
+      vx1[cs] = *reinterpret_cast<const u32x4*>(sb + off_vx[cs] + 16);
+      vm0[cs] = *reinterpret_cast<const u32x4*>(sb + off_vm[cs]);
+      vm1[cs] = *reinterpret_cast<const u32x4*>(sb + off_vm[cs] + 16);
+    }
     // ------------------------------------------------------------ scores
     // v[half][r]: MFMA output row 4 (lane / 16) + r of the half's 16 tokens
     // (column = token); rows 0..GP-1 carry the hi parts of the heads, rows
@@ -394,8 +423,8 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h, int t0, int t1
       }
     }
 #pragma unroll
-    for (int g = 0; g < GP; ++g) grow |= mt[g] > m_run[g];
-    if (grow) {  // uniform: some head's running max grew; rescale what was accumulated
+    for (int g = 0; g < GP; ++g) grow |= mt[g] > m_run[g] + kLazyMax;
+    if (grow) {  // uniform: some head's block max passed its reference; rescale what was accumulated
       const int ln = (int)opaque_u32((uint32_t)lane);  // lane predicates are formed here, not kept live
       float alpha[GP];
 #pragma unroll
@@ -431,7 +460,7 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h, int t0, int t1
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float mr = (GP == 8 && hh0) ? m_run[(4 + r) % GP] : m_run[r];
-        const float p = __builtin_amdgcn_exp2f(x[r] - (mr == -INFINITY ? 0.f : mr));
+        const float p = __builtin_amdgcn_exp2f(x[r] - (mr == -INFINITY ? 0.f : mr + kLazyMax));
         lsum[r] += p;
         spw[(hh0 + r) * 32] = p;
       }
@@ -447,10 +476,7 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h, int t0, int t1
     const int vtok0 = base + 8 * kq;
 #pragma unroll
     for (int cs = 0; cs < CS; ++cs) {
-      const u32x4 x0 = *reinterpret_cast<const u32x4*>(sb + off_vx[cs]);
-      const u32x4 x1 = *reinterpret_cast<const u32x4*>(sb + off_vx[cs] + 16);
-      const u32x4 m0 = *reinterpret_cast<const u32x4*>(sb + off_vm[cs]);
-      const u32x4 m1 = *reinterpret_cast<const u32x4*>(sb + off_vm[cs] + 16);
+      const u32x4 x0 = vx0[cs], x1 = vx1[cs], m0 = vm0[cs], m1 = vm1[cs];
       const uint32_t xv[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
       uint32_t sz[8] = {m0[0], m0[1], m0[2], m0[3], m1[0], m1[1], m1[2], m1[3]};
       if (!full) {
@@ -508,35 +534,60 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h, int t0, int t1
     }
   };
 
-  // ---- the stream: this wave takes steps wave, wave + 4, ...; ring depth R::nslot
+  // ---- the stream.  Wave w starts with steps w + NW k (k < nslot - 1);
+  // after those, steps are handed out by the per-item LDS counter *s_claim
+  // (NW (nslot - 1) at item start): a wave claims the next unprocessed step
+  // whenever a ring slot frees up, so waves that get more issue cycles take
+  // more steps and the item's waves finish together.  Ring depth R::nslot;
+  // stq[k] is the step held by slot k (-1: none).  Claims are increasing per
+  // wave, and once the counter passes the last step every later claim fails.
   const int nsteps = (t1 - t0 + 31) / 32;
-  const int mine = wave < nsteps ? (nsteps - wave + kWaves - 1) / kWaves : 0;
   const bool exact_wait = a.scores == nullptr;  // score stores also count in vmcnt
+  bool more = true;
+  auto claim = [&]() -> int {
+    if (!more) return -1;
+    int v = 0;
+    if ((int)opaque_u32((uint32_t)lane) == 0) v = atomicAdd(s_claim, 1);
+    v = __builtin_amdgcn_readfirstlane(v);
+    more = v < nsteps;
+    return more ? v : -1;
+  };
+  int stq[R::nslot];
 #pragma unroll
-  for (int it = 0; it < R::nslot - 1; ++it)
-    if (it < mine) issue(wave + kWaves * it, it);
+  for (int k = 0; k < R::nslot - 1; ++k) {  // the first steps of each wave are fixed: wave + NW k
+    stq[k] = wave + NW * k < nsteps ? wave + NW * k : -1;
+    if (stq[k] >= 0) issue(stq[k], k);
+  }
+  more = stq[R::nslot - 2] >= 0;  // the counter starts at NW (nslot - 1)
+  stq[R::nslot - 1] = -1;
   setup(A1, A3);  // per-item work that needs no cache data runs while the first steps stream in
   // one ring lap per outer iteration, so every slot offset is a constant
-  auto stream_step = [&](int it, auto slot_c) {
+  auto stream_step = [&](auto slot_c) -> bool {
     constexpr int SL = decltype(slot_c)::value;
-    const int ahead = min(R::nslot - 1, mine - 1 - it);  // steps already issued after this one
-    if (it + R::nslot - 1 < mine) {
+    constexpr int FREE = (SL + R::nslot - 1) % R::nslot;  // the slot of the step computed last
+    if (stq[SL] < 0) return false;
+    stq[FREE] = claim();
+    if (stq[FREE] >= 0) {
       wait_lgkm0();  // ring slot reuse: the reads of the step that used it are complete
-      issue(wave + kWaves * (it + R::nslot - 1), (SL + R::nslot - 1) % R::nslot);
+      issue(stq[FREE], FREE);
     }
+    int ahead = 0;  // steps issued after this one (the slots after SL in ring order)
+#pragma unroll
+    for (int k = 1; k < R::nslot; ++k) ahead += stq[(SL + k) % R::nslot] >= 0 ? 1 : 0;
     if (!exact_wait || ahead == 0)
       wait_vmcnt<0>();
     else if (ahead == 1)
       wait_vmcnt<DPS>();
     else
       wait_vmcnt<(R::nslot - 1) * DPS>();
-    compute(ring + SL * R::slot, wave + kWaves * it);
+    compute(ring + SL * R::slot, stq[SL]);
+    return true;
   };
-  for (int it = 0; it < mine; it += R::nslot) {
-    stream_step(it, std::integral_constant<int, 0>{});
-    if (it + 1 < mine) stream_step(it + 1, std::integral_constant<int, 1>{});
+  for (;;) {
+    if (!stream_step(std::integral_constant<int, 0>{})) break;
+    if (!stream_step(std::integral_constant<int, 1>{})) break;
     if constexpr (R::nslot == 3)
-      if (it + 2 < mine) stream_step(it + 2, std::integral_constant<int, 2>{});
+      if (!stream_step(std::integral_constant<int, 2>{})) break;
   }
   wait_vmcnt<0>();
   __syncthreads();  // every wave is done with the ring before it becomes the merge area
@@ -592,21 +643,21 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h, int t0, int t1
   if (lane == 0) {
 #pragma unroll
     for (int g = 0; g < GP; ++g) {
-      s_stat[(wave * GP + g) * 2] = m_run[g];
+      s_stat[(wave * GP + g) * 2] = m_run[g] + kLazyMax;  // the weights' effective reference
       s_stat[(wave * GP + g) * 2 + 1] = lh[g];
     }
   }
   __syncthreads();
   // combine the four waves; results for head g in m_out[g], l_out[g] and s_merge[g][:]
   const int tid = threadIdx.x;
-  for (int idx = tid; idx < GP * D; idx += kWaves * 64) {
+  for (int idx = tid; idx < GP * D; idx += NW * 64) {
     const int g = idx / D;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_stat[(w * GP + g) * 2]);
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, s_stat[(w * GP + g) * 2]);
     float acc = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const float lwv = s_stat[(w * GP + g) * 2 + 1];
       const float f = lwv > 0.f ? __builtin_amdgcn_exp2f(s_stat[(w * GP + g) * 2] - M) : 0.f;
       acc += f * s_merge[w * GP * D + idx];
@@ -616,10 +667,10 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h, int t0, int t1
   if (tid < GP) {
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_stat[(w * GP + tid) * 2]);
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, s_stat[(w * GP + tid) * 2]);
     float L = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const float lwv = s_stat[(w * GP + tid) * 2 + 1];
       L += lwv > 0.f ? lwv * __builtin_amdgcn_exp2f(s_stat[(w * GP + tid) * 2] - M) : 0.f;
     }
@@ -635,12 +686,13 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h, int t0, int t1
 template <int D, int GP>
 __device__ void split_recent(const DArgs& a, int b, int h, int R, float* s_p, float* s_merge, float* m_out,
                              float* l_out) {
+  constexpr int NW = split_waves<D, GP>();
   const int tid = threadIdx.x;
   const uint16_t* kb = a.rk + (((int64_t)b * a.Hkv + h) * a.W) * D;
   const uint16_t* vb = a.rv + (((int64_t)b * a.Hkv + h) * a.W) * D;
   // s_p reused as [GP][W] logits (W <= 4096 fits in the merge area instead when large)
   float* lg = s_merge;  // [GP][R] logits, then weights; R <= W
-  for (int idx = tid; idx < a.G * R; idx += kWaves * 64) {
+  for (int idx = tid; idx < a.G * R; idx += NW * 64) {
     const int g = idx / R, t = idx % R;
     const int64_t qoff = ((int64_t)b * a.Hq + h * a.G + g) * D;
     float acc = 0.f;
@@ -668,14 +720,14 @@ __device__ void split_recent(const DArgs& a, int b, int h, int R, float* s_p, fl
   __syncthreads();
   // acc[g][c] into s_p scratch area (GP * D floats available after the merge area)
   float* accs = s_merge + GP * a.W;
-  for (int idx = tid; idx < a.G * D; idx += kWaves * 64) {
+  for (int idx = tid; idx < a.G * D; idx += NW * 64) {
     const int g = idx / D, c = idx % D;
     float acc = 0.f;
     for (int t = 0; t < R; ++t) acc = __builtin_fmaf(lg[g * R + t], bf16_to_f32(vb[(int64_t)t * D + c]), acc);
     accs[idx] = acc;
   }
   __syncthreads();
-  for (int idx = tid; idx < a.G * D; idx += kWaves * 64) s_merge[idx] = accs[idx];
+  for (int idx = tid; idx < a.G * D; idx += NW * 64) s_merge[idx] = accs[idx];
   __syncthreads();
 }
 
@@ -685,11 +737,11 @@ __device__ void split_recent(const DArgs& a, int b, int h, int R, float* s_p, fl
 // s_pq: A rows = heads (fp16 hi/lo of q~ 2^-e_g, with 2^e_g above the head's
 // largest |q~_j| so fp16 cannot overflow), B = the 16 S tiles of the context,
 // three products per tile; wave w takes column tiles w, w + 4, ...
-template <int D>
+template <int D, int NW>
 __device__ __forceinline__ void rotate_project(const DArgs& a, const DevTables& dv, int b, int h, float* s_q, float* s_pq,
                                int* s_exp) {
   constexpr int P = D / 64;
-  constexpr int KT = D / 32, NT = D / 16, NTW = NT / kWaves;
+  constexpr int KT = D / 32, NT = D / 16, NTW = NT / NW;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int G = a.G;
   const int64_t q0 = ((int64_t)b * a.Hq + (int64_t)h * G) * D;
@@ -699,12 +751,12 @@ __device__ __forceinline__ void rotate_project(const DArgs& a, const DevTables& 
   for (int i = 0; i < NTW; ++i) {
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
-      const size_t tb = ((((size_t)(wave + kWaves * i)) * KT + kt) * 2) * 64 * 8;
+      const size_t tb = ((((size_t)(wave + NW * i)) * KT + kt) * 2) * 64 * 8;
       bhi[i][kt] = *reinterpret_cast<const f16x8*>(dv.s_tiles + tb + lane * 8);
       blo[i][kt] = *reinterpret_cast<const f16x8*>(dv.s_tiles + tb + 512 + lane * 8);
     }
   }
-  for (int g = wave; g < G; g += kWaves) {
+  for (int g = wave; g < G; g += NW) {
     float x[P];
 #pragma unroll
     for (int e = 0; e < P; ++e) {
@@ -763,7 +815,7 @@ __device__ __forceinline__ void rotate_project(const DArgs& a, const DevTables& 
   const float unscale = 1.0f / (float)(1 << kSScaleLog2);
 #pragma unroll
   for (int i = 0; i < NTW; ++i) {
-    const int nt = wave + kWaves * i;
+    const int nt = wave + NW * i;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
@@ -788,13 +840,14 @@ __device__ __forceinline__ void rotate_project(const DArgs& a, const DevTables& 
 // [w total / grid, (w + 1) total / grid), so consecutive items mostly share
 // (b, h) and reuse its rotated query operands.
 template <int D, int GP, int KB, int VB>
-__global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DArgs a, int pr) {
+__global__ __launch_bounds__((split_waves<D, GP>() * 64)) void decode_split_kernel(DArgs a, int pr) {
+  constexpr int NW = split_waves<D, GP>();
   constexpr int KT = D / 32;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   using SL = SplitLds<D, GP, KB, VB>;
   float* s_p = reinterpret_cast<float*>(lds);
-  float* s_stat = s_p + kWaves * SL::kPWave;
-  int32_t* s_blk = reinterpret_cast<int32_t*>(s_stat + kWaves * GP * 2);
+  float* s_stat = s_p + NW * SL::kPWave;
+  int32_t* s_blk = reinterpret_cast<int32_t*>(s_stat + NW * GP * 2);
   unsigned char* s_main = lds + SL::kMainOffset;
   float* s_merge = reinterpret_cast<float*>(s_main);
   __shared__ uint2 s_pair[256];  // centroid pair -> {bf16 hi parts, bf16 lo parts}
@@ -803,92 +856,74 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DArgs a, int 
   __shared__ __attribute__((aligned(16))) float s_q[GP * D];
   __shared__ __attribute__((aligned(16))) float s_pq[GP * D];
   __shared__ int s_exp[GP];
+  __shared__ int s_claim;  // next unclaimed step of the current item
   const int tid = threadIdx.x, lane = tid & 63;
 
   // tables: centroid pairs of this preset, +-1 patterns of sign bytes
   const DevTables& dv = a.dev[pr];
-  for (int i = tid; i < (1 << (2 * KB)); i += kWaves * 64) s_pair[i] = make_uint2(dv.pair_lut[2 * i], dv.pair_lut[2 * i + 1]);
+  static_assert((1 << (2 * KB)) <= NW * 64, "one centroid pair per thread");
+  // loaded here, stored after the scan's first loads are issued, so the two
+  // global round trips overlap
+  const uint2 pair_v = tid < (1 << (2 * KB)) ? make_uint2(dv.pair_lut[2 * tid], dv.pair_lut[2 * tid + 1]) : make_uint2(0u, 0u);
   {
     u32x4 w;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       w[e] = (((tid >> (2 * e)) & 1) ? 0x3F80u : 0xBF80u) | ((((tid >> (2 * e + 1)) & 1) ? 0x3F80u : 0xBF80u) << 16);
-    s_sgn[tid] = w;  // 256 threads, one entry each
+    if (tid < 256) s_sgn[tid] = w;  // one entry per thread
   }
-
-  // work list: exclusive prefix over sequences of Hkv * splits(b) for the
-  // sequences of this preset, in the (still unused) ring area
-  int* s_scan = reinterpret_cast<int*>(s_main);
-  {
-    int carry = 0;
-    for (int base = 0; base < a.B; base += kWaves * 64) {
-      const int bb = base + tid;
-      const int items = (bb < a.B && seq_preset_of(a, bb) == pr) ? a.Hkv * seq_splits(a, bb) : 0;
-      int* sc = s_scan + base;
-      if (bb < a.B) sc[tid] = items;
-      __syncthreads();
-      // Hillis-Steele inclusive scan of this block of 256 entries, in place
-      for (int off = 1; off < kWaves * 64; off <<= 1) {
-        const int v = (bb < a.B && tid >= off) ? sc[tid - off] : 0;
-        __syncthreads();
-        if (bb < a.B) sc[tid] += v;
-        __syncthreads();
-      }
-      const int last = min(kWaves * 64, a.B - base) - 1;
-      const int tot = sc[last];
-      __syncthreads();
-      if (bb < a.B) sc[tid] = carry + sc[tid] - items;  // exclusive
-      carry += tot;
-      __syncthreads();
-    }
-    if (tid == 0) s_scan[a.B] = carry;
-    __syncthreads();
-  }
-  const int total = s_scan[a.B];
-  const int i0 = (int)((int64_t)blockIdx.x * total / gridDim.x);
-  const int i1 = (int)((int64_t)(blockIdx.x + 1) * total / gridDim.x);
-  int b = 0, cur_base = 0;
-  if (i0 < i1) {
-    int lo = 0, hi = a.B - 1;  // largest b with s_scan[b] <= i0
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_scan[mid] <= i0) lo = mid; else hi = mid - 1;
-    }
-    b = lo;
-    cur_base = s_scan[b];
-  }
-  __syncthreads();  // the ring area is free again
 
   bf16x8 A1[KT][2], A3[KT];
   int ready_bh = -1;  // (b, h) whose query operands A1 / A3 hold
-  for (int item = i0; item < i1; ++item) {
-    // advance to the sequence holding this item (sequences of the other
-    // preset, or with no splits, hold none)
-    while (b < a.B && item - cur_base >= (seq_preset_of(a, b) == pr ? a.Hkv * seq_splits(a, b) : 0)) {
-      cur_base += seq_preset_of(a, b) == pr ? a.Hkv * seq_splits(a, b) : 0;
-      ++b;
-    }
-    if (b >= a.B) break;  // inconsistent with the scan: stop
-    const int local = item - cur_base;
-    const int nsp = seq_splits(a, b);
-    const int h = local / nsp, c = local % nsp;
-    const int Lc = seq_cached(a, b);
-    const int nq_chunks = (Lc + a.chunk - 1) / a.chunk;
 
-    if (c < nq_chunks) {
-      const int t0 = c * a.chunk;
-      const int t1 = min(t0 + a.chunk, Lc);
-      // stage the chunk's block ids (-1 past its end)
-      {
-        const int nblk = (t1 - t0 + 15) >> 4;
-        const int32_t* btrow = a.bt + (int64_t)b * a.max_blocks + (t0 >> 4);
-        const int64_t pblocks = a.pool_blocks[pr];
-        for (int i = tid; i < (a.chunk >> 4) + 2; i += kWaves * 64) {
-          const int blk = i < nblk ? btrow[i] : -1;
-          s_blk[i] = (blk >= 0 && (int64_t)blk < pblocks) ? blk : -1;
-        }
+  // One item: split c of KV head h of sequence b, which has Lc cached tokens.
+  // kDirect: at most one split per sequence (the output is written here).
+  auto run_item = [&](int b, int h, int c, int Lc, auto direct_c) {
+    constexpr bool kDirect = decltype(direct_c)::value;
+    using R = Rec<D, KB, VB>;
+    constexpr bool kEarlyRotate = D == 128;
+    constexpr int kStageRounds = (kMaxChunk / 16 + 2 + NW * 64 - 1) / (NW * 64);
+    const int nq_chunks = (Lc + a.chunk - 1) / a.chunk;
+    const bool cached = c < nq_chunks;  // uniform
+    const int t0 = c * a.chunk;
+    const int t1 = min(t0 + a.chunk, Lc);
+    const int bh = b * a.Hkv + h;
+    // One load phase per item: the chunk's block ids go to registers (read
+    // up to the end of the table row, masked past the chunk's end once the
+    // length is known), then (d = 128) the query rotation / projection of a
+    // new (b, h) issues its own loads, so the round trips overlap and all of
+    // it completes before the first cache step is requested.  In direct mode
+    // none of it waits for the sequence length.  With d = 256 the projection
+    // tiles take too many registers to share the phase; the rotation then
+    // runs after the first steps are requested.
+    if (kDirect || cached) {
+      const int nstage = (a.chunk >> 4) + 2;
+      const int row_left = a.max_blocks - (t0 >> 4);
+      const int32_t* btrow = a.bt + (int64_t)b * a.max_blocks + (t0 >> 4);
+      const int64_t pblocks = a.pool_blocks[pr];
+      int blk[kStageRounds];
+#pragma unroll
+      for (int r = 0; r < kStageRounds; ++r) {
+        const int i = tid + r * NW * 64;
+        blk[r] = (i < nstage && i < row_left) ? btrow[i] : -1;
       }
-      __syncthreads();
+      if (kEarlyRotate && bh != ready_bh) rotate_project<D, NW>(a, dv, b, h, s_q, s_pq, s_exp);
+      const int nblk = (t1 - t0 + 15) >> 4;
+#pragma unroll
+      for (int r = 0; r < kStageRounds; ++r) {
+        const int i = tid + r * NW * 64;
+        if (i < nstage) s_blk[i] = (i < nblk && blk[r] >= 0 && (int64_t)blk[r] < pblocks) ? blk[r] : -1;
+      }
+      // steps wave + NW k, k < nslot - 1, are handed out statically
+      if (tid == 0) s_claim = NW * (R::nslot - 1);
+      // every path through the masked stores above has its loads complete
+      // here; otherwise the compiler keeps a load pending on the path that
+      // skips a store and answers a later write of that register with a full
+      // vmcnt wait, which would also wait for the first cache steps
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    }
+    __syncthreads();
+    if (cached) {
       // A operands (built while the first steps stream in): rows 0..GP-1 =
       // hi parts of head rows, GP..2GP-1 = lo parts.  A1[kt][m] slot e holds
       // coordinate 8 kt + 4 m + {0,1,0,1,2,3,2,3}[e] of the lane quarter,
@@ -896,9 +931,8 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DArgs a, int 
       // coordinate 8 kt + e (sign bits in order).  log2(e) sm_scale is folded
       // into q~, sqrt(pi/2) / d log2(e) sm_scale into p.
       auto setup = [&](bf16x8 (&A1r)[KT][2], bf16x8 (&A3r)[KT]) {
-        const int bh = b * a.Hkv + h;
         if (bh == ready_bh) return;
-        rotate_project<D>(a, dv, b, h, s_q, s_pq, s_exp);
+        if (!kEarlyRotate) rotate_project<D, NW>(a, dv, b, h, s_q, s_pq, s_exp);
         const int arow = lane & 15, kq = lane >> 4;
         const int g = arow % GP;
         const bool is_lo = arow >= GP;
@@ -936,17 +970,104 @@ __global__ __launch_bounds__(kWaves * 64) void decode_split_kernel(DArgs a, int 
         ready_bh = bh;
       };
       split_cached_chunk<D, GP, KB, VB>(a, pr, h, t0, t1, s_blk, s_pair, s_sgn, s_p, s_main, s_stat, A1, A3,
-                                        s_m, s_l, b, setup);
-    } else {
+                                        s_m, s_l, b, &s_claim, setup);
+    } else if (!kDirect) {
       split_recent<D, GP>(a, b, h, seq_recent(a, b), s_p, s_merge, s_m, s_l);
     }
-    // write the partial: (m, l, acc[D]) per query head of this KV head
-    for (int idx = tid; idx < a.G * (D + 2); idx += kWaves * 64) {
-      const int g = idx / (D + 2), k = idx % (D + 2);
-      float v = k == 0 ? s_m[g] : (k == 1 ? s_l[g] : s_merge[g * D + (k - 2)]);
-      a.part[(((int64_t)b * a.Hq + h * a.G + g) * a.splits_cap + c) * (D + 2) + k] = v;
+    if (kDirect) {
+      // the only split of this (sequence, KV head): acc / l is the output
+      // (zero for a sequence with no tokens)
+      for (int idx = tid; idx < a.G * D; idx += NW * 64) {
+        const int g = idx / D;
+        const float l = cached ? s_l[g] : 0.f;
+        a.out[((int64_t)b * a.Hq + h * a.G) * D + idx] = l > 0.f ? s_merge[idx] / l : 0.f;
+      }
+    } else {
+      // write the partial: (m, l, acc[D]) per query head of this KV head
+      for (int idx = tid; idx < a.G * (D + 2); idx += NW * 64) {
+        const int g = idx / (D + 2), k = idx % (D + 2);
+        float v = k == 0 ? s_m[g] : (k == 1 ? s_l[g] : s_merge[g * D + (k - 2)]);
+        a.part[(((int64_t)b * a.Hq + h * a.G + g) * a.splits_cap + c) * (D + 2) + k] = v;
+      }
     }
+    // Drain this item's stores here, where nothing else is in flight: the
+    // compiler otherwise carries them into the next item and answers them
+    // with full vmcnt waits after that item's first cache steps are
+    // requested, which would also wait for those steps.
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
+  };
+
+  if (a.direct) {
+    // one item per (sequence, KV head), contiguous ranges per workgroup: no
+    // work list is needed
+    if (tid < (1 << (2 * KB))) s_pair[tid] = pair_v;
+    const int total = a.B * a.Hkv;
+    const int i0 = (int)((int64_t)blockIdx.x * total / gridDim.x);
+    const int i1 = (int)((int64_t)(blockIdx.x + 1) * total / gridDim.x);
+    for (int item = i0; item < i1; ++item) {
+      const int b = item / a.Hkv, h = item % a.Hkv;
+      if (seq_preset_of(a, b) != pr) continue;  // uniform
+      run_item(b, h, 0, seq_cached(a, b), std::true_type{});
+    }
+    return;
+  }
+
+  // work list: exclusive prefix over sequences of Hkv * splits(b) for the
+  // sequences of this preset, in the (still unused) ring area
+  int* s_scan = reinterpret_cast<int*>(s_main);
+  {
+    int carry = 0;
+    for (int base = 0; base < a.B; base += NW * 64) {
+      const int bb = base + tid;
+      const int items = (bb < a.B && seq_preset_of(a, bb) == pr) ? a.Hkv * seq_splits(a, bb) : 0;
+      int* sc = s_scan + base;
+      if (bb < a.B) sc[tid] = items;
+      if (base == 0 && tid < (1 << (2 * KB))) s_pair[tid] = pair_v;
+      __syncthreads();
+      // Hillis-Steele inclusive scan of this block of 256 entries, in place
+      for (int off = 1; off < NW * 64; off <<= 1) {
+        const int v = (bb < a.B && tid >= off) ? sc[tid - off] : 0;
+        __syncthreads();
+        if (bb < a.B) sc[tid] += v;
+        __syncthreads();
+      }
+      const int last = min(NW * 64, a.B - base) - 1;
+      const int tot = sc[last];
+      __syncthreads();
+      if (bb < a.B) sc[tid] = carry + sc[tid] - items;  // exclusive
+      carry += tot;
+      __syncthreads();
+    }
+    if (tid == 0) s_scan[a.B] = carry;
+    __syncthreads();
+  }
+  const int total = s_scan[a.B];
+  const int i0 = (int)((int64_t)blockIdx.x * total / gridDim.x);
+  const int i1 = (int)((int64_t)(blockIdx.x + 1) * total / gridDim.x);
+  int b = 0, cur_base = 0;
+  if (i0 < i1) {
+    int lo = 0, hi = a.B - 1;  // largest b with s_scan[b] <= i0
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_scan[mid] <= i0) lo = mid; else hi = mid - 1;
+    }
+    b = lo;
+    cur_base = s_scan[b];
+  }
+  __syncthreads();  // the ring area is free again
+
+  for (int item = i0; item < i1; ++item) {
+    // advance to the sequence holding this item (sequences of the other
+    // preset, or with no splits, hold none)
+    while (b < a.B && item - cur_base >= (seq_preset_of(a, b) == pr ? a.Hkv * seq_splits(a, b) : 0)) {
+      cur_base += seq_preset_of(a, b) == pr ? a.Hkv * seq_splits(a, b) : 0;
+      ++b;
+    }
+    if (b >= a.B) break;  // inconsistent with the scan: stop
+    const int local = item - cur_base;
+    const int nsp = seq_splits(a, b);
+    run_item(b, local / nsp, local % nsp, seq_cached(a, b), std::false_type{});
   }
 }
 
@@ -1018,7 +1139,7 @@ static hipError_t launch_split(const DArgs& a, int pr, hipStream_t s) {
   (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   // persistent workgroups: as many as fit on the chip at once (LDS bounds it)
   const int per_cu = std::max(1, std::min(8, (int)((160 * 1024) / lds)));
-  hipLaunchKernelGGL(kern, dim3(cus * per_cu), dim3(kWaves * 64), lds, s, a, pr);
+  hipLaunchKernelGGL(kern, dim3(cus * per_cu), dim3(SL::NW * 64), lds, s, a, pr);
   return hipGetLastError();
 }
 
@@ -1030,8 +1151,13 @@ static hipError_t dispatch_preset(const DArgs& a, int pr, int kb, int vb, hipStr
 }
 
 template <int D>
-static hipError_t launch_all(const DArgs& a, const tq_decode_args* args, hipStream_t s) {
+static hipError_t launch_all(const DArgs& a0, const tq_decode_args* args, hipStream_t s) {
   hipError_t e = hipSuccess;
+  // with no recent window and max_seq_len <= chunk every sequence has at most
+  // one split (cached lengths are clamped to max_seq_len): the split kernel
+  // then writes the output itself and the combine pass is skipped
+  DArgs a = a0;
+  a.direct = (args->recent_k == nullptr && args->max_seq_len <= args->chunk_tokens) ? 1 : 0;
   if (args->split_events[0] && (e = hipEventRecord((hipEvent_t)args->split_events[0], s)) != hipSuccess) return e;
   for (int pr = 0; pr < args->num_presets; ++pr) {
     const tq_ctx* c = args->ctx[pr];
@@ -1039,6 +1165,7 @@ static hipError_t launch_all(const DArgs& a, const tq_decode_args* args, hipStre
     if (e != hipSuccess) return e;
   }
   if (args->split_events[1] && (e = hipEventRecord((hipEvent_t)args->split_events[1], s)) != hipSuccess) return e;
+  if (a.direct) return hipSuccess;
   hipLaunchKernelGGL(decode_combine_kernel<D>, dim3(a.B * a.Hq), dim3(kCombineThreads), 0, s, a);
   return hipGetLastError();
 }

@@ -465,8 +465,8 @@ int check_decode_shape(const tq_decode_args* a) {
     set_error("decode: query heads per KV head %d > 8 is not supported", G);
     return TQ_EUNSUPPORTED;
   }
-  if (a->chunk_tokens < 32 || a->chunk_tokens % 32 || a->chunk_tokens > 4096) {
-    set_error("decode: chunk_tokens %d must be a multiple of 32 in [32, 4096]", a->chunk_tokens);
+  if (a->chunk_tokens < 32 || a->chunk_tokens % 32 || a->chunk_tokens > 8192) {
+    set_error("decode: chunk_tokens %d must be a multiple of 32 in [32, 8192]", a->chunk_tokens);
     return TQ_EINVAL;
   }
   if (a->max_seq_len < 0 || a->max_blocks_per_seq < 0 || (int64_t)a->max_seq_len > 16ll * a->max_blocks_per_seq) {

@@ -1,5 +1,5 @@
 """GPU parity at the workloads' full sizes, in the launch configuration the
-benchmark uses (chunk_tokens = 4096), on sampled outputs.
+benchmark uses (chunk_tokens = 8192), on sampled outputs.
 
 The whole cache is written by tq_quantize_store from seeded inputs generated
 on the device; the records of the sampled (sequence, KV head) pairs are then
@@ -31,7 +31,7 @@ from parity import oracle_params, output_errors, score_errors
 pytestmark = pytest.mark.gpu
 
 TOL = 1e-3
-CHUNK = 4096
+CHUNK = 8192
 
 
 def _seq_inputs(seed, b, L, Hkv, d, p, factor):
