@@ -406,26 +406,40 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h, int t0, int t1
       }
     }
     // ------------------------------------------------------------ softmax
-    // Each lane holds four distinct (head, token) logits (see x above).
-    float y0 = x[0], y1 = x[1], y2 = x[2], y3 = x[3];
-    row_max16x4(y0, y1, y2, y3);
-    const float ys[4] = {y0, y1, y2, y3};
-    float mt[GP];
-    bool grow = false;
+    // Each lane holds four distinct (head, token) logits (see x above).  The
+    // block maxima are only needed when some logit passes its head's
+    // reference by more than kLazyMax: that test is one compare per logit
+    // and a ballot; the maxima are formed inside the (rare) rescale branch.
+    bool grow;
+    {
+      const int ln = (int)opaque_u32((uint32_t)lane);
+      const bool hi = GP == 8 && (ln & 16);  // GP = 8: lanes 16-31 / 48-63 carry heads 4..7
+      uint64_t over = 0;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int yr = __float_as_int(ys[r]);
-      if constexpr (GP == 4) {
-        mt[r] = fmaxf(__int_as_float(__builtin_amdgcn_readlane(yr, 0)), __int_as_float(__builtin_amdgcn_readlane(yr, 16)));
-      } else {
-        mt[r] = fmaxf(__int_as_float(__builtin_amdgcn_readlane(yr, 0)), __int_as_float(__builtin_amdgcn_readlane(yr, 32)));
-        mt[4 + r] = fmaxf(__int_as_float(__builtin_amdgcn_readlane(yr, 16)), __int_as_float(__builtin_amdgcn_readlane(yr, 48)));
+      for (int r = 0; r < 4; ++r) {
+        const float lim = (hi ? m_run[(4 + r) % GP] : m_run[r]) + kLazyMax;
+        over |= __builtin_amdgcn_ballot_w64(x[r] > lim);
       }
+      if constexpr (GP == 4) over &= 0xFFFFFFFFull;  // lanes 32-63 hold no logits
+      grow = over != 0;
     }
-#pragma unroll
-    for (int g = 0; g < GP; ++g) grow |= mt[g] > m_run[g] + kLazyMax;
     if (grow) {  // uniform: some head's block max passed its reference; rescale what was accumulated
       const int ln = (int)opaque_u32((uint32_t)lane);  // lane predicates are formed here, not kept live
+      // block maxima: 16-lane row maxima, then the rows holding each head
+      float y0 = x[0], y1 = x[1], y2 = x[2], y3 = x[3];
+      row_max16x4(y0, y1, y2, y3);
+      const float ys[4] = {y0, y1, y2, y3};
+      float mt[GP];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int yr = __float_as_int(ys[r]);
+        if constexpr (GP == 4) {
+          mt[r] = fmaxf(__int_as_float(__builtin_amdgcn_readlane(yr, 0)), __int_as_float(__builtin_amdgcn_readlane(yr, 16)));
+        } else {
+          mt[r] = fmaxf(__int_as_float(__builtin_amdgcn_readlane(yr, 0)), __int_as_float(__builtin_amdgcn_readlane(yr, 32)));
+          mt[4 + r] = fmaxf(__int_as_float(__builtin_amdgcn_readlane(yr, 16)), __int_as_float(__builtin_amdgcn_readlane(yr, 48)));
+        }
+      }
       float alpha[GP];
 #pragma unroll
       for (int g = 0; g < GP; ++g) {
