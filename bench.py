@@ -128,7 +128,7 @@ def bench_quantize(torch, tq, synth, steps, warmup):
     return {"workload": "quantize-65536tok-hkv8-d128-bf16-outliers0.5%x20", **res}
 
 
-def cpu_baseline(synth, seqs=2):
+def cpu_baseline(synth, seqs=24):
     """The oracle on a bounded sample of the decode workload: cache encoded
     by the oracle (not timed), then its decode of `seqs` sequences timed."""
     import numpy as np
