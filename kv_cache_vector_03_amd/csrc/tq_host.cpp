@@ -286,7 +286,7 @@ extern "C" int tq_codebook_init(const tq_preset* p, const int8_t* signs, const f
     sg2[i] = (float)c->signs[d + i];
   }
   const int NT = d / 16, KT = d / 32;
-  std::vector<uint16_t> tiles((size_t)NT * KT * 2 * 64 * 8);
+  std::vector<uint16_t> tiles((size_t)NT * KT * 2 * 64 * 8), tiles_d2(tiles.size());
   const float sscale = std::ldexp(1.0f, kSScaleLog2);
   for (int nt = 0; nt < NT; ++nt)
     for (int kt = 0; kt < KT; ++kt)
@@ -300,6 +300,9 @@ extern "C" int tq_codebook_init(const tq_preset* p, const int8_t* signs, const f
           size_t base = (((size_t)nt * KT + kt) * 2) * 64 * 8;
           tiles[base + (size_t)l * 8 + e] = h;
           tiles[base + 64 * 8 + (size_t)l * 8 + e] = lo;
+          const uint16_t flip = sg2[col] < 0.f ? 0x8000u : 0u;  // fp16 sign bit
+          tiles_d2[base + (size_t)l * 8 + e] = h ^ flip;
+          tiles_d2[base + 64 * 8 + (size_t)l * 8 + e] = lo ^ flip;
         }
   const int P = 1 << (2 * kb);
   std::vector<uint32_t> pair((size_t)P * 2);
@@ -315,7 +318,8 @@ extern "C" int tq_codebook_init(const tq_preset* p, const int8_t* signs, const f
   // ---- one device allocation, 256-byte aligned pieces
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   size_t o_c = 0, o_t = up(o_c + 4 * L), o_s1 = up(o_t + 4 * L), o_s2 = up(o_s1 + 4 * d), o_S = up(o_s2 + 4 * d),
-         o_tiles = up(o_S + 4 * (size_t)d * d), o_pair = up(o_tiles + 2 * tiles.size()),
+         o_tiles = up(o_S + 4 * (size_t)d * d), o_tiles2 = up(o_tiles + 2 * tiles.size()),
+         o_pair = up(o_tiles2 + 2 * tiles_d2.size()),
          total = up(o_pair + 4 * pair.size());
   if (hipGetDevice(&c->device) != hipSuccess) {
     set_error("tq_codebook_init: no HIP device");
@@ -335,6 +339,7 @@ extern "C" int tq_codebook_init(const tq_preset* p, const int8_t* signs, const f
   std::memcpy(img.data() + o_s2, sg2.data(), 4 * d);
   std::memcpy(img.data() + o_S, c->S.data(), 4 * (size_t)d * d);
   std::memcpy(img.data() + o_tiles, tiles.data(), 2 * tiles.size());
+  std::memcpy(img.data() + o_tiles2, tiles_d2.data(), 2 * tiles_d2.size());
   std::memcpy(img.data() + o_pair, pair.data(), 4 * pair.size());
   if (hipMemcpy(base, img.data(), total, hipMemcpyHostToDevice) != hipSuccess) {
     set_error("tq_codebook_init: upload failed");
@@ -348,6 +353,7 @@ extern "C" int tq_codebook_init(const tq_preset* p, const int8_t* signs, const f
   c->dev.signs2 = (const float*)(base + o_s2);
   c->dev.S = (const float*)(base + o_S);
   c->dev.s_tiles = (const uint16_t*)(base + o_tiles);
+  c->dev.s_tiles_d2 = (const uint16_t*)(base + o_tiles2);
   c->dev.pair_lut = (const uint32_t*)(base + o_pair);
   *out = c;
   return TQ_OK;

@@ -22,6 +22,9 @@ struct DevTables {
   // of (S * 2^kSScaleLog2): tile (nt, kt) holds lane l, element e =
   // S[16 nt + l%16][32 kt + 8 (l/16) + e]; layout [nt][kt][hi,lo][64][8] fp16.
   const uint16_t* s_tiles = nullptr;
+  // The same tiles for S diag(D2) (the columns j with D2_j = -1 negated,
+  // exactly: negating an fp16 hi/lo pair negates both parts).
+  const uint16_t* s_tiles_d2 = nullptr;
   // Decode pair table: entry a | b << k_bits = (bf16 hi c[a], bf16 hi c[b]),
   // (bf16 lo c[a], bf16 lo c[b]) as two dwords; [2^(2 k_bits)][2] uint32.
   const uint32_t* pair_lut = nullptr;

@@ -69,6 +69,37 @@ __device__ __forceinline__ void load_row_part(const void* base, int64_t elem_off
   }
 }
 
+// Lloyd-Max index of a rotated coordinate u for an odd-symmetric codebook
+// (c[L-1-k] = -c[k], t[L-2-k] = -t[k], t[H-1] = 0 with H = L/2), from its
+// magnitude: cnt = #{upper thresholds t[H..L-2] below |u|}, index = H + cnt
+// for u > 0 and H - 1 - cnt otherwise (= cnt ^ H, cnt ^ (H-1)), residual
+// u - c[index] = +-(|u| - c[H + cnt]).  Identical to the count #{t < u}
+// except where |u| equals a threshold exactly.  tU = t[H..L-2]; s_cU holds
+// c[H..L-1] in LDS.
+template <int KB>
+__device__ __forceinline__ void sym_code(float u, const float (&tU)[(1 << KB) / 2 - 1], const float* s_cU,
+                                         uint32_t& code, float& r) {
+  constexpr uint32_t H = (1u << KB) / 2;
+  const float m = fabsf(u);
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int i = 0; i < (int)H - 1; ++i) cnt += m > tU[i] ? 1u : 0u;
+  const float d = m - s_cU[cnt];
+  const bool pos = u > 0.f;
+  code = cnt ^ (pos ? H : H - 1u);
+  r = pos ? d : -d;
+}
+
+// One cross-lane Walsh-Hadamard stage over the 4 lanes of a row (partner =
+// lane ^ M): lower lanes x + y, upper lanes y - x, as y + sg * x with
+// sg = +-1 (one rounding, identical to the add / subtract).
+template <int M>
+__device__ __forceinline__ float wht_quad(float x, float sg) {
+  constexpr int kCtrl = M == 1 ? 0xB1 : 0x4E;  // quad_perm [1,0,3,2] / [2,3,0,1]
+  const float y = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, false));
+  return __builtin_fmaf(sg, x, y);
+}
+
 template <int D, int KB, int VB, bool BF16>
 __global__ __launch_bounds__(kQWaves<D> * 64) void quantize_kernel(QArgs a) {
   constexpr int E = D / 4;
@@ -87,27 +118,46 @@ __global__ __launch_bounds__(kQWaves<D> * 64) void quantize_kernel(QArgs a) {
   const int row = lane >> 2, part = lane & 3;
 
   if constexpr (QLds<D>::kTilesInLds) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(a.dev.s_tiles);
+    const u32x4* src = reinterpret_cast<const u32x4*>(a.dev.s_tiles_d2);
     u32x4* dst = reinterpret_cast<u32x4*>(s_tiles);
     constexpr int n16 = (int)(QLds<D>::tiles_bytes / 16);
     for (int i = tid; i < n16; i += kQWaves<D> * 64) dst[i] = src[i];
   }
-  if (tid < L) s_c[tid] = a.dev.centroids[tid];
-  float thr[L - 1];
+  // upper half of the (odd-symmetric) codebook
+  constexpr int H = L / 2;
+  if (tid < H) s_c[tid] = a.dev.centroids[H + tid];
+  float tU[H - 1];
 #pragma unroll
-  for (int i = 0; i < L - 1; ++i) thr[i] = a.dev.thresholds[i];
+  for (int i = 0; i < H - 1; ++i) tU[i] = a.dev.thresholds[H + i];
   // D1 / D2 signs of this lane's coordinates as bit masks (bit = negative)
-  uint32_t m1[SW], m2[SW];
+  // D1 as sign-bit patterns: fp32 inputs per element (m1), bf16 inputs per
+  // packed pair (bits 15 and 31 of each input dword).  D2 acts after the
+  // rotation: the kernel works on D2-free coordinates u' (u = D2 u'), whose
+  // index under the symmetric codebook is index(u) ^ (L-1) where D2 = -1
+  // (applied to the packed code words, pattern m2c) and whose residual is
+  // D2 r, projected with the D2-folded tiles.
+  constexpr int CW = E * KB / 32;  // code dwords per lane
+  uint32_t m1[SW], p1[E / 2], m2c[CW];
 #pragma unroll
   for (int w = 0; w < SW; ++w) {
     m1[w] = 0;
-    m2[w] = 0;
 #pragma unroll
-    for (int b = 0; b < 32; ++b) {
-      m1[w] |= (a.dev.signs1[part * E + 32 * w + b] < 0.f ? 1u : 0u) << b;
-      m2[w] |= (a.dev.signs2[part * E + 32 * w + b] < 0.f ? 1u : 0u) << b;
+    for (int b = 0; b < 32; ++b) m1[w] |= (a.dev.signs1[part * E + 32 * w + b] < 0.f ? 1u : 0u) << b;
+  }
+#pragma unroll
+  for (int i = 0; i < E / 2; ++i)
+    p1[i] = (a.dev.signs1[part * E + 2 * i] < 0.f ? 0x8000u : 0u) | (a.dev.signs1[part * E + 2 * i + 1] < 0.f ? 0x80000000u : 0u);
+#pragma unroll
+  for (int i = 0; i < CW; ++i) m2c[i] = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if (a.dev.signs2[part * E + e] < 0.f) {
+      const int bp = e * KB;
+      m2c[bp / 32] |= (uint32_t)(L - 1) << (bp % 32);
+      if ((bp % 32) + KB > 32) m2c[bp / 32 + 1] |= (uint32_t)(L - 1) >> (32 - bp % 32);
     }
   }
+  const float sg_1 = (part & 1) ? -1.f : 1.f, sg_2 = (part & 2) ? -1.f : 1.f;
   __syncthreads();
 
   uint16_t* a_hi = s_a + (size_t)wave * 2 * 16 * RS;
@@ -124,20 +174,36 @@ __global__ __launch_bounds__(kQWaves<D> * 64) void quantize_kernel(QArgs a) {
 
     // ---- key: norm, rotation, Lloyd-Max index, residual
     float x[E];
-    if (valid) {
-      load_row_part<BF16>(a.k, th * D + part * E, x);
-    } else {
+    if constexpr (BF16) {
+      // D1 applied to the packed pairs as they are unpacked
+      const u32x4* p = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.k) + (valid ? th * D + part * E : 0));
 #pragma unroll
-      for (int e = 0; e < E; ++e) x[e] = 0.f;
+      for (int i = 0; i < E / 8; ++i) {
+        u32x4 w = valid ? __builtin_nontemporal_load(p + i) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t ws = w[j] ^ p1[4 * i + j];
+          x[8 * i + 2 * j] = __uint_as_float(ws << 16);
+          x[8 * i + 2 * j + 1] = __uint_as_float(ws & 0xFFFF0000u);
+        }
+      }
+    } else {
+      if (valid) {
+        load_row_part<BF16>(a.k, th * D + part * E, x);
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) x[e] = 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) x[e] = __uint_as_float(__float_as_uint(x[e]) ^ (((m1[e / 32] >> (e % 32)) & 1u) << 31));
     }
+    // the norm is sign-blind: taken from the D1-flipped values
     float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < E; ++e) ss = __builtin_fmaf(x[e], x[e], ss);
     ss = group_sum<4>(ss);
     const float n = __builtin_sqrtf(ss);
     const bool zero = !(n > 0.f);
-#pragma unroll
-    for (int e = 0; e < E; ++e) x[e] = __uint_as_float(__float_as_uint(x[e]) ^ (((m1[e / 32] >> (e % 32)) & 1u) << 31));
 #pragma unroll
     for (int hs = 1; hs < E; hs <<= 1) {
 #pragma unroll
@@ -150,26 +216,19 @@ __global__ __launch_bounds__(kQWaves<D> * 64) void quantize_kernel(QArgs a) {
       }
     }
 #pragma unroll
-    for (int m = 1; m <= 2; m <<= 1) {
-      const bool upper = (part & m) != 0;
+    for (int e = 0; e < E; ++e) x[e] = wht_quad<1>(x[e], sg_1);
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        float y = __shfl_xor(x[e], m, 64);
-        x[e] = upper ? (y - x[e]) : (x[e] + y);
-      }
-    }
+    for (int e = 0; e < E; ++e) x[e] = wht_quad<2>(x[e], sg_2);
     const float inv = zero ? 0.f : inv_sqrt_d / n;
     uint32_t idx[E];
     float r2 = 0.f;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      float u = __uint_as_float(__float_as_uint(x[e] * inv) ^ (((m2[e / 32] >> (e % 32)) & 1u) << 31));
-      uint32_t c = 0;
-#pragma unroll
-      for (int i = 0; i < L - 1; ++i) c += (u > thr[i]) ? 1u : 0u;
-      c = zero ? 0u : c;
-      float r = zero ? 0.f : u - s_c[c];
+      uint32_t c;
+      float r;
+      sym_code<KB>(x[e] * inv, tU, s_c, c, r);  // D2-free index and residual
       idx[e] = c;
+      r = zero ? 0.f : r;
       r2 = __builtin_fmaf(r, r, r2);
       x[e] = r;
     }
@@ -207,8 +266,8 @@ __global__ __launch_bounds__(kQWaves<D> * 64) void quantize_kernel(QArgs a) {
           bhi = *reinterpret_cast<const f16x8*>(s_tiles + tb + lane * 8);
           blo = *reinterpret_cast<const f16x8*>(s_tiles + tb + 512 + lane * 8);
         } else {
-          bhi = *reinterpret_cast<const f16x8*>(a.dev.s_tiles + tb + lane * 8);
-          blo = *reinterpret_cast<const f16x8*>(a.dev.s_tiles + tb + 512 + lane * 8);
+          bhi = *reinterpret_cast<const f16x8*>(a.dev.s_tiles_d2 + tb + lane * 8);
+          blo = *reinterpret_cast<const f16x8*>(a.dev.s_tiles_d2 + tb + 512 + lane * 8);
         }
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[kt], bhi, acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[kt], blo, acc, 0, 0, 0);
@@ -229,7 +288,6 @@ __global__ __launch_bounds__(kQWaves<D> * 64) void quantize_kernel(QArgs a) {
     uint8_t* base = a.pool + ((int64_t)(slot >> 4) * a.hkv + h) * a.rec;
     const int s = slot & 15;
     {
-      constexpr int CW = E * KB / 32;  // code dwords per lane
       uint32_t w[CW];
 #pragma unroll
       for (int i = 0; i < CW; ++i) w[i] = 0;
@@ -239,6 +297,9 @@ __global__ __launch_bounds__(kQWaves<D> * 64) void quantize_kernel(QArgs a) {
         w[bp / 32] |= idx[e] << (bp % 32);
         if ((bp % 32) + KB > 32) w[bp / 32 + 1] |= idx[e] >> (32 - bp % 32);
       }
+      // D2: index(-u') = index(u') ^ (L-1); a zero vector keeps all-zero codes
+#pragma unroll
+      for (int i = 0; i < CW; ++i) w[i] = zero ? 0u : (w[i] ^ m2c[i]);
       uint32_t qw[SW];
 #pragma unroll
       for (int i = 0; i < SW; ++i) {
@@ -280,15 +341,34 @@ __global__ __launch_bounds__(kQWaves<D> * 64) void quantize_kernel(QArgs a) {
       const uint16_t s16 = f32_to_f16_bits((mx - mn) / LV);
       const uint16_t z16 = f32_to_f16_bits(mn);
       const float sc = f16_bits_to_f32(s16), zz = f16_bits_to_f32(z16);
+      // q = rint((v - z) / s) with the IEEE quotient.  The product with the
+      // rounded reciprocal lies within 3e-6 of that quotient (|q| <= 16), so
+      // it rounds the same way unless it falls within kVBand of a
+      // half-integer; such lanes redo the group with the division.
+      constexpr float kVBand = 8e-6f;
+      const float rs = 1.0f / sc;
       uint32_t vw[VB];
 #pragma unroll
       for (int i = 0; i < VB; ++i) vw[i] = 0;
+      bool near = false;
 #pragma unroll
       for (int e = 0; e < 32; ++e) {
-        float q = __builtin_rintf((x[32 * gl + e] - zz) / sc);
-        q = fminf(fmaxf(q, 0.f), LV);
+        const float t = (x[32 * gl + e] - zz) * rs;
+        const float q0 = __builtin_rintf(t);
+        near |= fabsf(t - q0) >= 0.5f - kVBand;
+        const float q = fminf(fmaxf(q0, 0.f), LV);
         uint32_t qi = (sc != 0.f) ? (uint32_t)q : 0u;
         vw[(e * VB) / 32] |= qi << ((e * VB) % 32);
+      }
+      if (near && sc != 0.f) {
+#pragma unroll
+        for (int i = 0; i < VB; ++i) vw[i] = 0;
+#pragma unroll
+        for (int e = 0; e < 32; ++e) {
+          float q = __builtin_rintf((x[32 * gl + e] - zz) / sc);
+          q = fminf(fmaxf(q, 0.f), LV);
+          vw[(e * VB) / 32] |= (uint32_t)q << ((e * VB) % 32);
+        }
       }
       if (store) {
         const int g = part * GL + gl;
