@@ -790,13 +790,18 @@ __device__ __forceinline__ void rotate_project(const DArgs& a, const DevTables& 
         }
       }
     }
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-      const bool upper = (lane & m) != 0;
+    {
+      const float s1 = lane_sign<1>(lane), s2 = lane_sign<2>(lane), s4 = lane_sign<4>(lane);
+      const float s8 = lane_sign<8>(lane), s16 = lane_sign<16>(lane), s32 = lane_sign<32>(lane);
 #pragma unroll
       for (int e = 0; e < P; ++e) {
-        const float y = __shfl_xor(x[e], m, 64);
-        x[e] = upper ? (y - x[e]) : (x[e] + y);
+        float v = x[e];
+        v = wht_xlane<1>(v, s1);
+        v = wht_xlane<2>(v, s2);
+        v = wht_xlane<4>(v, s4);
+        v = wht_xlane<8>(v, s8);
+        v = wht_xlane<16>(v, s16);
+        x[e] = wht_xlane<32>(v, s32);
       }
     }
     const float inv = 1.0f / __builtin_sqrtf((float)D);
@@ -808,8 +813,7 @@ __device__ __forceinline__ void rotate_project(const DArgs& a, const DevTables& 
       s_q[g * D + j] = v;
       amax = fmaxf(amax, fabsf(v));
     }
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+    amax = wave_max_xl(amax);
     if (lane == 0) s_exp[g] = amax > 0.f ? (int)((__float_as_uint(amax) >> 23) & 0xFFu) - 126 : 0;
   }
   __syncthreads();

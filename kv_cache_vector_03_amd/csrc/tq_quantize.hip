@@ -201,7 +201,7 @@ __global__ __launch_bounds__(kQWaves<D> * 64) void quantize_kernel(QArgs a) {
     float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < E; ++e) ss = __builtin_fmaf(x[e], x[e], ss);
-    ss = group_sum<4>(ss);
+    ss = quad_sum_xl(ss);
     const float n = __builtin_sqrtf(ss);
     const bool zero = !(n > 0.f);
 #pragma unroll
@@ -232,7 +232,7 @@ __global__ __launch_bounds__(kQWaves<D> * 64) void quantize_kernel(QArgs a) {
       r2 = __builtin_fmaf(r, r, r2);
       x[e] = r;
     }
-    const float gamma = __builtin_sqrtf(group_sum<4>(r2));
+    const float gamma = __builtin_sqrtf(quad_sum_xl(r2));
 
     // ---- stage the scaled residual as fp16 hi/lo rows for the MFMA A operand
 #pragma unroll
@@ -417,13 +417,6 @@ __device__ __forceinline__ void load_few(const void* base, int64_t elem_off, flo
   }
 }
 
-template <int D>
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m, 64);
-  return x;
-}
-
 template <int D, int KB, int VB, bool BF16>
 __global__ __launch_bounds__(kRowWaves * 64) void quantize_rows_kernel(QArgs a) {
   constexpr int P = D / 64;
@@ -460,12 +453,25 @@ __global__ __launch_bounds__(kRowWaves * 64) void quantize_rows_kernel(QArgs a) 
 #pragma unroll
   for (int i = 0; i < L - 1; ++i) thr[i] = a.dev.thresholds[i];
   if (tid < L) s_cent[tid] = a.dev.centroids[tid];
+  // this wave's projection tiles (column tiles wave, wave + 4, ...): they do
+  // not depend on the token, so their round trip overlaps the one above
+  constexpr int NTW = NT / kRowWaves;
+  f16x8 bhi[NTW][KT], blo[NTW][KT];
+#pragma unroll
+  for (int i = 0; i < NTW; ++i) {
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+      const size_t tb = ((((size_t)(wave + kRowWaves * i)) * KT + kt) * 2) * 64 * 8;
+      bhi[i][kt] = *reinterpret_cast<const f16x8*>(a.dev.s_tiles + tb + lane * 8);
+      blo[i][kt] = *reinterpret_cast<const f16x8*>(a.dev.s_tiles + tb + 512 + lane * 8);
+    }
+  }
 
   // ---- key: norm, D1, Walsh-Hadamard, 1/sqrt(d) n, D2, Lloyd-Max index, residual
   float ss = 0.f;
 #pragma unroll
   for (int e = 0; e < P; ++e) ss = __builtin_fmaf(x[e], x[e], ss);
-  const float n = __builtin_sqrtf(wave_sum<D>(ss));
+  const float n = __builtin_sqrtf(wave_sum_xl(ss));
   const bool zero = !(n > 0.f);
 #pragma unroll
   for (int e = 0; e < P; ++e) x[e] *= sg1[e];
@@ -480,13 +486,19 @@ __global__ __launch_bounds__(kRowWaves * 64) void quantize_rows_kernel(QArgs a) 
       }
     }
   }
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    const bool upper = (lane & m) != 0;
+  // the lane-index bits of the transform: butterflies between lanes l, l ^ m
+  {
+    const float s1 = lane_sign<1>(lane), s2 = lane_sign<2>(lane), s4 = lane_sign<4>(lane);
+    const float s8 = lane_sign<8>(lane), s16 = lane_sign<16>(lane), s32 = lane_sign<32>(lane);
 #pragma unroll
     for (int e = 0; e < P; ++e) {
-      const float y = __shfl_xor(x[e], m, 64);
-      x[e] = upper ? (y - x[e]) : (x[e] + y);
+      float v = x[e];
+      v = wht_xlane<1>(v, s1);
+      v = wht_xlane<2>(v, s2);
+      v = wht_xlane<4>(v, s4);
+      v = wht_xlane<8>(v, s8);
+      v = wht_xlane<16>(v, s16);
+      x[e] = wht_xlane<32>(v, s32);
     }
   }
   __syncthreads();  // s_cent
@@ -504,7 +516,7 @@ __global__ __launch_bounds__(kRowWaves * 64) void quantize_rows_kernel(QArgs a) 
     s_r[wave][j0 + e] = r * (float)(1 << kRScaleLog2);
     s_code[wave][j0 + e] = (uint8_t)c;
   }
-  const float gamma = __builtin_sqrtf(wave_sum<D>(r2));
+  const float gamma = __builtin_sqrtf(wave_sum_xl(r2));
   __syncthreads();  // every wave's residual is in LDS
 
   // ---- z = S r for the workgroup's token-heads (A rows 0..3); wave w takes
@@ -521,17 +533,6 @@ __global__ __launch_bounds__(kRowWaves * 64) void quantize_rows_kernel(QArgs a) 
         const uint16_t lb = f32_to_f16_bits(v - f16_bits_to_f32(hb));
         ahi[kt][e] = __builtin_bit_cast(_Float16, hb);
         alo[kt][e] = __builtin_bit_cast(_Float16, lb);
-      }
-    }
-    constexpr int NTW = NT / kRowWaves;
-    f16x8 bhi[NTW][KT], blo[NTW][KT];
-#pragma unroll
-    for (int i = 0; i < NTW; ++i) {
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-        const size_t tb = ((((size_t)(wave + kRowWaves * i)) * KT + kt) * 2) * 64 * 8;
-        bhi[i][kt] = *reinterpret_cast<const f16x8*>(a.dev.s_tiles + tb + lane * 8);
-        blo[i][kt] = *reinterpret_cast<const f16x8*>(a.dev.s_tiles + tb + 512 + lane * 8);
       }
     }
 #pragma unroll
@@ -587,11 +588,12 @@ __global__ __launch_bounds__(kRowWaves * 64) void quantize_rows_kernel(QArgs a) 
     mn = fminf(mn, vx[e]);
     mx = fmaxf(mx, vx[e]);
   }
-#pragma unroll
-  for (int m = 1; m < GLN; m <<= 1) {
-    mn = fminf(mn, __shfl_xor(mn, m, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, m, 64));
-  }
+  mn = __uint_as_float(group_reduce_xl<GLN>(__float_as_uint(mn), [](uint32_t p, uint32_t q) {
+    return __float_as_uint(fminf(__uint_as_float(p), __uint_as_float(q)));
+  }));
+  mx = __uint_as_float(group_reduce_xl<GLN>(__float_as_uint(mx), [](uint32_t p, uint32_t q) {
+    return __float_as_uint(fmaxf(__uint_as_float(p), __uint_as_float(q)));
+  }));
   const uint16_t s16 = f32_to_f16_bits((mx - mn) / LV);
   const uint16_t z16 = f32_to_f16_bits(mn);
   const float sc = f16_bits_to_f32(s16), zz = f16_bits_to_f32(z16);
@@ -605,8 +607,7 @@ __global__ __launch_bounds__(kRowWaves * 64) void quantize_rows_kernel(QArgs a) 
     const uint32_t qi = (sc != 0.f) ? (uint32_t)q : 0u;
     part |= qi << (((j0 + e) % CPD) * VB);
   }
-#pragma unroll
-  for (int m = 1; m < CPD / P; m <<= 1) part |= __shfl_xor(part, m, 64);
+  if constexpr (CPD / P > 1) part = group_reduce_xl<CPD / P>(part, [](uint32_t p, uint32_t q) { return p | q; });
   if (store) {
     const int g = j0 / 32;             // group
     const int i = (j0 % 32) / CPD;     // dword of the group
