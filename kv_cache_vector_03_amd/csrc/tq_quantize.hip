@@ -166,20 +166,40 @@ __global__ __launch_bounds__(kQWaves<D> * 64) void quantize_kernel(QArgs a) {
   const float inv_sqrt_d = 1.0f / __builtin_sqrtf((float)D);
   const float rscale = (float)(1 << kRScaleLog2);
 
-  for (int64_t tile = (int64_t)blockIdx.x * kQWaves<D> + wave; tile < a.num_tiles; tile += (int64_t)gridDim.x * kQWaves<D>) {
+  // bf16 inputs: the raw K and V dwords of the next tile are requested while
+  // the current one is processed (one tile of prefetch in registers)
+  const int64_t tstride = (int64_t)gridDim.x * kQWaves<D>;
+  constexpr int NR = BF16 ? E / 8 : 1;  // 16-byte pieces of a row part
+  auto fetch = [&](int64_t tl, u32x4 (&kd)[NR], u32x4 (&vd)[NR]) {
+    const int64_t thx = tl * 16 + row;
+    const bool ok = tl < a.num_tiles && thx < a.num_th;
+    const int64_t off = ok ? thx * D + part * E : 0;
+    const u32x4* pk = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.k) + off);
+    const u32x4* pv = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.v) + off);
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      kd[i] = ok ? __builtin_nontemporal_load(pk + i) : u32x4{0u, 0u, 0u, 0u};
+      vd[i] = ok ? __builtin_nontemporal_load(pv + i) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  int64_t tile = (int64_t)blockIdx.x * kQWaves<D> + wave;
+  u32x4 kr[NR], vr[NR];
+  if constexpr (BF16) fetch(tile, kr, vr);
+  for (; tile < a.num_tiles; tile += tstride) {
     const int64_t th = tile * 16 + row;
     const bool valid = th < a.num_th;
     const int64_t t = valid ? th / a.hkv : 0;
     const int h = valid ? (int)(th - t * a.hkv) : 0;
+    u32x4 kn[NR], vn[NR];
+    if constexpr (BF16) fetch(tile + tstride, kn, vn);
 
     // ---- key: norm, rotation, Lloyd-Max index, residual
     float x[E];
     if constexpr (BF16) {
       // D1 applied to the packed pairs as they are unpacked
-      const u32x4* p = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.k) + (valid ? th * D + part * E : 0));
 #pragma unroll
       for (int i = 0; i < E / 8; ++i) {
-        u32x4 w = valid ? __builtin_nontemporal_load(p + i) : u32x4{0u, 0u, 0u, 0u};
+        const u32x4 w = kr[i];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const uint32_t ws = w[j] ^ p1[4 * i + j];
@@ -254,8 +274,9 @@ __global__ __launch_bounds__(kQWaves<D> * 64) void quantize_kernel(QArgs a) {
         alo[kt] = *reinterpret_cast<const f16x8*>(a_lo + arow * RS + 32 * kt + 8 * kq);
       }
     }
-    // ---- z = S r on the matrix cores; sign bits by ballot
-#pragma unroll 1
+    // ---- z = S r on the matrix cores; sign bits by ballot (two column tiles
+    // in flight: independent accumulation chains)
+#pragma unroll 2
     for (int nt = 0; nt < NT; ++nt) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -322,7 +343,16 @@ __global__ __launch_bounds__(kQWaves<D> * 64) void quantize_kernel(QArgs a) {
     }
 
     // ---- value: min-max group quantisation of this lane's E channels
-    if (valid) {
+    if constexpr (BF16) {
+#pragma unroll
+      for (int i = 0; i < E / 8; ++i) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          x[8 * i + 2 * j] = __uint_as_float(vr[i][j] << 16);
+          x[8 * i + 2 * j + 1] = __uint_as_float(vr[i][j] & 0xFFFF0000u);
+        }
+      }
+    } else if (valid) {
       load_row_part<BF16>(a.v, th * D + part * E, x);
     } else {
 #pragma unroll
@@ -376,6 +406,13 @@ __global__ __launch_bounds__(kQWaves<D> * 64) void quantize_kernel(QArgs a) {
         for (int i = 0; i < VB; ++i)
           *reinterpret_cast<uint32_t*>(base + a.lay.vcodes + ((g * VB + i) * 16 + s) * 4) = vw[i];
         *reinterpret_cast<uint32_t*>(base + a.lay.vmeta + (g * 16 + s) * 4) = (uint32_t)s16 | ((uint32_t)z16 << 16);
+      }
+    }
+    if constexpr (BF16) {
+#pragma unroll
+      for (int i = 0; i < NR; ++i) {
+        kr[i] = kn[i];
+        vr[i] = vn[i];
       }
     }
   }
