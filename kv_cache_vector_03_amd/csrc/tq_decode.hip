@@ -818,13 +818,18 @@ __device__ __forceinline__ void rotate_project(const DArgs& a, const DevTables& 
   }
   __syncthreads();
   const int arow = lane & 15, kq = lane >> 4;
-  const float ascale = arow < G ? __builtin_ldexpf(1.0f, -s_exp[arow]) : 0.f;
+  // rows >= G read row 0 (unconditional vector reads) and are zeroed by the scale
+  const int arow_c = arow < G ? arow : 0;
+  const float ascale = arow < G ? __builtin_ldexpf(1.0f, -s_exp[arow_c]) : 0.f;
   f16x8 ahi[KT], alo[KT];
 #pragma unroll
   for (int kt = 0; kt < KT; ++kt) {
+    const f32x4 qa = *reinterpret_cast<const f32x4*>(s_q + arow_c * D + 32 * kt + 8 * kq);
+    const f32x4 qb = *reinterpret_cast<const f32x4*>(s_q + arow_c * D + 32 * kt + 8 * kq + 4);
+    const float qs[8] = {qa[0], qa[1], qa[2], qa[3], qb[0], qb[1], qb[2], qb[3]};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float v = arow < G ? s_q[arow * D + 32 * kt + 8 * kq + e] * ascale : 0.f;
+      const float v = qs[e] * ascale;
       const _Float16 hv = (_Float16)v;
       ahi[kt][e] = hv;
       alo[kt][e] = (_Float16)(v - (float)hv);
