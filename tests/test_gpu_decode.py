@@ -163,6 +163,41 @@ def test_split_count_invariance():
     assert spread <= 1e-4
 
 
+@pytest.mark.parametrize("chunk", [512, 4096])
+def test_rising_and_peaked_scores(chunk):
+    """Scores that keep rising along the sequence (the softmax reference has to
+    move many times) for the first KV head's query group and fall for the
+    second (the maximum comes first), with logits large enough that the
+    softmax is peaked; chunk 512 goes through the split partials and the
+    combine, 4096 is one split per sequence (direct output)."""
+    d, kb, vb, B, Hq, Hkv = 128, 3, 4, 2, 8, 2
+    G = Hq // Hkv
+    lens = [3000, 1999]
+    seed = 61
+    u = synth.queries(seed + 1, 1, 1, d)[0, 0].astype(np.float64)
+    u /= np.linalg.norm(u)
+
+    def kv(b, h, L):
+        K, V = synth.seq_kv(seed, b, h, L, d)
+        ramp = (8.0 * np.arange(L) / L)[:, None] * u[None, :]
+        return synth.bf16_round((K + ramp).astype(np.float32)), V
+
+    prm = oracle_params(seed, d, kb)
+    mb = int(np.ceil(max(lens) / 16))
+    nb = B * mb + 3
+    bt = synth.block_table(seed, B, mb, nb)
+    pool = paged.new_pool(nb, Hkv, paged.layout(d, kb, vb))
+    fields = oracle_cache(prm, d, kb, vb, lens, Hkv, bt, pool, seed, kv=kv)
+    q = 0.2 * synth.queries(seed, B, Hq, d).astype(np.float64)
+    q[:, :G] += 12.0 * u
+    q[:, G:] -= 12.0 * u
+    qb = synth.bf16_round(q.astype(np.float32))
+    ctx = _ctx(prm, d, kb, vb)
+    out, sc = _run_bf16(qb, [ctx], [pool], bt, lens, chunk=chunk)
+    ref_out, ref_sc = _oracle_decode(qb, fields, prm, lens)
+    _check(f"rising/peaked chunk={chunk}", out, sc, ref_out, ref_sc, lens)
+
+
 def test_head_dim_256_k4v4():
     d, kb, vb, B, Hq, Hkv = 256, 4, 4, 2, 16, 4
     lens = [777, 1500]
