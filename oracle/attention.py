@@ -42,7 +42,8 @@ def decode_one_sequence(q, fields_per_head, ctx, recent_k=None, recent_v=None, s
     ``q``: [Hq, d] query (fp32-exact values).
     ``fields_per_head``: list over KV heads of the dicts returned by
     ``oracle.paged.read_tokens`` (quantised tokens, all the same length L).
-    ``ctx``: dict with d1, d2, S, c32.
+    ``ctx``: dict with d1, d2, S, c32 and optionally ``qjl`` (False for
+    MSE-only keys; default True).
     ``recent_k``/``recent_v``: [Hkv, R, d] full-precision window or None.
 
     Returns (out [Hq, d], scores [Hq, L + R]) where scores are the unscaled
@@ -57,7 +58,7 @@ def decode_one_sequence(q, fields_per_head, ctx, recent_k=None, recent_v=None, s
     for h in range(Hq):
         f = fields_per_head[h // G]
         est = _keys.estimate_scores(q[h], f["idx"], f["sign"], f["n16"], f["g16"],
-                                    ctx["d1"], ctx["d2"], ctx["S"], ctx["c32"])
+                                    ctx["d1"], ctx["d2"], ctx["S"], ctx["c32"], qjl=ctx.get("qjl", True))
         vhat = _values.dequantize_values(f["q"], f["s16"], f["z16"])
         if recent_k is not None:
             rk = np.asarray(recent_k[h // G], dtype=np.float64)

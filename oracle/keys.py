@@ -14,6 +14,12 @@ Method (Roadmap §1; Hub "technical principle" steps 1-3; Yage, "step 2" and
    <q, k> (Hub, "unbiased estimator"; Roadmap §1: QJL keeps the inner-product
    estimate unbiased).
 
+MSE-only keys (iThome, "which path vLLM actually takes": vLLM's presets keep
+the Hadamard rotation and the MSE-quantised keys and leave QJL out; iThome,
+"the core idea": the MSE stage alone, then the 1-bit QJL residual for the
+inner product) stop after step 3: no sign bits and no residual norm are kept,
+and the score is n * <q~, c[idx]>, which shrinks towards zero on average.
+
 Readings where the pages are silent:
 
 * one (D1, D2, S) per context, shared by every head and token;
@@ -45,8 +51,10 @@ def QJL_SCALE(d: int) -> float:
     return math.sqrt(math.pi / 2.0) / d
 
 
-def encode_keys(k, d1, d2, S, c32, t32):
-    """Encode keys ``k`` of shape [N, d].
+def encode_keys(k, d1, d2, S, c32, t32, qjl=True):
+    """Encode keys ``k`` of shape [N, d].  With ``qjl=False`` (MSE-only keys)
+    steps 4-5 are skipped: ``sign``, ``g16``, ``gamma`` and ``z`` come back
+    as zeros (nothing of the residual is stored).
 
     Returns a dict with the stored fields
       ``idx``  int64 [N, d]   Lloyd-Max indices,
@@ -68,9 +76,14 @@ def encode_keys(k, d1, d2, S, c32, t32):
 
     idx = np.sum(u[:, :, None] > t[None, None, :], axis=2).astype(np.int64)
     r = u - c[idx]
-    gamma = np.sqrt(np.sum(r * r, axis=1))
-    z = r @ S.T
-    sign = (z >= 0.0).astype(np.uint8)
+    if qjl:
+        gamma = np.sqrt(np.sum(r * r, axis=1))
+        z = r @ S.T
+        sign = (z >= 0.0).astype(np.uint8)
+    else:
+        gamma = np.zeros(N)
+        z = np.zeros((N, d))
+        sign = np.zeros((N, d), dtype=np.uint8)
 
     idx[zero] = 0
     sign[zero] = 0
@@ -99,13 +112,14 @@ def query_tables(q, d1, d2, S):
     return qt, qt @ S.T
 
 
-def estimate_scores(q, idx, sign, n16, g16, d1, d2, S, c32):
+def estimate_scores(q, idx, sign, n16, g16, d1, d2, S, c32, qjl=True):
     """Estimated <q, k_t> for one query q [d] against stored keys:
 
       est_t = n_t * ( sum_j q~_j c[idx_tj]
                       + sqrt(pi/2)/d * gamma_t * sum_i p_i (2 sigma_ti - 1) ),
 
-    with q~ = Pi q, p = S q~ and the stored binary16 n_t, gamma_t."""
+    with q~ = Pi q, p = S q~ and the stored binary16 n_t, gamma_t.  MSE-only
+    keys (``qjl=False``) drop the second term: est_t = n_t <q~, c[idx_t]>."""
     q = np.asarray(q, dtype=np.float64)
     d = q.shape[-1]
     qt, p = query_tables(q, d1, d2, S)
@@ -113,5 +127,7 @@ def estimate_scores(q, idx, sign, n16, g16, d1, d2, S, c32):
     n = _bits.from_fp16_bits(n16)
     g = _bits.from_fp16_bits(g16)
     mse = (c[np.asarray(idx)] * qt[None, :]).sum(axis=1)
+    if not qjl:
+        return n * mse
     pm = (2.0 * np.asarray(sign, dtype=np.float64) - 1.0) @ p
     return n * (mse + QJL_SCALE(d) * g * pm)

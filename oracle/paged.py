@@ -18,6 +18,9 @@ a multiple of 16 bytes:
                           byte f of slot s at ((f // 4) * 16 + s) * 4 + f % 4
   Vmeta   [d/32][16][2]   fp16 (scale, zero) per (group, slot)
 
+MSE-only presets (keys without the QJL sketch) have no Kqjl region and a
+Kmeta region of [16] fp16 n (32 bytes); the other regions are unchanged.
+
 Token t of sequence s lives in block ``block_table[s][t // 16]``, slot
 ``t % 16``; the writer addresses slot ``slot_mapping[i]`` of token i as block
 ``slot_mapping[i] // 16``, slot ``slot_mapping[i] % 16``.
@@ -34,10 +37,10 @@ __all__ = ["BLOCK", "layout", "write_tokens", "read_tokens", "new_pool"]
 BLOCK = 16
 
 
-def layout(d: int, b_k: int, b_v: int) -> dict:
+def layout(d: int, b_k: int, b_v: int, qjl: bool = True) -> dict:
     kc = BLOCK * (b_k * d // 8)
-    kq = BLOCK * (d // 8)
-    km = BLOCK * 4
+    kq = BLOCK * (d // 8) if qjl else 0
+    km = BLOCK * (4 if qjl else 2)
     vc = (b_v * d // 8) * BLOCK
     vm = (d // 32) * BLOCK * 4
     off = {}
@@ -46,7 +49,7 @@ def layout(d: int, b_k: int, b_v: int) -> dict:
         off[name] = (o, size)
         o += size
     off["bytes"] = o
-    off["d"], off["b_k"], off["b_v"] = d, b_k, b_v
+    off["d"], off["b_k"], off["b_v"], off["qjl"] = d, b_k, b_v, qjl
     return off
 
 
@@ -73,13 +76,17 @@ def write_tokens(pool, slot_mapping, head: int, kenc: dict, venc: dict, lay: dic
     sm = np.asarray(slot_mapping, dtype=np.int64)
     blk = (sm // BLOCK)[:, None]
     slot = sm % BLOCK
+    qjl = lay["qjl"]
     kcodes = _bits.pack(kenc["idx"], b_k)
-    kqjl = _bits.pack(kenc["sign"], 1)
-    kmeta = np.stack([kenc["n16"], kenc["g16"]], axis=1).astype(np.uint16).view(np.uint8)
+    if qjl:
+        kmeta = np.stack([kenc["n16"], kenc["g16"]], axis=1).astype(np.uint16).view(np.uint8)
+    else:
+        kmeta = np.asarray(kenc["n16"], dtype=np.uint16)[:, None].view(np.uint8)
     vcodes = _bits.pack(venc["q"], b_v)
     pool[blk, head, _region_index(lay, "kcodes", slot, b_k * d // 8, True)] = kcodes
-    pool[blk, head, _region_index(lay, "kqjl", slot, d // 8, True)] = kqjl
-    pool[blk, head, _region_index(lay, "kmeta", slot, 4, True)] = kmeta
+    if qjl:
+        pool[blk, head, _region_index(lay, "kqjl", slot, d // 8, True)] = _bits.pack(kenc["sign"], 1)
+    pool[blk, head, _region_index(lay, "kmeta", slot, kmeta.shape[1], True)] = kmeta
     pool[blk, head, _region_index(lay, "vcodes", slot, b_v * d // 8, False)] = vcodes
     o, _ = lay["vmeta"]
     for g in range(ng):
@@ -90,15 +97,20 @@ def write_tokens(pool, slot_mapping, head: int, kenc: dict, venc: dict, lay: dic
 
 def read_tokens(pool, block_table_row, length: int, head: int, lay: dict) -> dict:
     """Read the first ``length`` tokens of one sequence and KV head back into
-    fields: idx [L, d], sign [L, d], n16, g16 [L], q [L, d], s16, z16 [L, d/32]."""
+    fields: idx [L, d], sign [L, d], n16, g16 [L], q [L, d], s16, z16 [L, d/32]
+    (sign and g16 are zeros for MSE-only keys)."""
     d, b_k, b_v = lay["d"], lay["b_k"], lay["b_v"]
     ng = d // 32
     t = np.arange(length, dtype=np.int64)
     blk = np.asarray(block_table_row, dtype=np.int64)[t // BLOCK][:, None]
     slot = t % BLOCK
+    qjl = lay["qjl"]
     kcodes = pool[blk, head, _region_index(lay, "kcodes", slot, b_k * d // 8, True)]
-    kqjl = pool[blk, head, _region_index(lay, "kqjl", slot, d // 8, True)]
-    kmeta = np.ascontiguousarray(pool[blk, head, _region_index(lay, "kmeta", slot, 4, True)]).view(np.uint16)
+    if qjl:
+        sign = _bits.unpack(pool[blk, head, _region_index(lay, "kqjl", slot, d // 8, True)], 1, d).astype(np.uint8)
+    else:
+        sign = np.zeros((length, d), dtype=np.uint8)
+    kmeta = np.ascontiguousarray(pool[blk, head, _region_index(lay, "kmeta", slot, 4 if qjl else 2, True)]).view(np.uint16)
     vcodes = pool[blk, head, _region_index(lay, "vcodes", slot, b_v * d // 8, False)]
     o, _ = lay["vmeta"]
     s16 = np.zeros((length, ng), np.uint16)
@@ -109,9 +121,9 @@ def read_tokens(pool, block_table_row, length: int, head: int, lay: dict) -> dic
         s16[:, g], z16[:, g] = pair[:, 0], pair[:, 1]
     return {
         "idx": _bits.unpack(kcodes, b_k, d),
-        "sign": _bits.unpack(kqjl, 1, d).astype(np.uint8),
+        "sign": sign,
         "n16": kmeta[:, 0].copy(),
-        "g16": kmeta[:, 1].copy(),
+        "g16": kmeta[:, 1].copy() if qjl else np.zeros(length, dtype=np.uint16),
         "q": _bits.unpack(vcodes, b_v, d),
         "s16": s16,
         "z16": z16,
