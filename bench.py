@@ -14,6 +14,8 @@ Printed as ONE JSON line:
               events around its launch, against the 8 TB/s HBM peak;
   quantize  = tq_quantize_store throughput on the quantise workload (65536
               new bf16 tokens x 8 KV heads, 0.5% x20 outliers, K3V4 and K3V2);
+  mse_only  = the same decode step with MSE-only keys (no QJL sketch, 130 B
+              per token-head): step and split-kernel times, TB/s of its KV bytes;
   cpu_baseline = the fp64 CPU oracle on a bounded sample of the decode
               workload, on this host's cores.
 The cache pool is rotated over several copies so that the 256 MB last-level
@@ -58,11 +60,11 @@ def _traffic_record(per_launch_units):
     return rec.get("hbm_bytes_per_launch")
 
 
-def setup_decode(torch, tq, synth, chunk, copies):
+def setup_decode(torch, tq, synth, chunk, copies, mse_only=False):
     d, B, Hq, Hkv, L, kb, vb, nb, seed = 128, 32, 32, 8, 8192, 3, 4, 16384, 3
     signs1, signs2, S = synth.method_params(seed, d)
     import numpy as np
-    ctx = tq.tq_codebook_init(d, kb, vb, signs=np.stack([signs1, signs2]), S=S)
+    ctx = tq.tq_codebook_init(d, kb, vb, signs=np.stack([signs1, signs2]), S=S, mse_only=mse_only)
     bt_np = synth.block_table(seed, B, L // 16, nb)
     bt = torch.from_numpy(bt_np).cuda()
     pools = [torch.zeros((nb, Hkv, ctx.block_bytes), dtype=torch.uint8, device="cuda") for _ in range(copies)]
@@ -84,7 +86,7 @@ def setup_decode(torch, tq, synth, chunk, copies):
     nbytes = tq.tq_decode_workspace_bytes(q, [ctx], [pools[0]], bt, lens, out, chunk_tokens=chunk, max_seq_len=L)
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     return dict(ctx=ctx, bt=bt, pools=pools, knew=knew, vnew=vnew, slot_new=slot_new, q=q, lens=lens, out=out, ws=ws,
-                B=B, Hq=Hq, Hkv=Hkv, d=d, L=L, chunk=chunk, kv_bytes=B * Hkv * L * REC_BYTES_K3V4,
+                B=B, Hq=Hq, Hkv=Hkv, d=d, L=L, chunk=chunk, kv_bytes=B * Hkv * L * (ctx.block_bytes // 16),
                 units=B * Hkv * L)
 
 
@@ -93,6 +95,39 @@ def decode_step(tq, s, i, events=None):
     tq.tq_quantize_store(s["ctx"], s["knew"], s["vnew"], s["slot_new"], pool)
     tq.tq_decode_attention(s["q"], [s["ctx"]], [pool], s["bt"], s["lens"], s["out"], s["ws"],
                            chunk_tokens=s["chunk"], max_seq_len=s["L"], split_events=events)
+
+
+def time_decode(torch, tq, s, steps, warmup):
+    """Average step time (store + decode) over `steps` steps, then the split
+    kernel's average launch duration from HIP events on its stream."""
+    for i in range(warmup):
+        decode_step(tq, s, i)
+    torch.cuda.synchronize()
+    # timed region: K steps of the whole path (store + decode), nothing else
+    # on the stream.
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        decode_step(tq, s, i)
+    stop.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(stop) / steps
+    # the same K steps again with the split (streaming) kernel bracketed by
+    # HIP events on its own stream each step, for its average launch duration
+    # (kept out of the step timing: an event record between launches adds a
+    # few microseconds of idle time to the step).
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in evs:  # create the underlying HIP events
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    for i in range(steps):
+        decode_step(tq, s, i, events=(evs[i][0].cuda_event, evs[i][1].cuda_event))
+    torch.cuda.synchronize()
+    split_ms = sorted(a.elapsed_time(b) for a, b in evs)
+    return ms_step, sum(split_ms) / len(split_ms), split_ms
 
 
 def bench_quantize(torch, tq, synth, steps, warmup):
@@ -189,40 +224,28 @@ def main():
     torch.cuda.init()
     print(f"[bench] device {torch.cuda.get_device_name(0)}; building the decode cache", file=sys.stderr, flush=True)
     s = setup_decode(torch, tq, synth, args.chunk, copies=3)
-    for i in range(args.warmup):
-        decode_step(tq, s, i)
-    torch.cuda.synchronize()
-
-    # timed region: K steps of the whole path (store + decode), nothing else
-    # on the stream.
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
-    for i in range(args.steps):
-        decode_step(tq, s, i)
-    stop.record()
-    torch.cuda.synchronize()
-    ms_step = start.elapsed_time(stop) / args.steps
-
-    # the same K steps again with the split (streaming) kernel bracketed by
-    # HIP events on its own stream each step, for its average launch duration
-    # (kept out of the step timing: an event record between launches adds a
-    # few microseconds of idle time to the step).
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    for a, b in evs:  # create the underlying HIP events
-        a.record()
-        b.record()
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        decode_step(tq, s, i, events=(evs[i][0].cuda_event, evs[i][1].cuda_event))
-    torch.cuda.synchronize()
-    split_ms = sorted(a.elapsed_time(b) for a, b in evs)
-    split_avg = sum(split_ms) / len(split_ms)
+    ms_step, split_avg, split_ms = time_decode(torch, tq, s, args.steps, args.warmup)
     value = s["kv_bytes"] / (ms_step * 1e-3) / 1e12
     achieved = s["kv_bytes"] / (split_avg * 1e-3) / 1e9
     print(f"[bench] decode step {ms_step * 1e3:.1f} us, split kernel avg {split_avg * 1e3:.1f} us "
           f"(median {split_ms[len(split_ms) // 2] * 1e3:.1f})", file=sys.stderr, flush=True)
+    for p in s["pools"]:
+        del p
+    s.clear()
+    torch.cuda.empty_cache()
+
+    # the same workload with MSE-only keys (no QJL sketch: 130 B per token-head)
+    print("[bench] decode workload, MSE-only keys", file=sys.stderr, flush=True)
+    s = setup_decode(torch, tq, synth, args.chunk, copies=3, mse_only=True)
+    m_step, m_split, _ = time_decode(torch, tq, s, args.steps, args.warmup)
+    mse = {"workload": "decode-b32-hq32-hkv8-d128-ctx8192-k3v4-mse-only: store 1 new token + attend 8192",
+           "kv_bytes_per_step": s["kv_bytes"], "ms_per_step": round(m_step, 5),
+           "tbs": round(s["kv_bytes"] / (m_step * 1e-3) / 1e12, 4),
+           "split_avg_ms": round(m_split, 5),
+           "split_hbm_frac": round(s["kv_bytes"] / (m_split * 1e-3) / 1e12 / HBM_PEAK_TBS, 4),
+           "decode_tokens_per_s": round(32 / (m_step * 1e-3), 1)}
+    print(f"[bench] MSE-only decode step {m_step * 1e3:.1f} us, split kernel avg {m_split * 1e3:.1f} us",
+          file=sys.stderr, flush=True)
     for p in s["pools"]:
         del p
     s.clear()
@@ -258,6 +281,7 @@ def main():
                      "frac": round(achieved / (HBM_PEAK_TBS * 1000), 4), "traffic": traffic,
                      "kernel": "decode_split_kernel<128,4,3,4>", "bytes_per_launch": 32 * 8 * 8192 * REC_BYTES_K3V4,
                      "avg_launch_ms": round(split_avg, 5)},
+        "mse_only": mse,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

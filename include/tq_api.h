@@ -52,6 +52,12 @@ enum { TQ_DTYPE_F32 = 0, TQ_DTYPE_BF16 = 1 };
  *   v_bits     : value bits, 2 or 4 (Hub, step 4).
  *   v_group    : value group size, must be 32 (Hub, step 4).
  *   block_size : tokens per paged block, must be 16.
+ *   flags      : 0, or TQ_PRESET_MSE_ONLY for keys without the QJL sketch
+ *                (iThome, "which path vLLM actually takes": presets with the
+ *                Hadamard rotation and MSE-quantised keys but no QJL): the
+ *                record then holds no sign bits and no residual norm, and
+ *                the score is n <q~, c[idx]> alone.  Other bits are
+ *                rejected with TQ_EUNSUPPORTED.
  *   seed       : seed of the library's own draw of D1, D2 and S when the
  *                caller does not pass them (splitmix64 counter stream; the
  *                signs are the top bit of consecutive outputs, the Gaussians
@@ -62,9 +68,11 @@ typedef struct {
   int32_t v_bits;
   int32_t v_group;
   int32_t block_size;
-  int32_t reserved;
+  int32_t flags;
   uint64_t seed;
 } tq_preset;
+
+enum { TQ_PRESET_MSE_ONLY = 1 };
 
 typedef struct tq_ctx tq_ctx; /* opaque; created by tq_codebook_init */
 
@@ -75,7 +83,8 @@ typedef struct tq_ctx tq_ctx; /* opaque; created by tq_codebook_init */
  *   kmeta  [16][2] fp16      (norm n, residual norm gamma) per slot
  *   vcodes [v_bits*d/32][16][4] dword w of every slot's value-code stream
  *                            together (byte f of slot s at ((f/4)*16+s)*4+f%4)
- *   vmeta  [d/32][16][2]     fp16 (scale, zero) per (group, slot)            */
+ *   vmeta  [d/32][16][2]     fp16 (scale, zero) per (group, slot)
+ * MSE-only presets: kqjl is empty (kqjl == kmeta) and kmeta is [16] fp16 n. */
 typedef struct {
   int64_t kcodes, kqjl, kmeta, vcodes, vmeta;
   int64_t record_bytes;
@@ -128,7 +137,8 @@ size_t tq_block_bytes(const tq_ctx* ctx);
  * quantiser in one launch; iThome "which path vLLM actually takes": quantise,
  * pack and write into the paged KV cache).  Per (token, head):
  *   n = ||k||; u = D2 (H/sqrt d) D1 k / n; idx_j = #{t : thr_t < u_j};
- *   r = u - c[idx]; gamma = ||r||; sign_i = [(S r)_i >= 0];
+ *   r = u - c[idx]; gamma = ||r||; sign_i = [(S r)_i >= 0] (MSE-only presets
+ *   stop at idx and store n alone);
  *   values per group of 32: s = fp16((max-min)/(2^v_bits-1)), z = fp16(min),
  *   q = clamp(rint((v - z)/s), 0, 2^v_bits - 1) (q = 0 when s = 0).
  *   k, v         : device [num_tokens][num_kv_heads][head_dim], in_dtype
@@ -153,7 +163,8 @@ int tq_quantize_store(const tq_ctx* ctx, const void* k, const void* v, int32_t i
  * graph capture).  Score of query head h (KV head h / G) against cached
  * token t:
  *   est_t = n_t ( sum_j q~_j c[idx_tj] + sqrt(pi/2)/d gamma_t sum_i p_i (2 sign_ti - 1) ),
- *   q~ = D2 (H/sqrt d) D1 q, p = S q~, n_t and gamma_t the stored fp16 values;
+ *   q~ = D2 (H/sqrt d) D1 q, p = S q~, n_t and gamma_t the stored fp16 values
+ *   (MSE-only presets: est_t = n_t sum_j q~_j c[idx_tj]);
  * recent full-precision tokens (Hub, vLLM integration: hybrid mode) score
  * <q, k> exactly.  out = softmax(sm_scale * scores) . values, values being
  * q s + z for cached tokens and the bf16 values for recent ones.  A sequence

@@ -13,7 +13,7 @@ import ctypes
 import os
 
 __all__ = [
-    "TQ_OK", "TQ_EINVAL", "TQ_EUNSUPPORTED", "TQ_EHIP", "TQ_ENOMEM", "TQ_DTYPE_F32", "TQ_DTYPE_BF16",
+    "TQ_OK", "TQ_EINVAL", "TQ_EUNSUPPORTED", "TQ_EHIP", "TQ_ENOMEM", "TQ_DTYPE_F32", "TQ_DTYPE_BF16", "TQ_PRESET_MSE_ONLY",
     "TqError", "Context", "library_path", "load", "tq_codebook_init", "tq_ctx_destroy", "tq_ctx_tables",
     "tq_lloyd_max", "tq_record_layout", "tq_draw_params", "tq_block_bytes", "tq_quantize_store",
     "tq_decode_workspace_bytes", "tq_decode_attention", "tq_last_error", "EXPORTED_SYMBOLS",
@@ -21,6 +21,7 @@ __all__ = [
 
 TQ_OK, TQ_EINVAL, TQ_EUNSUPPORTED, TQ_EHIP, TQ_ENOMEM = 0, -1, -2, -3, -4
 TQ_DTYPE_F32, TQ_DTYPE_BF16 = 0, 1
+TQ_PRESET_MSE_ONLY = 1
 
 EXPORTED_SYMBOLS = [
     "tq_codebook_init", "tq_ctx_destroy", "tq_ctx_tables", "tq_ctx_preset", "tq_lloyd_max", "tq_record_layout",
@@ -44,7 +45,7 @@ class TqError(RuntimeError):
 
 class tq_preset(ctypes.Structure):
     _fields_ = [("head_dim", ctypes.c_int32), ("k_bits", ctypes.c_int32), ("v_bits", ctypes.c_int32),
-                ("v_group", ctypes.c_int32), ("block_size", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("v_group", ctypes.c_int32), ("block_size", ctypes.c_int32), ("flags", ctypes.c_int32),
                 ("seed", ctypes.c_uint64)]
 
 
@@ -139,9 +140,10 @@ def _dtype_code(t):
 class Context:
     """Owner of a ``tq_ctx*`` (freed on ``close()`` or garbage collection)."""
 
-    def __init__(self, handle: int, head_dim: int, k_bits: int, v_bits: int):
+    def __init__(self, handle: int, head_dim: int, k_bits: int, v_bits: int, mse_only: bool = False):
         self.handle = handle
         self.head_dim, self.k_bits, self.v_bits = head_dim, k_bits, v_bits
+        self.mse_only = mse_only
 
     @property
     def block_bytes(self) -> int:
@@ -159,11 +161,13 @@ class Context:
             pass
 
 
-def tq_codebook_init(head_dim: int, k_bits: int, v_bits: int, seed: int = 0, signs=None, S=None) -> Context:
+def tq_codebook_init(head_dim: int, k_bits: int, v_bits: int, seed: int = 0, signs=None, S=None,
+                     mse_only: bool = False) -> Context:
     """Create a context.  ``signs`` (int8 [2, d]) and ``S`` (float32 [d, d])
-    are host numpy arrays or None (then drawn from ``seed``)."""
+    are host numpy arrays or None (then drawn from ``seed``); ``mse_only``
+    selects keys without the QJL sketch (TQ_PRESET_MSE_ONLY)."""
     lib = load()
-    p = tq_preset(head_dim, k_bits, v_bits, 32, 16, 0, seed)
+    p = tq_preset(head_dim, k_bits, v_bits, 32, 16, TQ_PRESET_MSE_ONLY if mse_only else 0, seed)
     h = ctypes.c_void_p()
     if signs is not None:
         import numpy as np
@@ -172,7 +176,7 @@ def tq_codebook_init(head_dim: int, k_bits: int, v_bits: int, seed: int = 0, sig
         import numpy as np
         S = np.ascontiguousarray(S, dtype=np.float32)
     _check(lib.tq_codebook_init(ctypes.byref(p), _ptr(signs), _ptr(S), ctypes.byref(h)), "tq_codebook_init")
-    return Context(h.value, head_dim, k_bits, v_bits)
+    return Context(h.value, head_dim, k_bits, v_bits, mse_only)
 
 
 def tq_ctx_destroy(ctx: Context) -> None:
@@ -200,8 +204,8 @@ def tq_lloyd_max(head_dim: int, bits: int):
     return c, t
 
 
-def tq_record_layout(head_dim: int, k_bits: int, v_bits: int) -> dict:
-    p = tq_preset(head_dim, k_bits, v_bits, 32, 16, 0, 0)
+def tq_record_layout(head_dim: int, k_bits: int, v_bits: int, mse_only: bool = False, flags=None) -> dict:
+    p = tq_preset(head_dim, k_bits, v_bits, 32, 16, (TQ_PRESET_MSE_ONLY if mse_only else 0) if flags is None else flags, 0)
     out = tq_layout()
     _check(load().tq_record_layout(ctypes.byref(p), ctypes.byref(out)), "tq_record_layout")
     return {f: getattr(out, f) for f, _ in tq_layout._fields_}

@@ -36,6 +36,10 @@
 #include "tq_common.hip.h"
 #include "tq_internal.h"
 
+#ifndef TQ_DECODE_QJL
+#error "compile with -DTQ_DECODE_QJL=1 (keys with the QJL sketch) or 0 (MSE-only keys)"
+#endif
+
 namespace tq {
 
 constexpr int kMaxG = 8;
@@ -109,22 +113,24 @@ constexpr int kMaxChunk = 8192;  // largest chunk_tokens (block ids of a chunk a
 constexpr float kLazyMax = 2.0f;
 
 // Compile-time geometry of one (block, KV head) record (the same byte layout
-// the host computes) and of one 32-token step = two records.
-template <int D, int KB, int VB>
+// the host computes) and of one 32-token step = two records.  QJ = false:
+// MSE-only keys (no sign bits, key metadata = fp16 n per slot).
+template <int D, int KB, int VB, bool QJ>
 struct Rec {
   static constexpr int kcodes = 0;
   static constexpr int kqjl = kcodes + 16 * (KB * D / 8);
-  static constexpr int kmeta = kqjl + 16 * (D / 8);
-  static constexpr int vcodes = kmeta + 64;
+  static constexpr int kmeta = kqjl + (QJ ? 16 * (D / 8) : 0);
+  static constexpr int kmeta_slot = QJ ? 4 : 2;  // bytes of one slot's key metadata
+  static constexpr int vcodes = kmeta + 16 * kmeta_slot;
   static constexpr int vmeta = vcodes + (VB * D / 8) * 16;
   static constexpr int bytes = vmeta + (D / 32) * 64;
   static constexpr int slot = 2 * bytes;              // LDS bytes of one ring slot (one step)
   static constexpr int nslot = D == 128 ? 3 : 2;      // ring depth (steps in flight + 1)
 };
 
-template <int D, int GP, int KB, int VB>
+template <int D, int GP, int KB, int VB, bool QJ>
 struct SplitLds {
-  static_assert(Rec<D, KB, VB>::bytes % 16 == 0, "record size");
+  static_assert(Rec<D, KB, VB, QJ>::bytes % 16 == 0, "record size");
   // per-wave softmax weights [GP][32]; with GP = 4 the idle lanes 32-63 store
   // theirs to a second, never-read copy so that the store needs no lane mask
   static constexpr int kPWave = GP * 32 * (GP == 4 ? 2 : 1);
@@ -132,7 +138,7 @@ struct SplitLds {
   static constexpr int kPBytes = NW * kPWave * 4;
   static constexpr int kStatBytes = NW * GP * 2 * 4;
   static constexpr int kBlkBytes = (kMaxChunk / 16 + 16) * 4;
-  static constexpr int kRingBytes = NW * Rec<D, KB, VB>::nslot * Rec<D, KB, VB>::slot;
+  static constexpr int kRingBytes = NW * Rec<D, KB, VB, QJ>::nslot * Rec<D, KB, VB, QJ>::slot;
   static constexpr int kMergeBytes = NW * GP * D * 4;  // overlays the ring after the stream
   static constexpr int kMainBytes = kRingBytes > kMergeBytes ? kRingBytes : kMergeBytes;
   static constexpr int kMainOffset = kPBytes + kStatBytes + kBlkBytes;
@@ -227,12 +233,12 @@ __device__ __forceinline__ uint32_t opaque_u32(uint32_t x) {
 constexpr int kWaitVm0 = 0x0F70;
 __device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory"); }
 
-template <int D, int GP, int KB, int VB, class Setup>
+template <int D, int GP, int KB, int VB, bool QJ, class Setup>
 __device__ void split_cached_chunk(const DArgs& a, int pr, int h, int t0, int t1, const int32_t* s_blk,
                                    const uint2* s_pair, const u32x4* s_sgn, float* s_p, unsigned char* s_main,
                                    float* s_stat, bf16x8 (&A1)[D / 32][2], bf16x8 (&A3)[D / 32],
                                    float* m_out, float* l_out, int b, int* s_claim, Setup&& setup) {
-  using R = Rec<D, KB, VB>;
+  using R = Rec<D, KB, VB, QJ>;
   constexpr int NW = split_waves<D, GP>();
   constexpr int KT = D / 32;
   constexpr int CS = D / 128;      // value column sets
@@ -250,14 +256,14 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h, int t0, int t1
   const uint8_t* pool = a.pool[pr];
   const int64_t rec = a.rec[pr];
   const int64_t pblocks = a.pool_blocks[pr];
-  float* sp = s_p + wave * SplitLds<D, GP, KB, VB>::kPWave;
+  float* sp = s_p + wave * SplitLds<D, GP, KB, VB, QJ>::kPWave;
   unsigned char* ring = s_main + wave * R::nslot * R::slot;
   const uint32_t ring_lds = lds_offset(ring);
 
   // per-lane byte offsets inside a record
   const int off_kc = R::kcodes + tok * (KB * D / 8) + kq * QB;
   const int off_kj = R::kqjl + tok * (D / 8) + kq * (D / 32);
-  const int off_km = R::kmeta + tok * 4;
+  const int off_km = R::kmeta + tok * R::kmeta_slot;
   const int slot0 = (kq & 1) * 8;
   const int vhalf = kq >> 1;
   int off_vx[CS], off_vm[CS];
@@ -349,9 +355,12 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h, int t0, int t1
       for (int i = 0; i < QW; ++i) cw[i] = *reinterpret_cast<const uint32_t*>(hb + off_kc + 4 * i);
       cw[QW] = 0;
       uint32_t kj[D / 128];
+      if constexpr (QJ) {
 #pragma unroll
-      for (int i = 0; i < D / 128; ++i) kj[i] = *reinterpret_cast<const uint32_t*>(hb + off_kj + 4 * i);
-      const uint32_t km = *reinterpret_cast<const uint32_t*>(hb + off_km);
+        for (int i = 0; i < D / 128; ++i) kj[i] = *reinterpret_cast<const uint32_t*>(hb + off_kj + 4 * i);
+      }
+      const uint32_t km = QJ ? *reinterpret_cast<const uint32_t*>(hb + off_km)
+                             : (uint32_t)*reinterpret_cast<const uint16_t*>(hb + off_km);
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) {
         constexpr int TB = 8 * KB;
@@ -366,16 +375,23 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h, int t0, int t1
         const u32x4 b1 = {pe[2].x, pe[2].y, pe[3].x, pe[3].y};
         am = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1[kt][0], __builtin_bit_cast(bf16x8, b0), am, 0, 0, 0);
         am = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1[kt][1], __builtin_bit_cast(bf16x8, b1), am, 0, 0, 0);
-        const u32x4 bq = s_sgn[(kj[kt / 4] >> (8 * (kt % 4))) & 0xFFu];
-        aq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A3[kt], __builtin_bit_cast(bf16x8, bq), aq, 0, 0, 0);
+        if constexpr (QJ) {
+          const u32x4 bq = s_sgn[(kj[kt / 4] >> (8 * (kt % 4))) & 0xFFu];
+          aq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A3[kt], __builtin_bit_cast(bf16x8, bq), aq, 0, 0, 0);
+        }
       }
       // logit = log2(e) sm_scale n (q~.c + kappa gamma p.sign), with
       // log2(e) sm_scale folded into q~ and kappa log2(e) sm_scale into p (the
       // A operands)
       const float n = f16_bits_to_f32((uint16_t)(km & 0xFFFFu));
-      const float nk = n * f16_bits_to_f32((uint16_t)(km >> 16));
+      if constexpr (QJ) {
+        const float nk = n * f16_bits_to_f32((uint16_t)(km >> 16));
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[half][r] = __builtin_fmaf(nk, aq[r], n * am[r]);
+        for (int r = 0; r < 4; ++r) v[half][r] = __builtin_fmaf(nk, aq[r], n * am[r]);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[half][r] = n * am[r];
+      }
     }
     // x[r]: hi + lo of head row r, one swap per row.  GP = 4: the hi and lo
     // rows sit 16 lanes apart; after the swap lanes 0-15 hold the first 16
@@ -751,7 +767,7 @@ __device__ void split_recent(const DArgs& a, int b, int h, int R, float* s_p, fl
 // s_pq: A rows = heads (fp16 hi/lo of q~ 2^-e_g, with 2^e_g above the head's
 // largest |q~_j| so fp16 cannot overflow), B = the 16 S tiles of the context,
 // three products per tile; wave w takes column tiles w, w + 4, ...
-template <int D, int NW>
+template <int D, int NW, bool QJ>
 __device__ __forceinline__ void rotate_project(const DArgs& a, const DevTables& dv, int b, int h, float* s_q, float* s_pq,
                                int* s_exp) {
   constexpr int P = D / 64;
@@ -759,10 +775,10 @@ __device__ __forceinline__ void rotate_project(const DArgs& a, const DevTables& 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int G = a.G;
   const int64_t q0 = ((int64_t)b * a.Hq + (int64_t)h * G) * D;
-  // the S tiles do not depend on q: load them first
+  // the S tiles do not depend on q: load them first (MSE-only keys need no p)
   f16x8 bhi[NTW][KT], blo[NTW][KT];
 #pragma unroll
-  for (int i = 0; i < NTW; ++i) {
+  for (int i = 0; i < (QJ ? NTW : 0); ++i) {
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
       const size_t tb = ((((size_t)(wave + NW * i)) * KT + kt) * 2) * 64 * 8;
@@ -817,6 +833,7 @@ __device__ __forceinline__ void rotate_project(const DArgs& a, const DevTables& 
     if (lane == 0) s_exp[g] = amax > 0.f ? (int)((__float_as_uint(amax) >> 23) & 0xFFu) - 126 : 0;
   }
   __syncthreads();
+  if constexpr (!QJ) return;
   const int arow = lane & 15, kq = lane >> 4;
   // rows >= G read row 0 (unconditional vector reads) and are zeroed by the scale
   const int arow_c = arow < G ? arow : 0;
@@ -862,19 +879,19 @@ __device__ __forceinline__ void rotate_project(const DArgs& a, const DevTables& 
 // every workgroup runs at start-up; workgroup w takes the contiguous range
 // [w total / grid, (w + 1) total / grid), so consecutive items mostly share
 // (b, h) and reuse its rotated query operands.
-template <int D, int GP, int KB, int VB>
+template <int D, int GP, int KB, int VB, bool QJ>
 __global__ __launch_bounds__((split_waves<D, GP>() * 64)) void decode_split_kernel(DArgs a, int pr) {
   constexpr int NW = split_waves<D, GP>();
   constexpr int KT = D / 32;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-  using SL = SplitLds<D, GP, KB, VB>;
+  using SL = SplitLds<D, GP, KB, VB, QJ>;
   float* s_p = reinterpret_cast<float*>(lds);
   float* s_stat = s_p + NW * SL::kPWave;
   int32_t* s_blk = reinterpret_cast<int32_t*>(s_stat + NW * GP * 2);
   unsigned char* s_main = lds + SL::kMainOffset;
   float* s_merge = reinterpret_cast<float*>(s_main);
   __shared__ uint2 s_pair[256];  // centroid pair -> {bf16 hi parts, bf16 lo parts}
-  __shared__ u32x4 s_sgn[256];   // sign byte -> 8 bf16 of +-1 (bit i -> element i)
+  __shared__ u32x4 s_sgn[QJ ? 256 : 1];  // sign byte -> 8 bf16 of +-1 (bit i -> element i)
   __shared__ float s_m[kMaxG], s_l[kMaxG];
   __shared__ __attribute__((aligned(16))) float s_q[GP * D];
   __shared__ __attribute__((aligned(16))) float s_pq[GP * D];
@@ -893,7 +910,7 @@ __global__ __launch_bounds__((split_waves<D, GP>() * 64)) void decode_split_kern
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       w[e] = (((tid >> (2 * e)) & 1) ? 0x3F80u : 0xBF80u) | ((((tid >> (2 * e + 1)) & 1) ? 0x3F80u : 0xBF80u) << 16);
-    if (tid < 256) s_sgn[tid] = w;  // one entry per thread
+    if (QJ && tid < 256) s_sgn[tid] = w;  // one entry per thread
   }
 
   bf16x8 A1[KT][2], A3[KT];
@@ -903,7 +920,7 @@ __global__ __launch_bounds__((split_waves<D, GP>() * 64)) void decode_split_kern
   // kDirect: at most one split per sequence (the output is written here).
   auto run_item = [&](int b, int h, int c, int Lc, auto direct_c) {
     constexpr bool kDirect = decltype(direct_c)::value;
-    using R = Rec<D, KB, VB>;
+    using R = Rec<D, KB, VB, QJ>;
     constexpr bool kEarlyRotate = D == 128;
     constexpr int kStageRounds = (kMaxChunk / 16 + 2 + NW * 64 - 1) / (NW * 64);
     const int nq_chunks = (Lc + a.chunk - 1) / a.chunk;
@@ -930,7 +947,7 @@ __global__ __launch_bounds__((split_waves<D, GP>() * 64)) void decode_split_kern
         const int i = tid + r * NW * 64;
         blk[r] = (i < nstage && i < row_left) ? btrow[i] : -1;
       }
-      if (kEarlyRotate && bh != ready_bh) rotate_project<D, NW>(a, dv, b, h, s_q, s_pq, s_exp);
+      if (kEarlyRotate && bh != ready_bh) rotate_project<D, NW, QJ>(a, dv, b, h, s_q, s_pq, s_exp);
       const int nblk = (t1 - t0 + 15) >> 4;
 #pragma unroll
       for (int r = 0; r < kStageRounds; ++r) {
@@ -955,7 +972,7 @@ __global__ __launch_bounds__((split_waves<D, GP>() * 64)) void decode_split_kern
       // into q~, sqrt(pi/2) / d log2(e) sm_scale into p.
       auto setup = [&](bf16x8 (&A1r)[KT][2], bf16x8 (&A3r)[KT]) {
         if (bh == ready_bh) return;
-        if (!kEarlyRotate) rotate_project<D, NW>(a, dv, b, h, s_q, s_pq, s_exp);
+        if (!kEarlyRotate) rotate_project<D, NW, QJ>(a, dv, b, h, s_q, s_pq, s_exp);
         const int arow = lane & 15, kq = lane >> 4;
         const int g = arow % GP;
         const bool is_lo = arow >= GP;
@@ -978,10 +995,12 @@ __global__ __launch_bounds__((split_waves<D, GP>() * 64)) void decode_split_kern
           const float xs[8] = {xa[0], xa[1], xa[2], xa[3], xb[0], xb[1], xb[2], xb[3]};
           const float ys[8] = {ya[0], ya[1], ya[2], ya[3], yb[0], yb[1], yb[2], yb[3]};
           u32x4 w3;
+          if constexpr (QJ) {
 #pragma unroll
-          for (int e = 0; e < 8; e += 2)
-            w3[e / 2] = split(ys[e] * (kappa * a.logit_scale)) | (split(ys[e + 1] * (kappa * a.logit_scale)) << 16);
-          A3r[kt] = __builtin_bit_cast(bf16x8, w3);
+            for (int e = 0; e < 8; e += 2)
+              w3[e / 2] = split(ys[e] * (kappa * a.logit_scale)) | (split(ys[e + 1] * (kappa * a.logit_scale)) << 16);
+            A3r[kt] = __builtin_bit_cast(bf16x8, w3);
+          }
 #pragma unroll
           for (int m = 0; m < 2; ++m) {
             const float ls = a.logit_scale;
@@ -992,7 +1011,7 @@ __global__ __launch_bounds__((split_waves<D, GP>() * 64)) void decode_split_kern
         }
         ready_bh = bh;
       };
-      split_cached_chunk<D, GP, KB, VB>(a, pr, h, t0, t1, s_blk, s_pair, s_sgn, s_p, s_main, s_stat, A1, A3,
+      split_cached_chunk<D, GP, KB, VB, QJ>(a, pr, h, t0, t1, s_blk, s_pair, s_sgn, s_p, s_main, s_stat, A1, A3,
                                         s_m, s_l, b, &s_claim, setup);
     } else if (!kDirect) {
       split_recent<D, GP>(a, b, h, seq_recent(a, b), s_p, s_merge, s_m, s_l);
@@ -1102,6 +1121,7 @@ __global__ __launch_bounds__((split_waves<D, GP>() * 64)) void decode_split_kern
 constexpr int kCombineThreads = 128;
 constexpr int kCombineMaxSplits = 1024;
 
+#if TQ_DECODE_QJL
 template <int D>
 __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DArgs a) {
   __shared__ float s_w[kCombineMaxSplits];
@@ -1145,12 +1165,13 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DArgs a
     a.out[(int64_t)bh * D + c] = L > 0.f ? acc / L : 0.f;
   }
 }
+#endif  // TQ_DECODE_QJL
 
 // ---------------------------------------------------------------------------
-template <int D, int GP, int KB, int VB>
+template <int D, int GP, int KB, int VB, bool QJ>
 static hipError_t launch_split(const DArgs& a, int pr, hipStream_t s) {
-  auto kern = decode_split_kernel<D, GP, KB, VB>;
-  using SL = SplitLds<D, GP, KB, VB>;
+  auto kern = decode_split_kernel<D, GP, KB, VB, QJ>;
+  using SL = SplitLds<D, GP, KB, VB, QJ>;
   size_t lds = SL::total;
   const size_t recent_need = SL::kMainOffset + (size_t)(GP * a.W + GP * D) * 4;
   if (recent_need > lds) lds = recent_need;
@@ -1166,13 +1187,33 @@ static hipError_t launch_split(const DArgs& a, int pr, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int D, int GP>
+template <int D, int GP, bool QJ>
 static hipError_t dispatch_preset(const DArgs& a, int pr, int kb, int vb, hipStream_t s) {
-  if (kb == 2) return vb == 2 ? launch_split<D, GP, 2, 2>(a, pr, s) : launch_split<D, GP, 2, 4>(a, pr, s);
-  if (kb == 3) return vb == 2 ? launch_split<D, GP, 3, 2>(a, pr, s) : launch_split<D, GP, 3, 4>(a, pr, s);
-  return vb == 2 ? launch_split<D, GP, 4, 2>(a, pr, s) : launch_split<D, GP, 4, 4>(a, pr, s);
+  if (kb == 2) return vb == 2 ? launch_split<D, GP, 2, 2, QJ>(a, pr, s) : launch_split<D, GP, 2, 4, QJ>(a, pr, s);
+  if (kb == 3) return vb == 2 ? launch_split<D, GP, 3, 2, QJ>(a, pr, s) : launch_split<D, GP, 3, 4, QJ>(a, pr, s);
+  return vb == 2 ? launch_split<D, GP, 4, 2, QJ>(a, pr, s) : launch_split<D, GP, 4, 4, QJ>(a, pr, s);
 }
 
+// The split launches of one key kind.  This source is compiled twice, with
+// TQ_DECODE_QJL = 1 (keys with the QJL sketch; this object also holds the
+// combine kernel and the entry point) and = 0 (MSE-only keys), so that no
+// kernel is instantiated in both objects.
+hipError_t launch_split_qjl(const DArgs& a, int pr, int d, int G, int kb, int vb, hipStream_t s);
+hipError_t launch_split_mse(const DArgs& a, int pr, int d, int G, int kb, int vb, hipStream_t s);
+
+#if TQ_DECODE_QJL
+hipError_t launch_split_qjl(const DArgs& a, int pr, int d, int G, int kb, int vb, hipStream_t s) {
+  if (d == 128) return G <= 4 ? dispatch_preset<128, 4, true>(a, pr, kb, vb, s) : dispatch_preset<128, 8, true>(a, pr, kb, vb, s);
+  return G <= 4 ? dispatch_preset<256, 4, true>(a, pr, kb, vb, s) : dispatch_preset<256, 8, true>(a, pr, kb, vb, s);
+}
+#else
+hipError_t launch_split_mse(const DArgs& a, int pr, int d, int G, int kb, int vb, hipStream_t s) {
+  if (d == 128) return G <= 4 ? dispatch_preset<128, 4, false>(a, pr, kb, vb, s) : dispatch_preset<128, 8, false>(a, pr, kb, vb, s);
+  return G <= 4 ? dispatch_preset<256, 4, false>(a, pr, kb, vb, s) : dispatch_preset<256, 8, false>(a, pr, kb, vb, s);
+}
+#endif
+
+#if TQ_DECODE_QJL
 template <int D>
 static hipError_t launch_all(const DArgs& a0, const tq_decode_args* args, hipStream_t s) {
   hipError_t e = hipSuccess;
@@ -1184,7 +1225,7 @@ static hipError_t launch_all(const DArgs& a0, const tq_decode_args* args, hipStr
   if (args->split_events[0] && (e = hipEventRecord((hipEvent_t)args->split_events[0], s)) != hipSuccess) return e;
   for (int pr = 0; pr < args->num_presets; ++pr) {
     const tq_ctx* c = args->ctx[pr];
-    e = a.G <= 4 ? dispatch_preset<D, 4>(a, pr, c->kb, c->vb, s) : dispatch_preset<D, 8>(a, pr, c->kb, c->vb, s);
+    e = c->qjl ? launch_split_qjl(a, pr, D, a.G, c->kb, c->vb, s) : launch_split_mse(a, pr, D, a.G, c->kb, c->vb, s);
     if (e != hipSuccess) return e;
   }
   if (args->split_events[1] && (e = hipEventRecord((hipEvent_t)args->split_events[1], s)) != hipSuccess) return e;
@@ -1230,5 +1271,6 @@ hipError_t launch_decode(const tq_decode_args* args, const DecodePlan& plan, hip
   a.scores_stride = args->scores_stride;
   return plan.d == 128 ? launch_all<128>(a, args, stream) : launch_all<256>(a, args, stream);
 }
+#endif  // TQ_DECODE_QJL
 
 }  // namespace tq

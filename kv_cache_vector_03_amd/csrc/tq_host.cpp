@@ -155,12 +155,12 @@ extern "C" int tq_draw_params(uint64_t seed, int32_t d, int8_t* signs, float* S)
 // Paged record layout (iThome: block table + paged KV cache; the byte layout
 // is this library's own: 16-slot records, each region 16-byte aligned).
 // ---------------------------------------------------------------------------
-Layout tq::make_layout(int d, int kb, int vb) {
+Layout tq::make_layout(int d, int kb, int vb, bool qjl) {
   Layout l;
   int64_t o = 0;
   l.kcodes = o; o += 16 * (kb * d / 8);
-  l.kqjl = o;   o += 16 * (d / 8);
-  l.kmeta = o;  o += 16 * 4;
+  l.kqjl = o;   o += qjl ? 16 * (d / 8) : 0;
+  l.kmeta = o;  o += 16 * (qjl ? 4 : 2);
   l.vcodes = o; o += (vb * d / 8) * 16;
   l.vmeta = o;  o += (d / 32) * 16 * 4;
   l.bytes = o;
@@ -174,10 +174,12 @@ int check_preset(const tq_preset* p) {
     return TQ_EINVAL;
   }
   if ((p->head_dim != 128 && p->head_dim != 256) || p->k_bits < 2 || p->k_bits > 4 ||
-      (p->v_bits != 2 && p->v_bits != 4) || p->v_group != 32 || p->block_size != 16) {
-    set_error("unsupported preset: head_dim %d k_bits %d v_bits %d v_group %d block_size %d "
-              "(supported: head_dim 128|256, k_bits 2..4, v_bits 2|4, v_group 32, block_size 16)",
-              p->head_dim, p->k_bits, p->v_bits, p->v_group, p->block_size);
+      (p->v_bits != 2 && p->v_bits != 4) || p->v_group != 32 || p->block_size != 16 ||
+      (p->flags & ~TQ_PRESET_MSE_ONLY) != 0) {
+    set_error("unsupported preset: head_dim %d k_bits %d v_bits %d v_group %d block_size %d flags %d "
+              "(supported: head_dim 128|256, k_bits 2..4, v_bits 2|4, v_group 32, block_size 16, "
+              "flags 0|TQ_PRESET_MSE_ONLY)",
+              p->head_dim, p->k_bits, p->v_bits, p->v_group, p->block_size, p->flags);
     return TQ_EUNSUPPORTED;
   }
   return TQ_OK;
@@ -215,7 +217,7 @@ extern "C" int tq_record_layout(const tq_preset* p, tq_layout* out) {
     set_error("tq_record_layout: out is NULL");
     return TQ_EINVAL;
   }
-  Layout l = make_layout(p->head_dim, p->k_bits, p->v_bits);
+  Layout l = make_layout(p->head_dim, p->k_bits, p->v_bits, (p->flags & TQ_PRESET_MSE_ONLY) == 0);
   out->kcodes = l.kcodes;
   out->kqjl = l.kqjl;
   out->kmeta = l.kmeta;
@@ -260,7 +262,8 @@ extern "C" int tq_codebook_init(const tq_preset* p, const int8_t* signs, const f
   c->d = d;
   c->kb = kb;
   c->vb = vb;
-  c->lay = make_layout(d, kb, vb);
+  c->qjl = (p->flags & TQ_PRESET_MSE_ONLY) == 0;
+  c->lay = make_layout(d, kb, vb, c->qjl);
   c->c64.resize(L);
   c->t64.resize(L - 1);
   tq_lloyd_max(d, kb, c->c64.data(), c->t64.data());

@@ -40,6 +40,7 @@ struct tq_ctx {
   tq_preset preset;
   int device = 0;
   int d = 0, kb = 0, vb = 0;
+  bool qjl = true;  // false: MSE-only keys (no sign bits, no residual norm)
   std::vector<double> c64, t64;
   std::vector<float> c32, t32;
   std::vector<int8_t> signs;  // [2][d]
@@ -56,7 +57,7 @@ constexpr int kRScaleLog2 = 6;   // r is pre-scaled by 64 before the fp16 split
 
 void set_error(const char* fmt, ...);
 
-Layout make_layout(int d, int kb, int vb);
+Layout make_layout(int d, int kb, int vb, bool qjl);
 
 // Kernel launchers (defined in the .hip files); return a hipError_t.
 hipError_t launch_quantize(const tq_ctx* c, const void* k, const void* v, int in_dtype, int64_t num_tokens,

@@ -100,7 +100,7 @@ __device__ __forceinline__ float wht_quad(float x, float sg) {
   return __builtin_fmaf(sg, x, y);
 }
 
-template <int D, int KB, int VB, bool BF16>
+template <int D, int KB, int VB, bool BF16, bool QJ>
 __global__ __launch_bounds__(kQWaves<D> * 64) void quantize_kernel(QArgs a) {
   constexpr int E = D / 4;
   constexpr int L = 1 << KB;
@@ -117,7 +117,7 @@ __global__ __launch_bounds__(kQWaves<D> * 64) void quantize_kernel(QArgs a) {
   const int wave = tid >> 6, lane = tid & 63;
   const int row = lane >> 2, part = lane & 3;
 
-  if constexpr (QLds<D>::kTilesInLds) {
+  if constexpr (QLds<D>::kTilesInLds && QJ) {
     const u32x4* src = reinterpret_cast<const u32x4*>(a.dev.s_tiles_d2);
     u32x4* dst = reinterpret_cast<u32x4*>(s_tiles);
     constexpr int n16 = (int)(QLds<D>::tiles_bytes / 16);
@@ -255,6 +255,8 @@ __global__ __launch_bounds__(kQWaves<D> * 64) void quantize_kernel(QArgs a) {
     const float gamma = __builtin_sqrtf(quad_sum_xl(r2));
 
     // ---- stage the scaled residual as fp16 hi/lo rows for the MFMA A operand
+    // (MSE-only keys skip the whole sketch)
+    if constexpr (QJ) {
 #pragma unroll
     for (int e = 0; e < E; e += 2) {
       float v0 = x[e] * rscale, v1 = x[e + 1] * rscale;
@@ -302,6 +304,7 @@ __global__ __launch_bounds__(kQWaves<D> * 64) void quantize_kernel(QArgs a) {
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);
     __builtin_amdgcn_wave_barrier();
+    }  // QJ
 
     // ---- pack and store the key record
     const int32_t slot = valid ? a.slot_mapping[t] : -1;
@@ -324,6 +327,10 @@ __global__ __launch_bounds__(kQWaves<D> * 64) void quantize_kernel(QArgs a) {
       uint32_t qw[SW];
 #pragma unroll
       for (int i = 0; i < SW; ++i) {
+        if constexpr (!QJ) {
+          qw[i] = 0;
+          continue;
+        }
         uint32_t lo16 = (uint32_t)(ballots[(part * E / 16 + 2 * i) * 4 + (row & 3)] >> (16 * (row >> 2))) & 0xFFFFu;
         uint32_t hi16 = (uint32_t)(ballots[(part * E / 16 + 2 * i + 1) * 4 + (row & 3)] >> (16 * (row >> 2))) & 0xFFFFu;
         qw[i] = zero ? 0u : (lo16 | (hi16 << 16));
@@ -332,12 +339,16 @@ __global__ __launch_bounds__(kQWaves<D> * 64) void quantize_kernel(QArgs a) {
         uint32_t* kc = reinterpret_cast<uint32_t*>(base + a.lay.kcodes + s * (KB * D / 8) + part * (KB * E / 8));
 #pragma unroll
         for (int i = 0; i < CW; ++i) kc[i] = w[i];
-        uint32_t* kq = reinterpret_cast<uint32_t*>(base + a.lay.kqjl + s * (D / 8) + part * (E / 8));
+        if constexpr (QJ) {
+          uint32_t* kq = reinterpret_cast<uint32_t*>(base + a.lay.kqjl + s * (D / 8) + part * (E / 8));
 #pragma unroll
-        for (int i = 0; i < SW; ++i) kq[i] = qw[i];
-        if (part == 0) {
-          uint32_t meta = (uint32_t)f32_to_f16_bits(zero ? 0.f : n) | ((uint32_t)f32_to_f16_bits(gamma) << 16);
-          *reinterpret_cast<uint32_t*>(base + a.lay.kmeta + s * 4) = meta;
+          for (int i = 0; i < SW; ++i) kq[i] = qw[i];
+          if (part == 0) {
+            uint32_t meta = (uint32_t)f32_to_f16_bits(zero ? 0.f : n) | ((uint32_t)f32_to_f16_bits(gamma) << 16);
+            *reinterpret_cast<uint32_t*>(base + a.lay.kmeta + s * 4) = meta;
+          }
+        } else if (part == 0) {
+          *reinterpret_cast<uint16_t*>(base + a.lay.kmeta + s * 2) = f32_to_f16_bits(zero ? 0.f : n);
         }
       }
     }
@@ -454,7 +465,7 @@ __device__ __forceinline__ void load_few(const void* base, int64_t elem_off, flo
   }
 }
 
-template <int D, int KB, int VB, bool BF16>
+template <int D, int KB, int VB, bool BF16, bool QJ>
 __global__ __launch_bounds__(kRowWaves * 64) void quantize_rows_kernel(QArgs a) {
   constexpr int P = D / 64;
   constexpr int L = 1 << KB;
@@ -494,13 +505,15 @@ __global__ __launch_bounds__(kRowWaves * 64) void quantize_rows_kernel(QArgs a) 
   // not depend on the token, so their round trip overlaps the one above
   constexpr int NTW = NT / kRowWaves;
   f16x8 bhi[NTW][KT], blo[NTW][KT];
+  if constexpr (QJ) {
 #pragma unroll
-  for (int i = 0; i < NTW; ++i) {
+    for (int i = 0; i < NTW; ++i) {
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
-      const size_t tb = ((((size_t)(wave + kRowWaves * i)) * KT + kt) * 2) * 64 * 8;
-      bhi[i][kt] = *reinterpret_cast<const f16x8*>(a.dev.s_tiles + tb + lane * 8);
-      blo[i][kt] = *reinterpret_cast<const f16x8*>(a.dev.s_tiles + tb + 512 + lane * 8);
+      for (int kt = 0; kt < KT; ++kt) {
+        const size_t tb = ((((size_t)(wave + kRowWaves * i)) * KT + kt) * 2) * 64 * 8;
+        bhi[i][kt] = *reinterpret_cast<const f16x8*>(a.dev.s_tiles + tb + lane * 8);
+        blo[i][kt] = *reinterpret_cast<const f16x8*>(a.dev.s_tiles + tb + 512 + lane * 8);
+      }
     }
   }
 
@@ -557,8 +570,8 @@ __global__ __launch_bounds__(kRowWaves * 64) void quantize_rows_kernel(QArgs a) 
   __syncthreads();  // every wave's residual is in LDS
 
   // ---- z = S r for the workgroup's token-heads (A rows 0..3); wave w takes
-  // column tiles w, w + 4, ...
-  {
+  // column tiles w, w + 4, ...  (skipped for MSE-only keys)
+  if constexpr (QJ) {
     const int arow = lane & 15, kq = lane >> 4;
     f16x8 ahi[KT], alo[KT];
 #pragma unroll
@@ -609,11 +622,15 @@ __global__ __launch_bounds__(kRowWaves * 64) void quantize_rows_kernel(QArgs a) 
       }
       *reinterpret_cast<uint32_t*>(base + a.lay.kcodes + sl * (KB * D / 8) + 4 * lane) = w;
     }
-    if (lane < D / 32)
-      *reinterpret_cast<uint32_t*>(base + a.lay.kqjl + sl * (D / 8) + 4 * lane) = zero ? 0u : s_qjl[wave][lane];
-    if (lane == 0) {
-      const uint32_t meta = (uint32_t)f32_to_f16_bits(zero ? 0.f : n) | ((uint32_t)f32_to_f16_bits(gamma) << 16);
-      *reinterpret_cast<uint32_t*>(base + a.lay.kmeta + sl * 4) = meta;
+    if constexpr (QJ) {
+      if (lane < D / 32)
+        *reinterpret_cast<uint32_t*>(base + a.lay.kqjl + sl * (D / 8) + 4 * lane) = zero ? 0u : s_qjl[wave][lane];
+      if (lane == 0) {
+        const uint32_t meta = (uint32_t)f32_to_f16_bits(zero ? 0.f : n) | ((uint32_t)f32_to_f16_bits(gamma) << 16);
+        *reinterpret_cast<uint32_t*>(base + a.lay.kmeta + sl * 4) = meta;
+      }
+    } else if (lane == 0) {
+      *reinterpret_cast<uint16_t*>(base + a.lay.kmeta + sl * 2) = f32_to_f16_bits(zero ? 0.f : n);
     }
   }
 
@@ -655,16 +672,16 @@ __global__ __launch_bounds__(kRowWaves * 64) void quantize_rows_kernel(QArgs a) 
   }
 }
 
-template <int D, int KB, int VB, bool BF16>
+template <int D, int KB, int VB, bool BF16, bool QJ>
 static hipError_t launch_rows(const QArgs& a, hipStream_t stream) {
   const int64_t grid = (a.num_th + kRowWaves - 1) / kRowWaves;
-  hipLaunchKernelGGL((quantize_rows_kernel<D, KB, VB, BF16>), dim3((unsigned)grid), dim3(kRowWaves * 64), 0, stream, a);
+  hipLaunchKernelGGL((quantize_rows_kernel<D, KB, VB, BF16, QJ>), dim3((unsigned)grid), dim3(kRowWaves * 64), 0, stream, a);
   return hipGetLastError();
 }
 
-template <int D, int KB, int VB, bool BF16>
+template <int D, int KB, int VB, bool BF16, bool QJ>
 static hipError_t launch_q(const QArgs& a, hipStream_t stream) {
-  auto kern = quantize_kernel<D, KB, VB, BF16>;
+  auto kern = quantize_kernel<D, KB, VB, BF16, QJ>;
   const size_t lds = QLds<D>::total;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);
@@ -679,20 +696,25 @@ static hipError_t launch_q(const QArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int D, int KB, bool BF16>
+template <int D, int KB, bool BF16, bool QJ>
 static hipError_t dispatch_vb(const QArgs& a, int vb, hipStream_t s) {
   if (a.num_th <= kRowPathMaxTokenHeads)
-    return vb == 2 ? launch_rows<D, KB, 2, BF16>(a, s) : launch_rows<D, KB, 4, BF16>(a, s);
-  return vb == 2 ? launch_q<D, KB, 2, BF16>(a, s) : launch_q<D, KB, 4, BF16>(a, s);
+    return vb == 2 ? launch_rows<D, KB, 2, BF16, QJ>(a, s) : launch_rows<D, KB, 4, BF16, QJ>(a, s);
+  return vb == 2 ? launch_q<D, KB, 2, BF16, QJ>(a, s) : launch_q<D, KB, 4, BF16, QJ>(a, s);
+}
+
+template <int D, bool BF16, bool QJ>
+static hipError_t dispatch_kb(const QArgs& a, int kb, int vb, hipStream_t s) {
+  switch (kb) {
+    case 2: return dispatch_vb<D, 2, BF16, QJ>(a, vb, s);
+    case 3: return dispatch_vb<D, 3, BF16, QJ>(a, vb, s);
+    default: return dispatch_vb<D, 4, BF16, QJ>(a, vb, s);
+  }
 }
 
 template <int D, bool BF16>
-static hipError_t dispatch_kb(const QArgs& a, int kb, int vb, hipStream_t s) {
-  switch (kb) {
-    case 2: return dispatch_vb<D, 2, BF16>(a, vb, s);
-    case 3: return dispatch_vb<D, 3, BF16>(a, vb, s);
-    default: return dispatch_vb<D, 4, BF16>(a, vb, s);
-  }
+static hipError_t dispatch_kind(const QArgs& a, bool qjl, int kb, int vb, hipStream_t s) {
+  return qjl ? dispatch_kb<D, BF16, true>(a, kb, vb, s) : dispatch_kb<D, BF16, false>(a, kb, vb, s);
 }
 
 hipError_t launch_quantize(const tq_ctx* c, const void* k, const void* v, int in_dtype, int64_t num_tokens,
@@ -711,8 +733,9 @@ hipError_t launch_quantize(const tq_ctx* c, const void* k, const void* v, int in
   a.dev = c->dev;
   a.num_tiles = (a.num_th + 15) / 16;
   const bool bf = in_dtype == TQ_DTYPE_BF16;
-  if (c->d == 128) return bf ? dispatch_kb<128, true>(a, c->kb, c->vb, stream) : dispatch_kb<128, false>(a, c->kb, c->vb, stream);
-  return bf ? dispatch_kb<256, true>(a, c->kb, c->vb, stream) : dispatch_kb<256, false>(a, c->kb, c->vb, stream);
+  if (c->d == 128)
+    return bf ? dispatch_kind<128, true>(a, c->qjl, c->kb, c->vb, stream) : dispatch_kind<128, false>(a, c->qjl, c->kb, c->vb, stream);
+  return bf ? dispatch_kind<256, true>(a, c->qjl, c->kb, c->vb, stream) : dispatch_kind<256, false>(a, c->qjl, c->kb, c->vb, stream);
 }
 
 }  // namespace tq

@@ -33,23 +33,27 @@ def oracle_params(seed: int, d: int, k_bits: int):
             "signs": np.stack([d1, d2]).astype(np.int8)}
 
 
-def expected_records(K, V, slots, head, prm, d, kb, vb, pool, mask):
+def expected_records(K, V, slots, head, prm, d, kb, vb, pool, mask, qjl=True):
     """Encode K, V [N, d] of one KV head with the oracle, write them into the
     expected ``pool`` and mark every bit the comparison must exempt in
-    ``mask`` (same layout).  Returns a dict of exemption counts."""
-    ke = keys.encode_keys(K, prm["d1"], prm["d2"], prm["S"], prm["c32"], prm["t32"])
+    ``mask`` (same layout).  Returns a dict of exemption counts.  ``qjl=False``:
+    MSE-only keys (no sign bits or residual norm to compare)."""
+    ke = keys.encode_keys(K, prm["d1"], prm["d2"], prm["S"], prm["c32"], prm["t32"], qjl=qjl)
     ve = values.encode_values(V, vb)
-    lay = paged.layout(d, kb, vb)
+    lay = paged.layout(d, kb, vb, qjl=qjl)
     paged.write_tokens(pool, slots, head, ke, ve, lay)
 
     t = prm["t32"].astype(np.float64)
     code_band = np.min(np.abs(ke["u"][..., None] - t), axis=-1) <= BAND
     code_band &= ~ke["zero"][:, None]
     vec_hit = code_band.any(axis=1)
-    qjl_band = (np.abs(ke["z"]) <= BAND) & ~ke["zero"][:, None]
-    qjl_band |= vec_hit[:, None]
+    if qjl:
+        qjl_band = (np.abs(ke["z"]) <= BAND) & ~ke["zero"][:, None]
+        qjl_band |= vec_hit[:, None]
+    else:
+        qjl_band = np.zeros_like(code_band)
     n_band = (fp16_midpoint_distance(ke["n"]) <= BAND) & ~ke["zero"]
-    g_band = ((fp16_midpoint_distance(ke["gamma"]) <= BAND) | vec_hit) & ~ke["zero"]
+    g_band = ((fp16_midpoint_distance(ke["gamma"]) <= BAND) | vec_hit) & ~ke["zero"] & qjl
     x = ve["x"]
     v_band = np.abs(x - np.floor(x) - 0.5) <= BAND
     v_band = np.where(np.isnan(x), False, v_band)
@@ -79,19 +83,20 @@ def compare_pools(gpu, expected, mask, select=None):
     return int(outside), int(inside)
 
 
-def oracle_cache(prm, d, kb, vb, lengths, Hkv, block_table, pool, seed, p=0.0, factor=20.0, seqs=None, kv=None):
+def oracle_cache(prm, d, kb, vb, lengths, Hkv, block_table, pool, seed, p=0.0, factor=20.0, seqs=None, kv=None,
+                 qjl=True):
     """Encode seeded keys/values of every (sequence, KV head) with the oracle
     and write them into ``pool`` through ``block_table``.  ``kv(b, h, L)``
     overrides the generator.  Returns the fields per sequence (list over KV
-    heads) for the oracle's decode."""
-    lay = paged.layout(d, kb, vb)
+    heads) for the oracle's decode.  ``qjl=False``: MSE-only keys."""
+    lay = paged.layout(d, kb, vb, qjl=qjl)
     fields = {}
     for b in (range(len(lengths)) if seqs is None else seqs):
         L = int(lengths[b])
         per_head = []
         for h in range(Hkv):
             K, V = kv(b, h, L) if kv is not None else synth.seq_kv(seed, b, h, L, d, p, factor)
-            ke = keys.encode_keys(K.astype(np.float64), prm["d1"], prm["d2"], prm["S"], prm["c32"], prm["t32"])
+            ke = keys.encode_keys(K.astype(np.float64), prm["d1"], prm["d2"], prm["S"], prm["c32"], prm["t32"], qjl=qjl)
             ve = values.encode_values(V, vb)
             t = np.arange(L)
             slots = block_table[b][t // 16].astype(np.int64) * 16 + t % 16

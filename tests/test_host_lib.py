@@ -43,10 +43,11 @@ def test_lloyd_max_agrees_with_oracle(d, b):
     assert t[len(t) // 2] == 0.0 and np.array_equal(c, -c[::-1])
 
 
+@pytest.mark.parametrize("mse_only", [False, True])
 @pytest.mark.parametrize("d,bk,bv", [(128, 3, 4), (128, 3, 2), (128, 4, 4), (128, 2, 2), (256, 4, 4), (256, 3, 2)])
-def test_record_layout_matches_oracle(d, bk, bv):
-    lib_lay = tq.tq_record_layout(d, bk, bv)
-    o = paged.layout(d, bk, bv)
+def test_record_layout_matches_oracle(d, bk, bv, mse_only):
+    lib_lay = tq.tq_record_layout(d, bk, bv, mse_only=mse_only)
+    o = paged.layout(d, bk, bv, qjl=not mse_only)
     for name in ("kcodes", "kqjl", "kmeta", "vcodes", "vmeta"):
         assert lib_lay[name] == o[name][0]
     assert lib_lay["record_bytes"] == o["bytes"]
@@ -76,6 +77,11 @@ def test_unsupported_presets_are_rejected():
         assert "unsupported preset" in tq.tq_last_error()
     p = tq.tq_preset(128, 3, 4, 16, 16, 0, 0)
     assert lib.tq_record_layout(ctypes.byref(p), ctypes.byref(lay)) == tq.TQ_EUNSUPPORTED
+    for flags in (2, 3, -1):  # only TQ_PRESET_MSE_ONLY is a known flag
+        p = tq.tq_preset(128, 3, 4, 32, 16, flags, 0)
+        assert lib.tq_record_layout(ctypes.byref(p), ctypes.byref(lay)) == tq.TQ_EUNSUPPORTED
+    p = tq.tq_preset(128, 3, 4, 32, 16, tq.TQ_PRESET_MSE_ONLY, 0)
+    assert lib.tq_record_layout(ctypes.byref(p), ctypes.byref(lay)) == tq.TQ_OK
     assert lib.tq_record_layout(None, ctypes.byref(lay)) == tq.TQ_EINVAL
 
 
