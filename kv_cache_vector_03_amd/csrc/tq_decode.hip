@@ -7,25 +7,29 @@
 // partials live in a caller-provided workspace; Roadmap §4.4: empty rows and
 // empty splits must not produce NaN or divide by zero.
 //
-// Three launches on one stream:
-//   prep    : q~ = D2 (H/sqrt d) D1 q and p = S q~ per (sequence, query head),
-//             and the per-preset list of work items (sequence, KV head, split);
-//   split   : a persistent grid walks the work items; each 4-wave workgroup
-//             streams one chunk of cached tokens (or the recent full-precision
-//             window) and leaves (m, l, acc[d]) per query head;
-//   combine : log-sum-exp merge of the splits (empty splits contribute 0).
+// One or two launches on one stream:
+//   split   : a persistent grid walks the work items (sequence, KV head,
+//             split); each workgroup rotates and projects the item's queries
+//             (q~ = D2 (H/sqrt d) D1 q, p = S q~), streams one chunk of cached
+//             tokens (or the recent full-precision window) and leaves
+//             (m, l, acc[d]) per query head, or the normalised output itself
+//             when every sequence is a single split;
+//   combine : log-sum-exp merge of the splits (empty splits contribute 0),
+//             only when some sequence has more than one split.
 //
 // In `split`, a wave consumes 32 tokens (two paged blocks) per step:
 //   scores   [G x 16] per block = q~ . c[idx] + p . (2 sigma - 1) on
 //            v_mfma_f32_16x16x32_bf16: A = q~ (bf16 hi rows and lo rows stacked
 //            in the 16 MFMA rows), B = centroid hi / lo of the packed codes
 //            fetched two codes at a time from an LDS pair table, and B = +-1
-//            from an LDS byte table for the sign bits;
+//            from an LDS byte table for the sign bits (MSE-only keys: the
+//            first product alone);
 //   softmax  running max / sum per head in the exp2 domain;
-//   values   acc[(group, head)][channel] += (p s)_hi,lo . (128 + q) on the same
-//            MFMA, with the zero-points and the +128 bias folded into one
-//            per-(group, head) scalar; only the rows of each column's own
-//            group are kept at the end.
+//   values   acc[(group, head)][channel] += (p s)_hi,lo . (1024 + sigma q) on
+//            v_mfma_f32_16x16x32_f16, with the zero-points folded into one
+//            per-(group, head) scalar and the bias removed by one more
+//            product; only the rows of each column's own group are kept at
+//            the end.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
