@@ -52,12 +52,17 @@ enum { TQ_DTYPE_F32 = 0, TQ_DTYPE_BF16 = 1 };
  *   v_bits     : value bits, 2 or 4 (Hub, step 4).
  *   v_group    : value group size, must be 32 (Hub, step 4).
  *   block_size : tokens per paged block, must be 16.
- *   flags      : 0, or TQ_PRESET_MSE_ONLY for keys without the QJL sketch
- *                (iThome, "which path vLLM actually takes": presets with the
- *                Hadamard rotation and MSE-quantised keys but no QJL): the
- *                record then holds no sign bits and no residual norm, and
- *                the score is n <q~, c[idx]> alone.  Other bits are
- *                rejected with TQ_EUNSUPPORTED.
+ *   flags      : a bitwise or of
+ *                TQ_PRESET_MSE_ONLY : keys without the QJL sketch (iThome,
+ *                  "which path vLLM actually takes": presets with the
+ *                  Hadamard rotation and MSE-quantised keys but no QJL): the
+ *                  record then holds no sign bits and no residual norm, and
+ *                  the score is n <q~, c[idx]> alone;
+ *                TQ_PRESET_UNIFORM : equally spaced key centroids (Roadmap
+ *                  §4.3, the "tq4u" mode: c_k = k step + c0) with the
+ *                  least-squares step for the rotated-coordinate law
+ *                  (tq_uniform_codebook) instead of the Lloyd-Max codebook.
+ *                Other bits are rejected with TQ_EUNSUPPORTED.
  *   seed       : seed of the library's own draw of D1, D2 and S when the
  *                caller does not pass them (splitmix64 counter stream; the
  *                signs are the top bit of consecutive outputs, the Gaussians
@@ -72,7 +77,7 @@ typedef struct {
   uint64_t seed;
 } tq_preset;
 
-enum { TQ_PRESET_MSE_ONLY = 1 };
+enum { TQ_PRESET_MSE_ONLY = 1, TQ_PRESET_UNIFORM = 2 };
 
 typedef struct tq_ctx tq_ctx; /* opaque; created by tq_codebook_init */
 
@@ -93,7 +98,8 @@ typedef struct {
 /* ------------------------------------------------------------------ init --
  * Solve the Lloyd-Max codebook of the rotated-coordinate law for
  * (head_dim, k_bits) in fp64 (Hub, technical principle steps 1-2: optimal
- * scalar codebooks for the Beta-distributed rotated coordinates), round it to
+ * scalar codebooks for the Beta-distributed rotated coordinates; with
+ * TQ_PRESET_UNIFORM the equally spaced codebook instead), round it to
  * fp32 centroids and fp32 midpoint thresholds, take the rotation signs and
  * the QJL matrix, and upload everything to the current HIP device.
  *   signs : [2][head_dim] int8, each +1 or -1 (row 0 = D1, row 1 = D2), or
@@ -125,6 +131,10 @@ int tq_ctx_preset(const tq_ctx* ctx, tq_preset* out);
  * tq_draw_params: the seeded draw of D1, D2 (int8 [2][d]) and S (fp32 [d][d])
  * used when tq_codebook_init gets NULL arrays. */
 int tq_lloyd_max(int32_t head_dim, int32_t bits, double* centroids, double* thresholds);
+/* tq_uniform_codebook: the equally spaced codebook of least mean squared
+ * error for the same law (centroids (k - (2^bits-1)/2) step, midpoint
+ * thresholds), same argument rules as tq_lloyd_max. */
+int tq_uniform_codebook(int32_t head_dim, int32_t bits, double* centroids, double* thresholds);
 int tq_record_layout(const tq_preset* preset, tq_layout* out);
 int tq_draw_params(uint64_t seed, int32_t head_dim, int8_t* signs, float* S);
 

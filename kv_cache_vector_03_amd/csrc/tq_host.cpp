@@ -118,6 +118,53 @@ extern "C" int tq_lloyd_max(int32_t d, int32_t bits, double* centroids, double* 
 }
 
 // ---------------------------------------------------------------------------
+// Uniform codebook (Roadmap §4.3, the "tq4u" mode: equally spaced centroids,
+// dequantised as idx * step + c0).  The page fixes the spacing rule only as
+// "linear"; the step taken here is the one of least mean squared error for
+// the same rotated-coordinate law: centroids c_k = a_k step with
+// a_k = k - (L-1)/2 (c0 = -(L-1) step / 2), thresholds at the midpoints.  With
+// cells moving with the step, the midpoint thresholds make the boundary terms
+// of dD/dstep vanish, so the optimum is the root of
+//   F(step) = sum_k a_k (M1_k - a_k step M0_k),
+// M0_k, M1_k the mass and first moment of cell k.  F > 0 for small steps and
+// < 0 for large ones; the root is bracketed and found by bisection to the
+// last bit.
+// ---------------------------------------------------------------------------
+extern "C" int tq_uniform_codebook(int32_t d, int32_t bits, double* centroids, double* thresholds) {
+  if (d < 4 || (d & 1) || bits < 1 || bits > 8 || !centroids || !thresholds) {
+    set_error("tq_uniform_codebook: need even head_dim >= 4, bits in 1..8 and non-NULL outputs");
+    return TQ_EINVAL;
+  }
+  const int L = 1 << bits;
+  const int tm = d - 3;
+  auto F = [&](double step) {
+    double acc = 0.0;
+    for (int k = 0; k < L; ++k) {
+      const double ak = k - 0.5 * (L - 1);
+      // cell k = (midpoint below, midpoint above), cut to the support [-1, 1]
+      const double a = k == 0 ? -1.0 : std::min(1.0, std::max(-1.0, (ak - 0.5) * step));
+      const double b = k == L - 1 ? 1.0 : std::min(1.0, std::max(-1.0, (ak + 0.5) * step));
+      acc += ak * (first_moment(a, b, tm) - ak * step * J(a, b, tm));
+    }
+    return acc;
+  };
+  double lo = 1e-4 / std::sqrt((double)d), hi = 8.0 / std::sqrt((double)d);
+  if (!(F(lo) > 0.0) || !(F(hi) < 0.0)) {
+    set_error("tq_uniform_codebook: no sign change of the stationarity condition for d %d bits %d", d, bits);
+    return TQ_EINVAL;
+  }
+  for (int it = 0; it < 200 && hi - lo > 0.0; ++it) {
+    const double mid = 0.5 * (lo + hi);
+    if (mid <= lo || mid >= hi) break;
+    (F(mid) > 0.0 ? lo : hi) = mid;
+  }
+  const double step = 0.5 * (lo + hi);
+  for (int k = 0; k < L; ++k) centroids[k] = (k - 0.5 * (L - 1)) * step;
+  for (int k = 0; k + 1 < L; ++k) thresholds[k] = 0.5 * (centroids[k] + centroids[k + 1]);
+  return TQ_OK;
+}
+
+// ---------------------------------------------------------------------------
 // Seeded draw of D1, D2 and S (splitmix64 counter stream).
 // ---------------------------------------------------------------------------
 namespace {
@@ -175,10 +222,10 @@ int check_preset(const tq_preset* p) {
   }
   if ((p->head_dim != 128 && p->head_dim != 256) || p->k_bits < 2 || p->k_bits > 4 ||
       (p->v_bits != 2 && p->v_bits != 4) || p->v_group != 32 || p->block_size != 16 ||
-      (p->flags & ~TQ_PRESET_MSE_ONLY) != 0) {
+      (p->flags & ~(TQ_PRESET_MSE_ONLY | TQ_PRESET_UNIFORM)) != 0) {
     set_error("unsupported preset: head_dim %d k_bits %d v_bits %d v_group %d block_size %d flags %d "
               "(supported: head_dim 128|256, k_bits 2..4, v_bits 2|4, v_group 32, block_size 16, "
-              "flags 0|TQ_PRESET_MSE_ONLY)",
+              "flags: TQ_PRESET_MSE_ONLY, TQ_PRESET_UNIFORM or both)",
               p->head_dim, p->k_bits, p->v_bits, p->v_group, p->block_size, p->flags);
     return TQ_EUNSUPPORTED;
   }
@@ -266,7 +313,10 @@ extern "C" int tq_codebook_init(const tq_preset* p, const int8_t* signs, const f
   c->lay = make_layout(d, kb, vb, c->qjl);
   c->c64.resize(L);
   c->t64.resize(L - 1);
-  tq_lloyd_max(d, kb, c->c64.data(), c->t64.data());
+  if (p->flags & TQ_PRESET_UNIFORM)
+    tq_uniform_codebook(d, kb, c->c64.data(), c->t64.data());
+  else
+    tq_lloyd_max(d, kb, c->c64.data(), c->t64.data());
   c->c32.resize(L);
   c->t32.resize(L - 1);
   for (int k = 0; k < L; ++k) c->c32[k] = (float)c->c64[k];

@@ -30,7 +30,7 @@ from __future__ import annotations
 import math
 
 import numpy as np
-from scipy import special
+from scipy import optimize, special
 
 __all__ = [
     "beta_half",
@@ -128,10 +128,39 @@ def lloyd_max(d: int, bits: int, tol: float = 1e-14, max_iter: int = 100000):
     return c, t, it
 
 
-def tables_fp32(d: int, bits: int):
+def uniform(d: int, bits: int):
+    """Equally spaced codebook (Roadmap §4.3, the "tq4u" mode: centroids
+    idx * step + c0).  The page does not say how the step is chosen; the
+    reading here is the step of least mean squared error for the rotated
+    coordinate law, with c0 = -(L - 1) step / 2 (a symmetric codebook) and
+    thresholds at the midpoints.
+
+    With c_k = a_k step, a_k = k - (L - 1)/2, the distortion
+    D(step) = sum_k E[(U - a_k step)^2 1{U in cell k}] has
+    dD/dstep = -2 sum_k a_k (E[U 1{cell k}] - a_k step P(cell k)) (the moving
+    midpoints contribute nothing: both neighbouring centroids are equally far
+    from them), so the optimum is the root of that sum, found by Brent's
+    method.  Returns ``(centroids, thresholds, step)`` in fp64."""
+    levels = 1 << bits
+    a = np.arange(levels, dtype=np.float64) - 0.5 * (levels - 1)
+
+    def dist_slope(step):
+        mids = np.clip((a[:-1] + 0.5) * step, -1.0, 1.0)  # cell edges cut to the support
+        lo = np.concatenate(([-1.0], mids))
+        hi = np.concatenate((mids, [1.0]))
+        return float(np.sum(a * (cell_first_moment(lo, hi, d) - a * step * cell_mass(lo, hi, d))))
+
+    step = optimize.brentq(dist_slope, 1e-4 / np.sqrt(d), 8.0 / np.sqrt(d), xtol=1e-300, rtol=8.9e-16, maxiter=500)
+    c = a * step
+    t = 0.5 * (c[:-1] + c[1:])
+    return c, t, step
+
+
+def tables_fp32(d: int, bits: int, uniform_codebook: bool = False):
     """The stored tables: fp32 centroids and fp32 thresholds, where each
-    threshold is the fp32 rounding of the fp64 midpoint."""
-    c, t, _ = lloyd_max(d, bits)
+    threshold is the fp32 rounding of the fp64 midpoint (of the Lloyd-Max
+    codebook, or of the equally spaced one)."""
+    c, t, _ = uniform(d, bits) if uniform_codebook else lloyd_max(d, bits)
     return c.astype(np.float32), t.astype(np.float32)
 
 

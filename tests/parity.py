@@ -26,9 +26,9 @@ def fp16_midpoint_distance(x):
         return np.where(x > 0, mid / x, np.inf)
 
 
-def oracle_params(seed: int, d: int, k_bits: int):
+def oracle_params(seed: int, d: int, k_bits: int, uniform: bool = False):
     d1, d2, S = synth.method_params(seed, d)
-    c32, t32 = codebook.tables_fp32(d, k_bits)
+    c32, t32 = codebook.tables_fp32(d, k_bits, uniform_codebook=uniform)
     return {"d1": d1.astype(np.float64), "d2": d2.astype(np.float64), "S": S, "c32": c32, "t32": t32,
             "signs": np.stack([d1, d2]).astype(np.int8)}
 

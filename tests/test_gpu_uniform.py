@@ -1,0 +1,102 @@
+"""GPU parity of the equally spaced key codebook (Roadmap §4.3, "tq4u":
+centroids idx * step + c0 with the least-squares step) against the oracle.
+
+The kernels take the codebook from the context's tables, so this checks the
+library's solver (fp32 tables identical to the oracle's) end to end: records
+bit-exact outside the 1e-6 band through both quantise kernels, and decode
+scores / outputs within 1e-3 on oracle-written caches, with and without the
+QJL sketch.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_vector_03_amd as tq
+import synth
+from oracle import attention, paged
+from parity import compare_pools, expected_records, oracle_cache, oracle_params, output_errors, score_errors
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-3
+
+
+@pytest.mark.parametrize("d,kb,vb,T,Hkv,mse_only", [
+    (128, 4, 4, 1500, 8, False),  # tiled kernel
+    (128, 3, 4, 700, 4, False),
+    (128, 4, 4, 900, 4, True),
+    (256, 4, 4, 601, 4, False),
+    (128, 4, 2, 32, 8, False),    # one wave per token-head
+    (128, 3, 4, 5, 8, True),
+])
+def test_uniform_codebook_quantize(d, kb, vb, T, Hkv, mse_only):
+    seed = kb * 10 + vb
+    prm = oracle_params(seed, d, kb, uniform=True)
+    rng = np.random.default_rng([111, d, kb, T])
+    K = synth.normal_with_outliers(rng, (T, Hkv, d), 0.005, 20.0)
+    V = synth.normal_with_outliers(rng, (T, Hkv, d), 0.005, 20.0)
+    nb = (T + 15) // 16 + 4
+    slots = rng.permutation(nb * 16)[:T].astype(np.int64)
+    ctx = tq.tq_codebook_init(d, kb, vb, signs=prm["signs"], S=prm["S"], mse_only=mse_only, uniform=True)
+    c, t, _, _ = tq.tq_ctx_tables(ctx)
+    assert np.array_equal(c, prm["c32"]) and np.array_equal(t, prm["t32"])
+    k = torch.from_numpy(K).to(torch.bfloat16).cuda()
+    v = torch.from_numpy(V).to(torch.bfloat16).cuda()
+    pool = torch.zeros((nb, Hkv, ctx.block_bytes), dtype=torch.uint8, device="cuda")
+    tq.tq_quantize_store(ctx, k, v, torch.from_numpy(slots.astype(np.int32)).cuda(), pool)
+    torch.cuda.synchronize()
+    gpu = pool.cpu().numpy()
+    ctx.close()
+    lay = paged.layout(d, kb, vb, qjl=not mse_only)
+    exp = paged.new_pool(nb, Hkv, lay)
+    mask = paged.new_pool(nb, Hkv, lay)
+    Kx = k.float().cpu().numpy().astype(np.float64)
+    Vx = v.float().cpu().numpy()
+    counts = {}
+    for h in range(Hkv):
+        cnt = expected_records(Kx[:, h], Vx[:, h], slots, h, prm, d, kb, vb, exp, mask, qjl=not mse_only)
+        for key, val in cnt.items():
+            counts[key] = counts.get(key, 0) + val
+    outside, inside = compare_pools(gpu, exp, mask)
+    print(f"[uniform quantize parity d{d} k{kb}v{vb} T={T}x{Hkv} mse_only={mse_only}] exempt={counts} "
+          f"differing bits outside band={outside} inside band={inside}", flush=True)
+    assert outside == 0
+
+
+@pytest.mark.parametrize("kb,vb,chunk,mse_only", [(4, 4, 512, False), (3, 2, 2048, False), (4, 4, 256, True)])
+def test_uniform_codebook_decode(kb, vb, chunk, mse_only):
+    seed, d, B, Hq, Hkv = 112 + kb, 128, 4, 8, 2
+    lens = np.array([1000, 33, 0, 2000])
+    prm = oracle_params(seed, d, kb, uniform=True)
+    prm["qjl"] = not mse_only
+    mb = int(np.ceil(lens.max() / 16))
+    nb = B * mb + 3
+    bt = synth.block_table(seed, B, mb, nb)
+    pool = paged.new_pool(nb, Hkv, paged.layout(d, kb, vb, qjl=not mse_only))
+    fields = oracle_cache(prm, d, kb, vb, lens, Hkv, bt, pool, seed, p=0.005, qjl=not mse_only)
+    q = synth.queries(seed, B, Hq, d)
+    ctx = tq.tq_codebook_init(d, kb, vb, signs=prm["signs"], S=prm["S"], mse_only=mse_only, uniform=True)
+    qd = torch.from_numpy(q).cuda()
+    pd = torch.from_numpy(pool).cuda()
+    btd = torch.from_numpy(bt.astype(np.int32)).cuda()
+    lensd = torch.from_numpy(lens.astype(np.int32)).cuda()
+    msl = mb * 16
+    out = torch.full((B, Hq, d), float("nan"), dtype=torch.float32, device="cuda")
+    sc = torch.full((B, Hq, msl), float("nan"), dtype=torch.float32, device="cuda")
+    nbytes = tq.tq_decode_workspace_bytes(qd, [ctx], [pd], btd, lensd, out, chunk_tokens=chunk, max_seq_len=msl)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+    tq.tq_decode_attention(qd, [ctx], [pd], btd, lensd, out, ws, chunk_tokens=chunk, max_seq_len=msl, scores_out=sc)
+    torch.cuda.synchronize()
+    out, sc = out.cpu().numpy(), sc.cpu().numpy()
+    ctx.close()
+    ref, errs = [], []
+    for b in range(B):
+        o, s = attention.decode_one_sequence(q[b].astype(np.float64), fields[b], prm)
+        ref.append(o)
+        if s.shape[1]:
+            errs.append(score_errors(sc[b, :, :s.shape[1]].astype(np.float64), s))
+    se, oe = max(errs), output_errors(out.astype(np.float64), np.stack(ref))
+    print(f"[uniform decode parity k{kb}v{vb} chunk {chunk} mse_only={mse_only}] max score err {se:.2e} "
+          f"max out err {oe:.2e}", flush=True)
+    assert np.all(np.isfinite(out)) and se <= TOL and oe <= TOL

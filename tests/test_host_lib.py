@@ -43,6 +43,16 @@ def test_lloyd_max_agrees_with_oracle(d, b):
     assert t[len(t) // 2] == 0.0 and np.array_equal(c, -c[::-1])
 
 
+@pytest.mark.parametrize("d", [128, 256])
+@pytest.mark.parametrize("b", [2, 3, 4])
+def test_uniform_codebook_agrees_with_oracle(d, b):
+    c, t = tq.tq_uniform_codebook(d, b)
+    c2, t2, step = codebook.uniform(d, b)
+    assert np.max(np.abs(c - c2)) < 1e-12 * step * (1 << b)
+    assert np.array_equal(c.astype(np.float32), c2.astype(np.float32))
+    assert np.array_equal(t.astype(np.float32), t2.astype(np.float32))
+
+
 @pytest.mark.parametrize("mse_only", [False, True])
 @pytest.mark.parametrize("d,bk,bv", [(128, 3, 4), (128, 3, 2), (128, 4, 4), (128, 2, 2), (256, 4, 4), (256, 3, 2)])
 def test_record_layout_matches_oracle(d, bk, bv, mse_only):
@@ -77,7 +87,7 @@ def test_unsupported_presets_are_rejected():
         assert "unsupported preset" in tq.tq_last_error()
     p = tq.tq_preset(128, 3, 4, 16, 16, 0, 0)
     assert lib.tq_record_layout(ctypes.byref(p), ctypes.byref(lay)) == tq.TQ_EUNSUPPORTED
-    for flags in (2, 3, -1):  # only TQ_PRESET_MSE_ONLY is a known flag
+    for flags in (4, 5, -1):  # TQ_PRESET_MSE_ONLY and TQ_PRESET_UNIFORM are the known flags
         p = tq.tq_preset(128, 3, 4, 32, 16, flags, 0)
         assert lib.tq_record_layout(ctypes.byref(p), ctypes.byref(lay)) == tq.TQ_EUNSUPPORTED
     p = tq.tq_preset(128, 3, 4, 32, 16, tq.TQ_PRESET_MSE_ONLY, 0)
