@@ -20,9 +20,10 @@ from __future__ import annotations
 import numpy as np
 
 from . import keys as _keys
+from . import rotation as _rot
 from . import values as _values
 
-__all__ = ["decode_one_sequence", "softmax_attend"]
+__all__ = ["decode_one_sequence", "softmax_attend", "fold_output_projection"]
 
 
 def softmax_attend(logits, values) -> np.ndarray:
@@ -71,3 +72,20 @@ def decode_one_sequence(q, fields_per_head, ctx, recent_k=None, recent_v=None, s
         outs.append(softmax_attend(scale * s_all, v_all))
         scores.append(s_all)
     return np.stack(outs), np.stack(scores)
+
+
+def fold_output_projection(w_o, d1, d2, num_heads: int) -> np.ndarray:
+    """Output projection with the inverse value rotation absorbed (Roadmap
+    §4.2, W_O weight absorption): when the cached values are rotated, the
+    attention output of head h is (approximately) Pi o_h, and
+    W_o [.., h d:(h+1) d] Pi^-1 restores W_o o.  Pi^-1 = D1 (H / sqrt d) D2:
+    the sign vectors in the reverse order of the forward rotation (the order
+    the page's code review caught).  Returns W_o blockdiag(Pi^-1, ...) in
+    fp64."""
+    w = np.asarray(w_o, dtype=np.float64)
+    d = np.asarray(d1).shape[0]
+    inv = _rot.inverse_rotation_matrix(d1, d2)
+    out = np.empty_like(w)
+    for h in range(num_heads):
+        out[:, h * d:(h + 1) * d] = w[:, h * d:(h + 1) * d] @ inv
+    return out

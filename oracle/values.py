@@ -23,8 +23,9 @@ from __future__ import annotations
 import numpy as np
 
 from . import bits as _bits
+from . import rotation as _rot
 
-__all__ = ["encode_values", "dequantize_values", "GROUP"]
+__all__ = ["encode_values", "dequantize_values", "rotate_values", "GROUP"]
 
 GROUP = 32
 
@@ -72,3 +73,14 @@ def dequantize_values(q, s16, z16) -> np.ndarray:
     s = _bits.from_fp16_bits(s16).reshape(N, d // GROUP, 1)
     z = _bits.from_fp16_bits(z16).reshape(N, d // GROUP, 1)
     return (q.reshape(N, d // GROUP, GROUP) * s + z).reshape(N, d)
+
+
+def rotate_values(v, d1, d2) -> np.ndarray:
+    """Rotated values for the weight-absorption variant (Roadmap §4.2: the
+    value vectors are rotated with the same D2 H D1 / sqrt(d) as the keys when
+    they are written, and the inverse rotation is folded into the output
+    projection instead of being applied at read time).
+
+    Reading: the rotation is taken exactly (fp64) and rounded once to fp32;
+    the group quantisation then runs on those fp32 values unchanged."""
+    return _rot.rotate(np.asarray(v, dtype=np.float64), d1, d2).astype(np.float32)
