@@ -61,7 +61,12 @@ enum { TQ_DTYPE_F32 = 0, TQ_DTYPE_BF16 = 1 };
  *                TQ_PRESET_UNIFORM : equally spaced key centroids (Roadmap
  *                  §4.3, the "tq4u" mode: c_k = k step + c0) with the
  *                  least-squares step for the rotated-coordinate law
- *                  (tq_uniform_codebook) instead of the Lloyd-Max codebook.
+ *                  (tq_uniform_codebook) instead of the Lloyd-Max codebook;
+ *                TQ_PRESET_ROTATE_V : values rotated with the keys' D2 H D1 /
+ *                  sqrt(d) before their group quantisation (Roadmap §4.2,
+ *                  W_O weight absorption): decode then returns rotated head
+ *                  outputs, and tq_fold_output_projection gives the output
+ *                  projection that undoes the rotation.
  *                Other bits are rejected with TQ_EUNSUPPORTED.
  *   seed       : seed of the library's own draw of D1, D2 and S when the
  *                caller does not pass them (splitmix64 counter stream; the
@@ -77,7 +82,7 @@ typedef struct {
   uint64_t seed;
 } tq_preset;
 
-enum { TQ_PRESET_MSE_ONLY = 1, TQ_PRESET_UNIFORM = 2 };
+enum { TQ_PRESET_MSE_ONLY = 1, TQ_PRESET_UNIFORM = 2, TQ_PRESET_ROTATE_V = 4 };
 
 typedef struct tq_ctx tq_ctx; /* opaque; created by tq_codebook_init */
 
@@ -138,6 +143,20 @@ int tq_uniform_codebook(int32_t head_dim, int32_t bits, double* centroids, doubl
 int tq_record_layout(const tq_preset* preset, tq_layout* out);
 int tq_draw_params(uint64_t seed, int32_t head_dim, int8_t* signs, float* S);
 
+/* Output projection with the inverse value rotation absorbed (Roadmap §4.2:
+ * the inverse D1 H D2 / sqrt(d) -- the sign vectors in the reverse order of
+ * the forward rotation -- folded into W_O once at load time, so decode over
+ * a TQ_PRESET_ROTATE_V cache needs no inverse rotation):
+ *   out[r][h d + j] = sum_i w_o[r][h d + i] Pi^-1[i][j],  h < num_q_heads,
+ * i.e. every d-wide block of every row is mapped through D2 H D1 / sqrt(d)
+ * (computed in fp64, rounded to fp32).
+ *   signs : the context's [2][head_dim] int8 +-1 (row 0 = D1, row 1 = D2), as
+ *           passed to tq_codebook_init or read back with tq_ctx_tables;
+ *   w_o, out : host fp32 [rows][num_q_heads * head_dim] row-major; out may
+ *           equal w_o.  Host-only; head_dim a power of two in 2..4096. */
+int tq_fold_output_projection(int32_t head_dim, const int8_t* signs, const float* w_o, int64_t rows,
+                              int32_t num_q_heads, float* out);
+
 /* Bytes of one (block, KV head) record; 0 on a NULL context. */
 size_t tq_block_bytes(const tq_ctx* ctx);
 
@@ -149,7 +168,8 @@ size_t tq_block_bytes(const tq_ctx* ctx);
  *   n = ||k||; u = D2 (H/sqrt d) D1 k / n; idx_j = #{t : thr_t < u_j};
  *   r = u - c[idx]; gamma = ||r||; sign_i = [(S r)_i >= 0] (MSE-only presets
  *   stop at idx and store n alone);
- *   values per group of 32: s = fp16((max-min)/(2^v_bits-1)), z = fp16(min),
+ *   values (TQ_PRESET_ROTATE_V: first v <- fp32(D2 (H/sqrt d) D1 v), exact in
+ *   fp64 before the one rounding) per group of 32: s = fp16((max-min)/(2^v_bits-1)), z = fp16(min),
  *   q = clamp(rint((v - z)/s), 0, 2^v_bits - 1) (q = 0 when s = 0).
  *   k, v         : device [num_tokens][num_kv_heads][head_dim], in_dtype
  *                  TQ_DTYPE_BF16 or TQ_DTYPE_F32; 16-byte aligned.

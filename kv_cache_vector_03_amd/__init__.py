@@ -14,7 +14,7 @@ import os
 
 __all__ = [
     "TQ_OK", "TQ_EINVAL", "TQ_EUNSUPPORTED", "TQ_EHIP", "TQ_ENOMEM", "TQ_DTYPE_F32", "TQ_DTYPE_BF16", "TQ_PRESET_MSE_ONLY",
-    "TQ_PRESET_UNIFORM", "tq_uniform_codebook",
+    "TQ_PRESET_UNIFORM", "TQ_PRESET_ROTATE_V", "tq_uniform_codebook", "tq_fold_output_projection",
     "TqError", "Context", "library_path", "load", "tq_codebook_init", "tq_ctx_destroy", "tq_ctx_tables",
     "tq_lloyd_max", "tq_record_layout", "tq_draw_params", "tq_block_bytes", "tq_quantize_store",
     "tq_decode_workspace_bytes", "tq_decode_attention", "tq_last_error", "EXPORTED_SYMBOLS",
@@ -24,10 +24,11 @@ TQ_OK, TQ_EINVAL, TQ_EUNSUPPORTED, TQ_EHIP, TQ_ENOMEM = 0, -1, -2, -3, -4
 TQ_DTYPE_F32, TQ_DTYPE_BF16 = 0, 1
 TQ_PRESET_MSE_ONLY = 1
 TQ_PRESET_UNIFORM = 2
+TQ_PRESET_ROTATE_V = 4
 
 EXPORTED_SYMBOLS = [
     "tq_codebook_init", "tq_ctx_destroy", "tq_ctx_tables", "tq_ctx_preset", "tq_lloyd_max", "tq_uniform_codebook",
-    "tq_record_layout",
+    "tq_record_layout", "tq_fold_output_projection",
     "tq_draw_params", "tq_block_bytes", "tq_quantize_store", "tq_decode_workspace_bytes", "tq_decode_attention",
     "tq_last_error",
 ]
@@ -89,6 +90,7 @@ def load(path: str | None = None):
         "tq_ctx_preset": (c.c_int, [P, c.POINTER(tq_preset)]),
         "tq_lloyd_max": (c.c_int, [c.c_int32, c.c_int32, P, P]),
         "tq_uniform_codebook": (c.c_int, [c.c_int32, c.c_int32, P, P]),
+        "tq_fold_output_projection": (c.c_int, [c.c_int32, P, P, c.c_int64, c.c_int32, P]),
         "tq_record_layout": (c.c_int, [c.POINTER(tq_preset), c.POINTER(tq_layout)]),
         "tq_draw_params": (c.c_int, [c.c_uint64, c.c_int32, P, P]),
         "tq_block_bytes": (c.c_size_t, [P]),
@@ -145,10 +147,10 @@ class Context:
     """Owner of a ``tq_ctx*`` (freed on ``close()`` or garbage collection)."""
 
     def __init__(self, handle: int, head_dim: int, k_bits: int, v_bits: int, mse_only: bool = False,
-                 uniform: bool = False):
+                 uniform: bool = False, rotate_v: bool = False):
         self.handle = handle
         self.head_dim, self.k_bits, self.v_bits = head_dim, k_bits, v_bits
-        self.mse_only, self.uniform = mse_only, uniform
+        self.mse_only, self.uniform, self.rotate_v = mse_only, uniform, rotate_v
 
     @property
     def block_bytes(self) -> int:
@@ -167,13 +169,15 @@ class Context:
 
 
 def tq_codebook_init(head_dim: int, k_bits: int, v_bits: int, seed: int = 0, signs=None, S=None,
-                     mse_only: bool = False, uniform: bool = False) -> Context:
+                     mse_only: bool = False, uniform: bool = False, rotate_v: bool = False) -> Context:
     """Create a context.  ``signs`` (int8 [2, d]) and ``S`` (float32 [d, d])
     are host numpy arrays or None (then drawn from ``seed``); ``mse_only``
     selects keys without the QJL sketch (TQ_PRESET_MSE_ONLY), ``uniform`` the
-    equally spaced key codebook (TQ_PRESET_UNIFORM)."""
+    equally spaced key codebook (TQ_PRESET_UNIFORM), ``rotate_v`` rotated
+    values (TQ_PRESET_ROTATE_V)."""
     lib = load()
-    flags = (TQ_PRESET_MSE_ONLY if mse_only else 0) | (TQ_PRESET_UNIFORM if uniform else 0)
+    flags = ((TQ_PRESET_MSE_ONLY if mse_only else 0) | (TQ_PRESET_UNIFORM if uniform else 0)
+             | (TQ_PRESET_ROTATE_V if rotate_v else 0))
     p = tq_preset(head_dim, k_bits, v_bits, 32, 16, flags, seed)
     h = ctypes.c_void_p()
     if signs is not None:
@@ -183,7 +187,7 @@ def tq_codebook_init(head_dim: int, k_bits: int, v_bits: int, seed: int = 0, sig
         import numpy as np
         S = np.ascontiguousarray(S, dtype=np.float32)
     _check(lib.tq_codebook_init(ctypes.byref(p), _ptr(signs), _ptr(S), ctypes.byref(h)), "tq_codebook_init")
-    return Context(h.value, head_dim, k_bits, v_bits, mse_only, uniform)
+    return Context(h.value, head_dim, k_bits, v_bits, mse_only, uniform, rotate_v)
 
 
 def tq_ctx_destroy(ctx: Context) -> None:
@@ -217,6 +221,19 @@ def tq_uniform_codebook(head_dim: int, bits: int):
     t = np.zeros((1 << bits) - 1, np.float64)
     _check(load().tq_uniform_codebook(head_dim, bits, _ptr(c), _ptr(t)), "tq_uniform_codebook")
     return c, t
+
+
+def tq_fold_output_projection(signs, w_o, num_q_heads: int):
+    """W_o [rows, num_q_heads * d] (host fp32) with the inverse value rotation
+    absorbed, for the context whose rotation signs are ``signs`` (int8 [2, d]);
+    returns a new fp32 numpy array."""
+    import numpy as np
+    sg = np.ascontiguousarray(signs, dtype=np.int8)
+    w = np.ascontiguousarray(w_o, dtype=np.float32)
+    out = np.empty_like(w)
+    _check(load().tq_fold_output_projection(sg.shape[1], _ptr(sg), _ptr(w), w.shape[0], num_q_heads, _ptr(out)),
+           "tq_fold_output_projection")
+    return out
 
 
 def tq_record_layout(head_dim: int, k_bits: int, v_bits: int, mse_only: bool = False, flags=None) -> dict:

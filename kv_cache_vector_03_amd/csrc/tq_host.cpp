@@ -222,10 +222,10 @@ int check_preset(const tq_preset* p) {
   }
   if ((p->head_dim != 128 && p->head_dim != 256) || p->k_bits < 2 || p->k_bits > 4 ||
       (p->v_bits != 2 && p->v_bits != 4) || p->v_group != 32 || p->block_size != 16 ||
-      (p->flags & ~(TQ_PRESET_MSE_ONLY | TQ_PRESET_UNIFORM)) != 0) {
+      (p->flags & ~(TQ_PRESET_MSE_ONLY | TQ_PRESET_UNIFORM | TQ_PRESET_ROTATE_V)) != 0) {
     set_error("unsupported preset: head_dim %d k_bits %d v_bits %d v_group %d block_size %d flags %d "
               "(supported: head_dim 128|256, k_bits 2..4, v_bits 2|4, v_group 32, block_size 16, "
-              "flags: TQ_PRESET_MSE_ONLY, TQ_PRESET_UNIFORM or both)",
+              "flags: an or of TQ_PRESET_MSE_ONLY, TQ_PRESET_UNIFORM, TQ_PRESET_ROTATE_V)",
               p->head_dim, p->k_bits, p->v_bits, p->v_group, p->block_size, p->flags);
     return TQ_EUNSUPPORTED;
   }
@@ -310,6 +310,7 @@ extern "C" int tq_codebook_init(const tq_preset* p, const int8_t* signs, const f
   c->kb = kb;
   c->vb = vb;
   c->qjl = (p->flags & TQ_PRESET_MSE_ONLY) == 0;
+  c->rotv = (p->flags & TQ_PRESET_ROTATE_V) != 0;
   c->lay = make_layout(d, kb, vb, c->qjl);
   c->c64.resize(L);
   c->t64.resize(L - 1);
@@ -447,6 +448,37 @@ extern "C" int tq_ctx_preset(const tq_ctx* c, tq_preset* out) {
     return TQ_EINVAL;
   }
   *out = c->preset;
+  return TQ_OK;
+}
+
+extern "C" int tq_fold_output_projection(int32_t d, const int8_t* signs, const float* w_o, int64_t rows,
+                                         int32_t num_q_heads, float* out) {
+  if (d < 2 || d > 4096 || (d & (d - 1)) || !signs || !w_o || !out || rows < 0 || num_q_heads <= 0) {
+    set_error("tq_fold_output_projection: need head_dim a power of two in 2..4096, non-NULL arrays, rows >= 0 "
+              "and num_q_heads > 0");
+    return TQ_EINVAL;
+  }
+  for (int i = 0; i < 2 * d; ++i)
+    if (signs[i] != 1 && signs[i] != -1) {
+      set_error("tq_fold_output_projection: signs[%d] = %d is not +-1", i, (int)signs[i]);
+      return TQ_EINVAL;
+    }
+  const double inv_sqrt_d = 1.0 / std::sqrt((double)d);
+  std::vector<double> y(d);
+  for (int64_t r = 0; r < rows; ++r)
+    for (int h = 0; h < num_q_heads; ++h) {
+      const size_t base = (size_t)r * num_q_heads * d + (size_t)h * d;
+      // row block w times Pi^-1 = (Pi w^T)^T: D1, Hadamard butterflies, D2
+      for (int j = 0; j < d; ++j) y[j] = (double)w_o[base + j] * (double)signs[j];
+      for (int hs = 1; hs < d; hs <<= 1)
+        for (int j = 0; j < d; ++j)
+          if ((j & hs) == 0) {
+            const double a = y[j], b = y[j + hs];
+            y[j] = a + b;
+            y[j + hs] = a - b;
+          }
+      for (int j = 0; j < d; ++j) out[base + j] = (float)(y[j] * inv_sqrt_d * (double)signs[d + j]);
+    }
   return TQ_OK;
 }
 

@@ -40,7 +40,8 @@ struct tq_ctx {
   tq_preset preset;
   int device = 0;
   int d = 0, kb = 0, vb = 0;
-  bool qjl = true;  // false: MSE-only keys (no sign bits, no residual norm)
+  bool qjl = true;   // false: MSE-only keys (no sign bits, no residual norm)
+  bool rotv = false; // values rotated before their group quantisation
   std::vector<double> c64, t64;
   std::vector<float> c32, t32;
   std::vector<int8_t> signs;  // [2][d]

@@ -100,7 +100,47 @@ __device__ __forceinline__ float wht_quad(float x, float sg) {
   return __builtin_fmaf(sg, x, y);
 }
 
-template <int D, int KB, int VB, bool BF16, bool QJ>
+// Rotated values (Roadmap §4.2, W_O weight absorption): v <- fp32(D2 (H /
+// sqrt d) D1 v), the butterflies taken in fp64 so that the one rounding to
+// fp32 at the end is the only one (a sum of d fp32 inputs with +-1
+// coefficients is exact in fp64 unless their exponents span more than 22
+// binades).  Tiled layout: lane (row, part) holds coordinates part * E + e;
+// the two highest index bits are the lanes part ^ 1, part ^ 2 of the row.
+// m1 / m2: bit e set where D1 / D2 of coordinate part * E + e is -1.
+template <int E>
+__device__ __forceinline__ void rotate_values_tiled(float (&x)[E], const uint32_t* m1, const uint32_t* m2, int part) {
+  double y[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) y[e] = ((m1[e / 32] >> (e % 32)) & 1u) ? -(double)x[e] : (double)x[e];
+#pragma unroll
+  for (int hs = 1; hs < E; hs <<= 1) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      if ((e & hs) == 0) {
+        const double p = y[e], q = y[e + hs];
+        y[e] = p + q;
+        y[e + hs] = p - q;
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 1; m <= 2; m <<= 1) {
+    const bool upper = (part & m) != 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const double o = __shfl_xor(y[e], m, 64);
+      y[e] = upper ? o - y[e] : y[e] + o;
+    }
+  }
+  const double inv = 1.0 / __builtin_sqrt((double)(4 * E));
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const double v = y[e] * inv;
+    x[e] = (float)(((m2[e / 32] >> (e % 32)) & 1u) ? -v : v);
+  }
+}
+
+template <int D, int KB, int VB, bool BF16, bool QJ, bool ROTV>
 __global__ __launch_bounds__(kQWaves<D> * 64) void quantize_kernel(QArgs a) {
   constexpr int E = D / 4;
   constexpr int L = 1 << KB;
@@ -155,6 +195,16 @@ __global__ __launch_bounds__(kQWaves<D> * 64) void quantize_kernel(QArgs a) {
       const int bp = e * KB;
       m2c[bp / 32] |= (uint32_t)(L - 1) << (bp % 32);
       if ((bp % 32) + KB > 32) m2c[bp / 32 + 1] |= (uint32_t)(L - 1) >> (32 - bp % 32);
+    }
+  }
+  // D2 of this lane's coordinates as bit masks, for rotated values
+  uint32_t m2v[SW];
+#pragma unroll
+  for (int w = 0; w < SW; ++w) {
+    m2v[w] = 0;
+    if constexpr (ROTV) {
+#pragma unroll
+      for (int b = 0; b < 32; ++b) m2v[w] |= (a.dev.signs2[part * E + 32 * w + b] < 0.f ? 1u : 0u) << b;
     }
   }
   const float sg_1 = (part & 1) ? -1.f : 1.f, sg_2 = (part & 2) ? -1.f : 1.f;
@@ -369,6 +419,7 @@ __global__ __launch_bounds__(kQWaves<D> * 64) void quantize_kernel(QArgs a) {
 #pragma unroll
       for (int e = 0; e < E; ++e) x[e] = 0.f;
     }
+    if constexpr (ROTV) rotate_values_tiled<E>(x, m1, m2v, part);
     constexpr int GL = E / 32;  // groups per lane
     constexpr float LV = (float)((1 << VB) - 1);
 #pragma unroll
@@ -465,7 +516,7 @@ __device__ __forceinline__ void load_few(const void* base, int64_t elem_off, flo
   }
 }
 
-template <int D, int KB, int VB, bool BF16, bool QJ>
+template <int D, int KB, int VB, bool BF16, bool QJ, bool ROTV>
 __global__ __launch_bounds__(kRowWaves * 64) void quantize_rows_kernel(QArgs a) {
   constexpr int P = D / 64;
   constexpr int L = 1 << KB;
@@ -634,7 +685,37 @@ __global__ __launch_bounds__(kRowWaves * 64) void quantize_rows_kernel(QArgs a) 
     }
   }
 
-  // ---- value: min-max quantisation of 32-channel groups (32 / P lanes each)
+  // ---- value: rotation (rotated-value presets; fp64 butterflies as in the
+  // tiled kernel, lane bits by shuffles), then min-max quantisation of
+  // 32-channel groups (32 / P lanes each)
+  if constexpr (ROTV) {
+    double y[P];
+#pragma unroll
+    for (int e = 0; e < P; ++e) y[e] = (double)vx[e] * (double)sg1[e];
+#pragma unroll
+    for (int hs = 1; hs < P; hs <<= 1) {
+#pragma unroll
+      for (int e = 0; e < P; ++e) {
+        if ((e & hs) == 0) {
+          const double p = y[e], q = y[e + hs];
+          y[e] = p + q;
+          y[e + hs] = p - q;
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      const bool upper = (lane & m) != 0;
+#pragma unroll
+      for (int e = 0; e < P; ++e) {
+        const double o = __shfl_xor(y[e], m, 64);
+        y[e] = upper ? o - y[e] : y[e] + o;
+      }
+    }
+    const double inv = 1.0 / __builtin_sqrt((double)D);
+#pragma unroll
+    for (int e = 0; e < P; ++e) vx[e] = (float)(y[e] * inv * (double)sg2[e]);
+  }
   constexpr int GLN = 32 / P;  // lanes per group
   float mn = vx[0], mx = vx[0];
 #pragma unroll
@@ -672,16 +753,16 @@ __global__ __launch_bounds__(kRowWaves * 64) void quantize_rows_kernel(QArgs a) 
   }
 }
 
-template <int D, int KB, int VB, bool BF16, bool QJ>
+template <int D, int KB, int VB, bool BF16, bool QJ, bool ROTV>
 static hipError_t launch_rows(const QArgs& a, hipStream_t stream) {
   const int64_t grid = (a.num_th + kRowWaves - 1) / kRowWaves;
-  hipLaunchKernelGGL((quantize_rows_kernel<D, KB, VB, BF16, QJ>), dim3((unsigned)grid), dim3(kRowWaves * 64), 0, stream, a);
+  hipLaunchKernelGGL((quantize_rows_kernel<D, KB, VB, BF16, QJ, ROTV>), dim3((unsigned)grid), dim3(kRowWaves * 64), 0, stream, a);
   return hipGetLastError();
 }
 
-template <int D, int KB, int VB, bool BF16, bool QJ>
+template <int D, int KB, int VB, bool BF16, bool QJ, bool ROTV>
 static hipError_t launch_q(const QArgs& a, hipStream_t stream) {
-  auto kern = quantize_kernel<D, KB, VB, BF16, QJ>;
+  auto kern = quantize_kernel<D, KB, VB, BF16, QJ, ROTV>;
   const size_t lds = QLds<D>::total;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);
@@ -696,25 +777,27 @@ static hipError_t launch_q(const QArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int D, int KB, bool BF16, bool QJ>
+template <int D, int KB, bool BF16, bool QJ, bool ROTV>
 static hipError_t dispatch_vb(const QArgs& a, int vb, hipStream_t s) {
   if (a.num_th <= kRowPathMaxTokenHeads)
-    return vb == 2 ? launch_rows<D, KB, 2, BF16, QJ>(a, s) : launch_rows<D, KB, 4, BF16, QJ>(a, s);
-  return vb == 2 ? launch_q<D, KB, 2, BF16, QJ>(a, s) : launch_q<D, KB, 4, BF16, QJ>(a, s);
+    return vb == 2 ? launch_rows<D, KB, 2, BF16, QJ, ROTV>(a, s) : launch_rows<D, KB, 4, BF16, QJ, ROTV>(a, s);
+  return vb == 2 ? launch_q<D, KB, 2, BF16, QJ, ROTV>(a, s) : launch_q<D, KB, 4, BF16, QJ, ROTV>(a, s);
 }
 
-template <int D, bool BF16, bool QJ>
+template <int D, bool BF16, bool QJ, bool ROTV>
 static hipError_t dispatch_kb(const QArgs& a, int kb, int vb, hipStream_t s) {
   switch (kb) {
-    case 2: return dispatch_vb<D, 2, BF16, QJ>(a, vb, s);
-    case 3: return dispatch_vb<D, 3, BF16, QJ>(a, vb, s);
-    default: return dispatch_vb<D, 4, BF16, QJ>(a, vb, s);
+    case 2: return dispatch_vb<D, 2, BF16, QJ, ROTV>(a, vb, s);
+    case 3: return dispatch_vb<D, 3, BF16, QJ, ROTV>(a, vb, s);
+    default: return dispatch_vb<D, 4, BF16, QJ, ROTV>(a, vb, s);
   }
 }
 
 template <int D, bool BF16>
-static hipError_t dispatch_kind(const QArgs& a, bool qjl, int kb, int vb, hipStream_t s) {
-  return qjl ? dispatch_kb<D, BF16, true>(a, kb, vb, s) : dispatch_kb<D, BF16, false>(a, kb, vb, s);
+static hipError_t dispatch_kind(const QArgs& a, bool qjl, bool rotv, int kb, int vb, hipStream_t s) {
+  if (rotv)
+    return qjl ? dispatch_kb<D, BF16, true, true>(a, kb, vb, s) : dispatch_kb<D, BF16, false, true>(a, kb, vb, s);
+  return qjl ? dispatch_kb<D, BF16, true, false>(a, kb, vb, s) : dispatch_kb<D, BF16, false, false>(a, kb, vb, s);
 }
 
 hipError_t launch_quantize(const tq_ctx* c, const void* k, const void* v, int in_dtype, int64_t num_tokens,
@@ -734,8 +817,10 @@ hipError_t launch_quantize(const tq_ctx* c, const void* k, const void* v, int in
   a.num_tiles = (a.num_th + 15) / 16;
   const bool bf = in_dtype == TQ_DTYPE_BF16;
   if (c->d == 128)
-    return bf ? dispatch_kind<128, true>(a, c->qjl, c->kb, c->vb, stream) : dispatch_kind<128, false>(a, c->qjl, c->kb, c->vb, stream);
-  return bf ? dispatch_kind<256, true>(a, c->qjl, c->kb, c->vb, stream) : dispatch_kind<256, false>(a, c->qjl, c->kb, c->vb, stream);
+    return bf ? dispatch_kind<128, true>(a, c->qjl, c->rotv, c->kb, c->vb, stream)
+              : dispatch_kind<128, false>(a, c->qjl, c->rotv, c->kb, c->vb, stream);
+  return bf ? dispatch_kind<256, true>(a, c->qjl, c->rotv, c->kb, c->vb, stream)
+            : dispatch_kind<256, false>(a, c->qjl, c->rotv, c->kb, c->vb, stream);
 }
 
 }  // namespace tq

@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 import kv_cache_vector_03_amd as tq
-from oracle import codebook, paged
+from oracle import attention, codebook, paged
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "tq_api.h")
@@ -53,6 +53,27 @@ def test_uniform_codebook_agrees_with_oracle(d, b):
     assert np.array_equal(t.astype(np.float32), t2.astype(np.float32))
 
 
+@pytest.mark.parametrize("d", [128, 256])
+def test_fold_output_projection_agrees_with_oracle(d):
+    rng = np.random.default_rng(131)
+    signs = np.stack([rng.choice([-1, 1], d), rng.choice([-1, 1], d)]).astype(np.int8)
+    H, rows = 3, 40
+    W = rng.standard_normal((rows, H * d)).astype(np.float32)
+    got = tq.tq_fold_output_projection(signs, W, H)
+    ref = attention.fold_output_projection(W, signs[0].astype(np.float64), signs[1].astype(np.float64), H)
+    assert got.dtype == np.float32
+    assert np.max(np.abs(got - ref)) <= 1e-6 * np.max(np.abs(ref))
+    # in place gives the same
+    lib = tq.load()
+    W2 = W.copy()
+    assert lib.tq_fold_output_projection(d, signs.ctypes.data, W2.ctypes.data, rows, H, W2.ctypes.data) == tq.TQ_OK
+    assert np.array_equal(W2, got)
+    bad = signs.copy()
+    bad[1, 3] = 0
+    assert lib.tq_fold_output_projection(d, bad.ctypes.data, W.ctypes.data, rows, H, W2.ctypes.data) == tq.TQ_EINVAL
+    assert lib.tq_fold_output_projection(96, signs.ctypes.data, W.ctypes.data, rows, H, W2.ctypes.data) == tq.TQ_EINVAL
+
+
 @pytest.mark.parametrize("mse_only", [False, True])
 @pytest.mark.parametrize("d,bk,bv", [(128, 3, 4), (128, 3, 2), (128, 4, 4), (128, 2, 2), (256, 4, 4), (256, 3, 2)])
 def test_record_layout_matches_oracle(d, bk, bv, mse_only):
@@ -87,7 +108,7 @@ def test_unsupported_presets_are_rejected():
         assert "unsupported preset" in tq.tq_last_error()
     p = tq.tq_preset(128, 3, 4, 16, 16, 0, 0)
     assert lib.tq_record_layout(ctypes.byref(p), ctypes.byref(lay)) == tq.TQ_EUNSUPPORTED
-    for flags in (4, 5, -1):  # TQ_PRESET_MSE_ONLY and TQ_PRESET_UNIFORM are the known flags
+    for flags in (8, 9, -1):  # TQ_PRESET_MSE_ONLY, _UNIFORM and _ROTATE_V are the known flags
         p = tq.tq_preset(128, 3, 4, 32, 16, flags, 0)
         assert lib.tq_record_layout(ctypes.byref(p), ctypes.byref(lay)) == tq.TQ_EUNSUPPORTED
     p = tq.tq_preset(128, 3, 4, 32, 16, tq.TQ_PRESET_MSE_ONLY, 0)
