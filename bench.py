@@ -279,7 +279,7 @@ def main():
         "quantize": qres,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_TBS * 1000, "unit": "GB/s",
                      "frac": round(achieved / (HBM_PEAK_TBS * 1000), 4), "traffic": traffic,
-                     "kernel": "decode_split_kernel<128,4,3,4>", "bytes_per_launch": 32 * 8 * 8192 * REC_BYTES_K3V4,
+                     "kernel": "decode_split_kernel<128,4,3,4,true>", "bytes_per_launch": 32 * 8 * 8192 * REC_BYTES_K3V4,
                      "avg_launch_ms": round(split_avg, 5)},
         "mse_only": mse,
         "cpu_baseline": cpu,
