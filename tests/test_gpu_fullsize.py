@@ -60,14 +60,14 @@ def _fill(ctx, pool, bt, lens, Hkv, d, seed, p, factor, sample):
     return kept
 
 
-def _oracle_records(pool, bt_np, b, h, K, V, prm, d, kb, vb):
+def _oracle_records(pool, bt_np, b, h, K, V, prm, d, kb, vb, qjl=True):
     """Overwrite the records of (b, h) in the device pool with the oracle's
     encoding of K, V; return the oracle fields for the decode reference."""
     L = K.shape[0]
-    lay = paged.layout(d, kb, vb)
+    lay = paged.layout(d, kb, vb, qjl=qjl)
     nblk = (L + 15) // 16
     tmp = paged.new_pool(nblk, pool.shape[1], lay)
-    ke = keys.encode_keys(K.astype(np.float64), prm["d1"], prm["d2"], prm["S"], prm["c32"], prm["t32"])
+    ke = keys.encode_keys(K.astype(np.float64), prm["d1"], prm["d2"], prm["S"], prm["c32"], prm["t32"], qjl=qjl)
     ve = values.encode_values(V, vb)
     t = np.arange(L)
     paged.write_tokens(tmp, (t // 16) * 16 + t % 16, h, ke, ve, lay)
@@ -109,23 +109,28 @@ def _check_pair(label, out, scores, q, b, h, G, fields, prm, L, rk=None, rv=None
     assert oe <= TOL, msg
 
 
-def test_decode_workload_full_size_sampled():
+@pytest.mark.parametrize("mse_only", [False, True])
+def test_decode_workload_full_size_sampled(mse_only):
+    """The benchmark's decode workload, with QJL keys and with MSE-only keys
+    (the benchmark's mse_only section)."""
     d, B, Hq, Hkv, L, kb, vb, nb, seed = 128, 32, 32, 8, 8192, 3, 4, 16384, 3
     G = Hq // Hkv
     prm = oracle_params(seed, d, kb)
-    ctx = tq.tq_codebook_init(d, kb, vb, signs=prm["signs"], S=prm["S"])
+    prm["qjl"] = not mse_only
+    ctx = tq.tq_codebook_init(d, kb, vb, signs=prm["signs"], S=prm["S"], mse_only=mse_only)
     bt_np = synth.block_table(seed, B, L // 16, nb)
     bt = torch.from_numpy(bt_np).cuda()
     pool = torch.zeros((nb, Hkv, ctx.block_bytes), dtype=torch.uint8, device="cuda")
     lens = np.full(B, L)
     sample = [(5, 3), (31, 0)]
     kept = _fill(ctx, pool, bt, lens, Hkv, d, seed, 0.0, 20.0, sample)
-    fields = {s: _oracle_records(pool, bt_np, s[0], s[1], *kept[s], prm, d, kb, vb) for s in sample}
+    fields = {s: _oracle_records(pool, bt_np, s[0], s[1], *kept[s], prm, d, kb, vb, qjl=not mse_only) for s in sample}
     q = synth.bf16_round(synth.queries(seed, B, Hq, d))
     qd = torch.from_numpy(q).to(torch.bfloat16).cuda()
     out, scores = _decode(qd, [ctx], [pool], bt, torch.from_numpy(lens.astype(np.int32)).cuda(), L)
     for (b, h) in sample:
-        _check_pair("decode b32 ctx8192 k3v4", out, scores, q, b, h, G, fields[(b, h)], prm, L)
+        _check_pair(f"decode b32 ctx8192 k3v4{' mse-only' if mse_only else ''}", out, scores, q, b, h, G,
+                    fields[(b, h)], prm, L)
     ctx.close()
 
 
