@@ -330,6 +330,10 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h, int t0, int t1
   }
 
   auto compute = [&](const unsigned char* sb, int st) {
+    // Issue priority: high through the score phase (LDS lookups feeding the
+    // score MFMAs), normal for the value phase, so that the two waves of a
+    // SIMD tend to be in different phases (measured ~1.5 % faster).
+    __builtin_amdgcn_s_setprio(2);
     const int base = t0 + 32 * st;
     // block ids were validated at staging: -1 marks a block outside the pool
     const bool ok0 = __builtin_amdgcn_readfirstlane(s_blk[2 * st]) >= 0;
@@ -500,6 +504,7 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h, int t0, int t1
       }
     }
     wait_lgkm0();  // the weights are in LDS
+    __builtin_amdgcn_s_setprio(0);
     // ------------------------------------------------------------ values
     // fp16 MFMA: A = p s as fp16 hi + lo, B = 1024 + sigma q exactly (code bits
     // or-ed into mantissa bits 4..7 of 1024, so sigma = 16, or 64 for the upper
