@@ -720,28 +720,58 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h, int t0, int t1
 }
 
 // Recent full-precision window: exact scores <q, k> with the unrotated query
-// and bf16 keys, bf16 values.  One token per lane for the scores, one channel
-// per lane for the values (the window is small next to the cache).
+// and bf16 keys, bf16 values.  One head at a time (few registers, so the
+// streaming path's allocation is unaffected); wave w takes tokens w, w + NW,
+// ...: its 64 lanes read a token's key row (and later its value row), d/64
+// channels each, so every row is one coalesced read, and the dot products
+// are wave reductions.  The softmax runs per head over the window; the
+// waves' partial value sums are added in LDS in wave order (deterministic).
 template <int D, int GP>
 __device__ void split_recent(const DArgs& a, int b, int h, int R, float* s_p, float* s_merge, float* m_out,
                              float* l_out) {
   constexpr int NW = split_waves<D, GP>();
-  const int tid = threadIdx.x;
+  constexpr int P = D / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint16_t* kb = a.rk + (((int64_t)b * a.Hkv + h) * a.W) * D;
   const uint16_t* vb = a.rv + (((int64_t)b * a.Hkv + h) * a.W) * D;
-  // s_p reused as [GP][W] logits (W <= 4096 fits in the merge area instead when large)
-  float* lg = s_merge;  // [GP][R] logits, then weights; R <= W
-  for (int idx = tid; idx < a.G * R; idx += NW * 64) {
-    const int g = idx / R, t = idx % R;
-    const int64_t qoff = ((int64_t)b * a.Hq + h * a.G + g) * D;
-    float acc = 0.f;
-    for (int j = 0; j < D; ++j) {
-      float qv = a.q_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(a.q)[qoff + j])
-                          : reinterpret_cast<const float*>(a.q)[qoff + j];
-      acc = __builtin_fmaf(qv, bf16_to_f32(kb[(int64_t)t * D + j]), acc);
+  float* lg = s_merge;                  // [GP][R] logits, then weights; R <= W
+  float* part = s_merge + GP * a.W;     // [GP][D] value sums, added wave by wave
+  const int64_t q0 = ((int64_t)b * a.Hq + (int64_t)h * a.G) * D;
+  auto load_row = [&](const uint16_t* row, float (&x)[P]) {
+    if constexpr (P == 2) {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(row + 2 * lane);
+      x[0] = __uint_as_float(w << 16);
+      x[1] = __uint_as_float(w & 0xFFFF0000u);
+    } else {
+      const uint2 w = *reinterpret_cast<const uint2*>(row + 4 * lane);
+      x[0] = __uint_as_float(w.x << 16);
+      x[1] = __uint_as_float(w.x & 0xFFFF0000u);
+      x[2] = __uint_as_float(w.y << 16);
+      x[3] = __uint_as_float(w.y & 0xFFFF0000u);
     }
-    if (a.scores) a.scores[((int64_t)b * a.Hq + h * a.G + g) * a.scores_stride + seq_cached(a, b) + t] = acc;
-    lg[g * R + t] = acc * a.logit_scale;
+  };
+  const int Lc = seq_cached(a, b);
+#pragma unroll 1
+  for (int g = 0; g < a.G; ++g) {
+    float qv[P];
+#pragma unroll
+    for (int e = 0; e < P; ++e) {
+      const int64_t i = q0 + (int64_t)g * D + P * lane + e;
+      qv[e] = a.q_bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(a.q)[i]) : reinterpret_cast<const float*>(a.q)[i];
+    }
+#pragma unroll 1
+    for (int t = wave; t < R; t += NW) {
+      float kx[P];
+      load_row(kb + (int64_t)t * D, kx);
+      float sdot = 0.f;
+#pragma unroll
+      for (int e = 0; e < P; ++e) sdot = __builtin_fmaf(qv[e], kx[e], sdot);
+      sdot = wave_sum_xl(sdot);
+      if (lane == 0) {
+        lg[g * R + t] = sdot * a.logit_scale;
+        if (a.scores) a.scores[((int64_t)b * a.Hq + h * a.G + g) * a.scores_stride + Lc + t] = sdot;
+      }
+    }
   }
   __syncthreads();
   if (tid < a.G) {
@@ -749,7 +779,7 @@ __device__ void split_recent(const DArgs& a, int b, int h, int R, float* s_p, fl
     for (int t = 0; t < R; ++t) M = fmaxf(M, lg[tid * R + t]);
     float L = 0.f;
     for (int t = 0; t < R; ++t) {
-      float p = __builtin_amdgcn_exp2f(lg[tid * R + t] - M);
+      const float p = __builtin_amdgcn_exp2f(lg[tid * R + t] - M);
       lg[tid * R + t] = p;
       L += p;
     }
@@ -757,16 +787,46 @@ __device__ void split_recent(const DArgs& a, int b, int h, int R, float* s_p, fl
     l_out[tid] = L;
   }
   __syncthreads();
-  // acc[g][c] into s_p scratch area (GP * D floats available after the merge area)
-  float* accs = s_merge + GP * a.W;
-  for (int idx = tid; idx < a.G * D; idx += NW * 64) {
-    const int g = idx / D, c = idx % D;
-    float acc = 0.f;
-    for (int t = 0; t < R; ++t) acc = __builtin_fmaf(lg[g * R + t], bf16_to_f32(vb[(int64_t)t * D + c]), acc);
-    accs[idx] = acc;
+#pragma unroll 1
+  for (int g = 0; g < a.G; ++g) {
+    float acc[P];
+#pragma unroll
+    for (int e = 0; e < P; ++e) acc[e] = 0.f;
+#pragma unroll 1
+    for (int t = wave; t < R; t += NW) {
+      float vx[P];
+      load_row(vb + (int64_t)t * D, vx);
+      const float w = lg[g * R + t];
+#pragma unroll
+      for (int e = 0; e < P; ++e) acc[e] = __builtin_fmaf(w, vx[e], acc[e]);
+    }
+#pragma unroll 1
+    for (int w = 0; w < NW; ++w) {
+      if (wave == w) {
+#pragma unroll
+        for (int e = 0; e < P; ++e) {
+          float* pp = part + g * D + P * lane + e;
+          *pp = (w == 0 ? 0.f : *pp) + acc[e];
+        }
+      }
+      __syncthreads();
+    }
+  }
+  // move the sums to s_merge[g][c] (they may overlap the part area when
+  // the window is shorter than d: read all, then write)
+  constexpr int NR = (GP * D + NW * 64 - 1) / (NW * 64);
+  float res[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const int idx = tid + r * NW * 64;
+    res[r] = idx < a.G * D ? part[idx] : 0.f;
   }
   __syncthreads();
-  for (int idx = tid; idx < a.G * D; idx += NW * 64) s_merge[idx] = accs[idx];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const int idx = tid + r * NW * 64;
+    if (idx < a.G * D) s_merge[idx] = res[r];
+  }
   __syncthreads();
 }
 
