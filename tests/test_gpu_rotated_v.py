@@ -120,3 +120,58 @@ def test_rotated_values_decode_and_folded_projection(chunk):
     print(f"[rotated-V decode + fold chunk {chunk}] max score err {max(errs):.2e} max out err {oerr:.2e} "
           f"folded projection err {yerr:.2e}", flush=True)
     assert max(errs) <= TOL and oerr <= TOL and yerr <= TOL
+
+
+def test_all_preset_flags_together_quantize_and_decode():
+    """Uniform codebook + MSE-only keys + rotated values in one preset: GPU
+    records bit-exact against the oracle outside the band, then decode over
+    the GPU-written cache against the oracle's attention on the same
+    records."""
+    seed, d, kb, vb, T, Hkv, Hq = 170, 128, 4, 4, 800, 2, 8
+    prm = oracle_params(seed, d, kb, uniform=True)
+    prm["qjl"] = False
+    rng = np.random.default_rng(171)
+    K = synth.normal_with_outliers(rng, (T, Hkv, d), 0.005, 20.0)
+    V = synth.normal_with_outliers(rng, (T, Hkv, d), 0.005, 20.0)
+    nb = T // 16 + 3
+    bt = synth.block_table(seed, 1, (T + 15) // 16, nb)
+    t = np.arange(T)
+    slots = bt[0][t // 16].astype(np.int64) * 16 + t % 16
+    ctx = tq.tq_codebook_init(d, kb, vb, signs=prm["signs"], S=prm["S"], mse_only=True, uniform=True, rotate_v=True)
+    k = torch.from_numpy(K).to(torch.bfloat16).cuda()
+    v = torch.from_numpy(V).to(torch.bfloat16).cuda()
+    pool = torch.zeros((nb, Hkv, ctx.block_bytes), dtype=torch.uint8, device="cuda")
+    tq.tq_quantize_store(ctx, k, v, torch.from_numpy(slots.astype(np.int32)).cuda(), pool)
+    torch.cuda.synchronize()
+    gpu = pool.cpu().numpy()
+    Kx = k.float().cpu().numpy().astype(np.float64)
+    Vx = v.float().cpu().numpy()
+    lay = paged.layout(d, kb, vb, qjl=False)
+    exp = paged.new_pool(nb, Hkv, lay)
+    mask = paged.new_pool(nb, Hkv, lay)
+    for h in range(Hkv):
+        expected_records(Kx[:, h], values.rotate_values(Vx[:, h], prm["d1"], prm["d2"]), slots, h, prm, d, kb, vb,
+                         exp, mask, qjl=False)
+    outside, inside = compare_pools(gpu, exp, mask)
+    print(f"[all flags quantize parity] differing bits outside band={outside} inside band={inside}", flush=True)
+    assert outside == 0
+    # decode over the oracle's records (identical to the GPU's outside the band)
+    fields = [paged.read_tokens(exp, bt[0], T, h, lay) for h in range(Hkv)]
+    q = synth.queries(seed, 1, Hq, d)
+    qd = torch.from_numpy(q).cuda()
+    btd = torch.from_numpy(bt.astype(np.int32)).cuda()
+    lens = torch.tensor([T], dtype=torch.int32, device="cuda")
+    msl = bt.shape[1] * 16
+    out = torch.full((1, Hq, d), float("nan"), dtype=torch.float32, device="cuda")
+    sc = torch.full((1, Hq, msl), float("nan"), dtype=torch.float32, device="cuda")
+    pd = torch.from_numpy(exp).cuda()
+    nbytes = tq.tq_decode_workspace_bytes(qd, [ctx], [pd], btd, lens, out, chunk_tokens=256, max_seq_len=msl)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+    tq.tq_decode_attention(qd, [ctx], [pd], btd, lens, out, ws, chunk_tokens=256, max_seq_len=msl, scores_out=sc)
+    torch.cuda.synchronize()
+    ctx.close()
+    ref_o, ref_s = attention.decode_one_sequence(q[0].astype(np.float64), fields, prm)
+    se = score_errors(sc[0, :, :T].cpu().numpy().astype(np.float64), ref_s)
+    oe = output_errors(out[0].cpu().numpy().astype(np.float64), ref_o)
+    print(f"[all flags decode parity] max score err {se:.2e} max out err {oe:.2e}", flush=True)
+    assert se <= TOL and oe <= TOL
