@@ -97,6 +97,33 @@ def test_small_batch_store(d, kb, vb, T, Hkv, dtype):
     _check(K, V, d, kb, vb, slots, nb, dtype, seed=kb * 10 + vb, label=f"small d{d} k{kb}v{vb} T={T}x{Hkv}")
 
 
+@pytest.mark.parametrize("T,Hkv", [(1024, 2), (683, 3), (1025, 2)])
+def test_row_and_tile_dispatch_boundary(T, Hkv):
+    """2048 token-heads take the one-wave-per-row kernel, 2049 and 2050 the
+    tiled one, whose last 16-row tile then holds one or two rows."""
+    d = 128
+    rng = np.random.default_rng([13, T, Hkv])
+    K = synth.normal_with_outliers(rng, (T, Hkv, d), 0.005, 20.0)
+    V = synth.normal_with_outliers(rng, (T, Hkv, d), 0.005, 20.0)
+    nb = (T + 15) // 16 + 3
+    slots = rng.permutation(nb * 16)[:T].astype(np.int64)
+    slots[T - 1] = -1  # the ragged tail's last row is a skipped token
+    _check(K, V, d, 3, 4, slots, nb, torch.bfloat16, seed=5, label=f"dispatch T={T}x{Hkv}")
+
+
+def test_empty_store_leaves_the_pool_untouched():
+    d, Hkv, nb = 128, 4, 3
+    prm = oracle_params(0, d, 3)
+    ctx = tq.tq_codebook_init(d, 3, 4, signs=prm["signs"], S=prm["S"])
+    pool = torch.full((nb, Hkv, ctx.block_bytes), 0xAB, dtype=torch.uint8, device="cuda")
+    k = torch.empty((0, Hkv, d), dtype=torch.bfloat16, device="cuda")
+    sm = torch.empty((0,), dtype=torch.int32, device="cuda")
+    tq.tq_quantize_store(ctx, k, k, sm, pool)
+    torch.cuda.synchronize()
+    assert bool((pool == 0xAB).all())
+    ctx.close()
+
+
 def test_edge_rows_zero_keys_constant_groups_skipped_slots():
     T, Hkv, d = 64, 2, 128
     rng = np.random.default_rng(9)
