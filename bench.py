@@ -41,8 +41,8 @@ REC_BYTES_K3V4 = 148  # per token-head: 48 code + 16 sign + 4 meta + 64 value + 
 
 def _kernel_source_sha():
     h = hashlib.sha256()
-    for name in ("tq_decode.hip", "tq_common.hip.h"):
-        with open(os.path.join(ROOT, "kv_cache_vector_03_amd", "csrc", name), "rb") as f:
+    for name in ("csrc/tq_decode.hip", "csrc/tq_common.hip.h", "build.py"):
+        with open(os.path.join(ROOT, "kv_cache_vector_03_amd", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
