@@ -49,7 +49,7 @@ def _kernel_source_sha():
 
 def _traffic_record(per_launch_units):
     """HBM bytes per split launch from the committed PMC summary, if it was
-    taken on the current kernel source; else None."""
+    taken on the current decode source and build flags; else None."""
     path = os.path.join(ROOT, "profiles", "decode_split_b32_ctx8192_k3v4_traffic.json")
     if not os.path.exists(path):
         return None
