@@ -6,20 +6,24 @@ A step is one decode step of the whole path on the decode workload (batch 32,
 3-bit Lloyd-Max keys + 1-bit QJL, 4-bit group-32 values, paged through a
 permuted block table): tq_quantize_store of the step's new token for every
 sequence and KV head, then tq_decode_attention over the 8192 cached tokens.
+The step is captured once per cache copy in a HIP graph and replayed.
 
 Printed as ONE JSON line:
   value     = KV bytes the decode must read per step (every packed record byte
-              of every cached token-head, 148 B each) / step time, in TB/s;
-  roofline  = the split kernel (the streaming kernel) timed live with HIP
-              events around its launch, against the 8 TB/s HBM peak;
-  quantize  = tq_quantize_store throughput on the quantise workload (65536
-              new bf16 tokens x 8 KV heads, 0.5% x20 outliers, K3V4 and K3V2);
-  mse_only  = the same decode step with MSE-only keys (no QJL sketch, 130 B
-              per token-head): step and split-kernel times, TB/s of its KV bytes;
-  cpu_baseline = the fp64 CPU oracle on a bounded sample of the decode
-              workload, on this host's cores.
-The cache pool is rotated over several copies so that the 256 MB last-level
-cache cannot serve repeated reads of one pool.
+              of every cached token-head, 148 B each) / mean step time over
+              the K timed steps, in TB/s;
+  roofline  = the split kernel (the streaming kernel): median time of one
+              launch from graphs of back-to-back split-only launches, against
+              the 8 TB/s HBM peak;
+  workloads = the other workloads timed the same way (median of replays):
+              the long-context d=256 decode, the ragged mixed-preset decode
+              with a bf16 window, the quantise workload (65536 new bf16
+              tokens x 8 KV heads, K3V4 and K3V2), MSE-only keys, and the
+              deterministic decode schedule;
+  cpu_baseline = the fp64 CPU oracle on bounded samples of the decode and
+              quantise workloads, on this host's cores.
+Caches smaller than a few times the 256 MB last-level cache are rotated over
+several copies so that repeated launches cannot be served from it.
 """
 
 from __future__ import annotations
@@ -37,6 +41,7 @@ sys.path.insert(0, ROOT)
 METRIC = "TQ decode attn: KV-bytes TB/s (% HBM peak) + tokens/s; quantize Mtok/s"
 HBM_PEAK_TBS = 8.0
 REC_BYTES_K3V4 = 148  # per token-head: 48 code + 16 sign + 4 meta + 64 value + 16 value-meta bytes
+SPLIT_LAUNCHES_PER_GRAPH = 6
 
 
 def _kernel_source_sha():
@@ -60,6 +65,61 @@ def _traffic_record(per_launch_units):
     return rec.get("hbm_bytes_per_launch")
 
 
+def _median(xs):
+    xs = sorted(xs)
+    n = len(xs)
+    return xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------- graphs --
+def capture(torch, fn):
+    """Run ``fn`` once on a side stream (torch's warm-up recipe), then capture
+    it into a HIP graph on torch's capture stream."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_total(torch, graphs, reps):
+    """Mean ms per replay over ``reps`` back-to-back replays (graphs taken
+    round-robin), bracketed by synchronisations and two events."""
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        graphs[i % len(graphs)].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def time_each(torch, graphs, reps):
+    """ms of every replay, each bracketed by its own event pair on the stream
+    the graph is launched on (the host runs ahead of the GPU, so the events do
+    not wait for the host)."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for i in range(reps):
+        evs[i][0].record()
+        graphs[i % len(graphs)].replay()
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+# --------------------------------------------------------- decode workload --
 def setup_decode(torch, tq, synth, chunk, copies, mse_only=False):
     d, B, Hq, Hkv, L, kb, vb, nb, seed = 128, 32, 32, 8, 8192, 3, 4, 16384, 3
     signs1, signs2, S = synth.method_params(seed, d)
@@ -90,47 +150,178 @@ def setup_decode(torch, tq, synth, chunk, copies, mse_only=False):
                 units=B * Hkv * L)
 
 
-def decode_step(tq, s, i, events=None):
+def decode_only(tq, s, i, deterministic=False):
+    pool = s["pools"][i % len(s["pools"])]
+    tq.tq_decode_attention(s["q"], [s["ctx"]], [pool], s["bt"], s["lens"], s["out"], s["ws"],
+                           chunk_tokens=s["chunk"], max_seq_len=s["L"], deterministic=deterministic)
+
+
+def decode_step(tq, s, i):
     pool = s["pools"][i % len(s["pools"])]
     tq.tq_quantize_store(s["ctx"], s["knew"], s["vnew"], s["slot_new"], pool)
-    tq.tq_decode_attention(s["q"], [s["ctx"]], [pool], s["bt"], s["lens"], s["out"], s["ws"],
-                           chunk_tokens=s["chunk"], max_seq_len=s["L"], split_events=events)
+    decode_only(tq, s, i)
+
+
+def split_graphs(torch, tq, s, deterministic=False):
+    """One graph per pool copy, each with SPLIT_LAUNCHES_PER_GRAPH back-to-back
+    decode launches over the copies in turn (no store between them)."""
+    n = len(s["pools"])
+
+    def make(j):
+        def fn():
+            for k in range(SPLIT_LAUNCHES_PER_GRAPH):
+                decode_only(tq, s, j + k, deterministic)
+        return fn
+
+    return [capture(torch, make(j)) for j in range(n)]
 
 
 def time_decode(torch, tq, s, steps, warmup):
-    """Average step time (store + decode) over `steps` steps, then the split
-    kernel's average launch duration from HIP events on its stream."""
+    """Step timing (graph replays of store + decode; mean over exactly
+    ``steps`` steps, and the median of per-step events in a second pass), the
+    eager step for comparison, and the split kernel's median launch time."""
     for i in range(warmup):
         decode_step(tq, s, i)
     torch.cuda.synchronize()
-    # timed region: K steps of the whole path (store + decode), nothing else
-    # on the stream.
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
+    n = len(s["pools"])
+    step_graphs = [capture(torch, (lambda j: (lambda: decode_step(tq, s, j)))(j)) for j in range(n)]
+    for g in step_graphs * 2:
+        g.replay()
+    # the timed region: exactly `steps` steps between two synchronisations
+    ms_step = time_total(torch, step_graphs, steps)
+    med_step = _median(time_each(torch, step_graphs, steps))
+    # eager launches of the same step (host-paced launch gaps included)
     torch.cuda.synchronize()
-    start.record()
+    t0 = time.perf_counter()
     for i in range(steps):
         decode_step(tq, s, i)
-    stop.record()
     torch.cuda.synchronize()
-    ms_step = start.elapsed_time(stop) / steps
-    # the same K steps again with the split (streaming) kernel bracketed by
-    # HIP events on its own stream each step, for its average launch duration
-    # (kept out of the step timing: an event record between launches adds a
-    # few microseconds of idle time to the step).
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for a, b in evs:  # create the underlying HIP events
-        a.record()
-        b.record()
-    torch.cuda.synchronize()
-    for i in range(steps):
-        decode_step(tq, s, i, events=(evs[i][0].cuda_event, evs[i][1].cuda_event))
-    torch.cuda.synchronize()
-    split_ms = sorted(a.elapsed_time(b) for a, b in evs)
-    return ms_step, sum(split_ms) / len(split_ms), split_ms
+    eager_ms = (time.perf_counter() - t0) * 1e3 / steps
+    sg = split_graphs(torch, tq, s)
+    for g in sg:
+        g.replay()
+    reps = max(10, steps // 2)
+    per = [t / SPLIT_LAUNCHES_PER_GRAPH for t in time_each(torch, sg, reps)]
+    del step_graphs, sg
+    return {"ms_per_step": ms_step, "median_ms_per_step": med_step, "eager_ms_per_step": eager_ms,
+            "split_median_ms": _median(per), "split_min_ms": min(per), "split_max_ms": max(per)}
 
 
-def bench_quantize(torch, tq, synth, steps, warmup):
+def time_split_deterministic(torch, tq, s, steps):
+    sg = split_graphs(torch, tq, s, deterministic=True)
+    for g in sg:
+        g.replay()
+    per = [t / SPLIT_LAUNCHES_PER_GRAPH for t in time_each(torch, sg, max(10, steps // 2))]
+    # repeated launches give bit-identical outputs on this schedule
+    outs = []
+    for i in range(2):
+        decode_only(tq, s, 0, deterministic=True)
+        torch.cuda.synchronize()
+        outs.append(s["out"].clone())
+    return _median(per), bool(torch.equal(outs[0], outs[1]))
+
+
+# ----------------------------------------------------- long / ragged decode --
+def setup_long(torch, tq, synth):
+    """B=8, Hq=16, Hkv=4, d=256, 131072 cached tokens, K4V4 (one 1.36 GB pool
+    copy: five times the last-level cache)."""
+    import numpy as np
+    d, B, Hq, Hkv, L, kb, vb, nb, seed = 256, 8, 16, 4, 131072, 4, 4, 65536, 4
+    s1, s2, S = synth.method_params(seed, d)
+    ctx = tq.tq_codebook_init(d, kb, vb, signs=np.stack([s1, s2]), S=S)
+    bt = torch.from_numpy(synth.block_table(seed, B, L // 16, nb)).cuda()
+    pool = torch.zeros((nb, Hkv, ctx.block_bytes), dtype=torch.uint8, device="cuda")
+    t = torch.arange(L, device="cuda")
+    for b in range(B):
+        slots = (bt[b][t // 16].long() * 16 + t % 16).to(torch.int32)
+        k = synth.torch_normal_bf16((L, Hkv, d), seed * 1000003 + 2 * b)
+        v = synth.torch_normal_bf16((L, Hkv, d), seed * 1000003 + 2 * b + 1)
+        tq.tq_quantize_store(ctx, k, v, slots, pool)
+        del k, v
+    q = synth.torch_normal_bf16((B, Hq, d), seed * 7 + 3)
+    lens = torch.full((B,), L, dtype=torch.int32, device="cuda")
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+    kw = dict(chunk_tokens=8192, max_seq_len=L)
+    ws = torch.empty(tq.tq_decode_workspace_bytes(q, [ctx], [pool], bt, lens, out, **kw), dtype=torch.uint8,
+                     device="cuda")
+    torch.cuda.synchronize()
+    fn = lambda: tq.tq_decode_attention(q, [ctx], [pool], bt, lens, out, ws, **kw)  # noqa: E731
+    return dict(keep=[ctx, bt, pool, q, lens, out, ws], fn=fn, B=B,
+                kv_bytes=B * Hkv * L * (ctx.block_bytes // 16),
+                workload="decode-b8-hq16-hkv4-d256-ctx131072-k4v4", chunk_tokens=8192)
+
+
+def setup_ragged(torch, tq, synth):
+    """B=64, Hq=32, Hkv=8, d=128, lognormal lengths in [1024, 131072]; the last
+    128 tokens of each sequence as a bf16 window, the rest quantised K3V2
+    (even sequences) or K4V4 (odd); N(0,1) with 0.5% x20 outliers."""
+    import numpy as np
+    d, B, Hq, Hkv, W, seed = 128, 64, 32, 8, 128, 5
+    presets = [(3, 2), (4, 4)]
+    total = synth.ragged_lengths(seed, B)
+    cached = np.maximum(total - W, 0)
+    rlens = np.minimum(total, W)
+    seq_preset = (np.arange(B) % 2).astype(np.int8)
+    ctxs = []
+    for i, (kb, vb) in enumerate(presets):
+        s1, s2, S = synth.method_params(seed + 10 * i, d)
+        ctxs.append(tq.tq_codebook_init(d, kb, vb, signs=np.stack([s1, s2]), S=S))
+    mb = int(np.ceil(cached.max() / 16))
+    bt_np = np.zeros((B, mb), dtype=np.int32)
+    pools = []
+    for pr in range(2):
+        seqs = [b for b in range(B) if seq_preset[b] == pr]
+        need = [int(np.ceil(cached[b] / 16)) for b in seqs]
+        nbp = sum(need) + 1
+        perm = np.random.default_rng([seed, pr, 0xB10C]).permutation(nbp).astype(np.int32)
+        off = 0
+        for b, n in zip(seqs, need):
+            bt_np[b, :n] = perm[off:off + n]
+            off += n
+        pools.append(torch.zeros((nbp, Hkv, ctxs[pr].block_bytes), dtype=torch.uint8, device="cuda"))
+    bt = torch.from_numpy(bt_np).cuda()
+    for b in range(B):
+        L = int(cached[b])
+        t = torch.arange(L, device="cuda")
+        slots = (bt[b][t // 16].long() * 16 + t % 16).to(torch.int32)
+        k = synth.torch_normal_bf16((L, Hkv, d), seed * 1000003 + 2 * b, p=0.005)
+        v = synth.torch_normal_bf16((L, Hkv, d), seed * 1000003 + 2 * b + 1, p=0.005)
+        tq.tq_quantize_store(ctxs[seq_preset[b]], k, v, slots, pools[seq_preset[b]])
+        del k, v
+    rk = synth.torch_normal_bf16((B, Hkv, W, d), seed * 7 + 5, p=0.005)
+    rv = synth.torch_normal_bf16((B, Hkv, W, d), seed * 7 + 6, p=0.005)
+    q = synth.torch_normal_bf16((B, Hq, d), seed * 7 + 3)
+    lens = torch.from_numpy(cached.astype(np.int32)).cuda()
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+    kw = dict(seq_preset=torch.from_numpy(seq_preset).cuda(), recent_k=rk, recent_v=rv,
+              recent_lens=torch.from_numpy(rlens.astype(np.int32)).cuda(), chunk_tokens=8192, max_seq_len=mb * 16)
+    ws = torch.empty(tq.tq_decode_workspace_bytes(q, ctxs, pools, bt, lens, out, **kw), dtype=torch.uint8,
+                     device="cuda")
+    torch.cuda.synchronize()
+    fn = lambda: tq.tq_decode_attention(q, ctxs, pools, bt, lens, out, ws, **kw)  # noqa: E731
+    rec = [ctxs[p].block_bytes // 16 for p in range(2)]
+    kv = int(sum(Hkv * (int(cached[b]) * rec[seq_preset[b]] + int(rlens[b]) * 2 * d * 2) for b in range(B)))
+    return dict(keep=[ctxs, bt, pools, rk, rv, q, lens, out, ws, kw], fn=fn, B=B, kv_bytes=kv,
+                workload="decode-ragged-b64-hq32-hkv8-d128-k3v2|k4v4-recent128", chunk_tokens=8192,
+                mean_len=float(total.mean()))
+
+
+def time_workload(torch, w, reps):
+    g = capture(torch, w["fn"])
+    g.replay()
+    ms = _median(time_each(torch, [g], reps))
+    del g
+    tbs = w["kv_bytes"] / (ms * 1e-3) / 1e12
+    res = {"workload": w["workload"], "kv_bytes_per_call": w["kv_bytes"], "median_ms": round(ms, 5),
+           "tbs": round(tbs, 4), "hbm_frac": round(tbs / HBM_PEAK_TBS, 4),
+           "decode_tokens_per_s": round(w["B"] / (ms * 1e-3), 1), "chunk_tokens": w["chunk_tokens"]}
+    if "mean_len" in w:
+        res["mean_tokens_per_seq"] = round(w["mean_len"], 1)
+    return res
+
+
+# ------------------------------------------------------- quantise workload --
+def bench_quantize(torch, tq, synth, reps):
     import numpy as np
     d, T, Hkv, nb, seed = 128, 65536, 8, 4096, 2
     signs1, signs2, S = synth.method_params(seed, d)
@@ -144,28 +335,23 @@ def bench_quantize(torch, tq, synth, steps, warmup):
     for kb, vb in ((3, 4), (3, 2)):
         ctx = tq.tq_codebook_init(d, kb, vb, signs=np.stack([signs1, signs2]), S=S)
         pool = torch.zeros((nb, Hkv, ctx.block_bytes), dtype=torch.uint8, device="cuda")
-        for i in range(warmup):
-            tq.tq_quantize_store(ctx, ks[i % copies], vs[i % copies], slots, pool)
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for i in range(steps):
-            tq.tq_quantize_store(ctx, ks[i % copies], vs[i % copies], slots, pool)
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / steps
+        gs = [capture(torch, (lambda c: (lambda: tq.tq_quantize_store(ctx, ks[c], vs[c], slots, pool)))(c))
+              for c in range(copies)]
+        ms = _median(time_each(torch, gs, reps))
         hbm = T * Hkv * (2 * d * 2 + ctx.block_bytes // 16) + T * 4
-        res[f"k{kb}v{vb}"] = {"ms": round(ms, 4), "mtok_per_s": round(T / ms / 1e3, 2),
+        res[f"k{kb}v{vb}"] = {"median_ms": round(ms, 5), "mtok_per_s": round(T / ms / 1e3, 2),
                               "hbm_bytes": hbm, "hbm_tbs": round(hbm / ms / 1e9, 3),
                               "hbm_frac": round(hbm / ms / 1e9 / HBM_PEAK_TBS, 4)}
+        del gs
         ctx.close()
     return {"workload": "quantize-65536tok-hkv8-d128-bf16-outliers0.5%x20", **res}
 
 
-def cpu_baseline(synth, seqs=24):
-    """The oracle on a bounded sample of the decode workload: cache encoded
-    by the oracle (not timed), then its decode of `seqs` sequences timed."""
+# --------------------------------------------------------------- oracle --
+def cpu_baseline(synth, seqs=24, quant_tokens=2048):
+    """The oracle on bounded samples: its decode of ``seqs`` sequences of the
+    decode workload (cache encoded by the oracle first, not timed), and its
+    encoding of ``quant_tokens`` tokens x 8 KV heads of the quantise workload."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -193,11 +379,29 @@ def cpu_baseline(synth, seqs=24):
             fields = [paged.read_tokens(pool, bt[b], L, h, lay) for h in range(Hkv)]
             attention.decode_one_sequence(q[b].astype(np.float64), fields, prm)
         dt = time.perf_counter() - t0
+        # quantise: encode + pack + scatter of quant_tokens x 8 heads (K3V4)
+        qs1, qs2, qS = synth.method_params(2, d)
+        rng = np.random.default_rng([2, 0xC0])
+        Kq = synth.normal_with_outliers(rng, (quant_tokens, Hkv, d))
+        Vq = synth.normal_with_outliers(rng, (quant_tokens, Hkv, d))
+        qpool = paged.new_pool(quant_tokens // 16, Hkv, lay)
+        t1 = time.perf_counter()
+        for h in range(Hkv):
+            ke = keys.encode_keys(Kq[:, h].astype(np.float64), qs1.astype(np.float64), qs2.astype(np.float64), qS,
+                                  c32, t32)
+            ve = values.encode_values(Vq[:, h], vb)
+            paged.write_tokens(qpool, np.arange(quant_tokens), h, ke, ve, lay)
+        dq = time.perf_counter() - t1
     kv = seqs * Hkv * L * REC_BYTES_K3V4
     return {"value": kv / dt / 1e12, "unit": "TB/s", "cores": cores, "kind": "oracle",
             "sample": f"{seqs} of the 32 sequences of the decode workload (all 8 KV heads x 8192 tokens, "
                       f"32 query heads), oracle decode from an oracle-written pool: {dt:.2f} s, "
-                      f"{seqs / dt:.3f} sequences/s; BLAS threads = cores, numpy elementwise work single-threaded"}
+                      f"{seqs / dt:.3f} sequences/s; BLAS threads = cores, numpy elementwise work single-threaded",
+            "decode_tokens_per_s": seqs / dt,
+            "quantize": {"mtok_per_s": quant_tokens / dq / 1e6, "seconds": dq,
+                         "sample": f"{quant_tokens} tokens x 8 KV heads of the quantise workload's shape "
+                                   f"(K3 + QJL, V4, bf16 N(0,1) with 0.5% x20 outliers), oracle encode + pack "
+                                   f"+ paged write"}}
 
 
 def main():
@@ -206,6 +410,9 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--chunk", type=int, default=8192, help="tokens per decode split (fixed grid)")
+    ap.add_argument("--skip-cpu", action="store_true", help="leave out the CPU oracle baseline")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="time the decode workload alone (for profiler runs of the split kernel)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="finish with three 256 MiB device-to-device copies (the reference kernel for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes)")
@@ -222,41 +429,55 @@ def main():
 
     tq.load()
     torch.cuda.init()
-    print(f"[bench] device {torch.cuda.get_device_name(0)}; building the decode cache", file=sys.stderr, flush=True)
+    log(f"device {torch.cuda.get_device_name(0)}; building the decode cache")
     s = setup_decode(torch, tq, synth, args.chunk, copies=3)
-    ms_step, split_avg, split_ms = time_decode(torch, tq, s, args.steps, args.warmup)
+    dec = time_decode(torch, tq, s, args.steps, args.warmup)
+    ms_step = dec["ms_per_step"]
     value = s["kv_bytes"] / (ms_step * 1e-3) / 1e12
-    achieved = s["kv_bytes"] / (split_avg * 1e-3) / 1e9
-    print(f"[bench] decode step {ms_step * 1e3:.1f} us, split kernel avg {split_avg * 1e3:.1f} us "
-          f"(median {split_ms[len(split_ms) // 2] * 1e3:.1f})", file=sys.stderr, flush=True)
+    split_ms = dec["split_median_ms"]
+    achieved = s["kv_bytes"] / (split_ms * 1e-3) / 1e9
+    log(f"decode step {ms_step * 1e3:.1f} us (median {dec['median_ms_per_step'] * 1e3:.1f}, eager "
+        f"{dec['eager_ms_per_step'] * 1e3:.1f}), split kernel median {split_ms * 1e3:.1f} us")
+    det_ms, det_equal = time_split_deterministic(torch, tq, s, args.steps)
+    log(f"deterministic split median {det_ms * 1e3:.1f} us, repeat bit-identical: {det_equal}")
     for p in s["pools"]:
         del p
     s.clear()
     torch.cuda.empty_cache()
 
-    # the same workload with MSE-only keys (no QJL sketch: 130 B per token-head)
-    print("[bench] decode workload, MSE-only keys", file=sys.stderr, flush=True)
-    s = setup_decode(torch, tq, synth, args.chunk, copies=3, mse_only=True)
-    m_step, m_split, _ = time_decode(torch, tq, s, args.steps, args.warmup)
-    mse = {"workload": "decode-b32-hq32-hkv8-d128-ctx8192-k3v4-mse-only: store 1 new token + attend 8192",
-           "kv_bytes_per_step": s["kv_bytes"], "ms_per_step": round(m_step, 5),
-           "tbs": round(s["kv_bytes"] / (m_step * 1e-3) / 1e12, 4),
-           "split_avg_ms": round(m_split, 5),
-           "split_hbm_frac": round(s["kv_bytes"] / (m_split * 1e-3) / 1e12 / HBM_PEAK_TBS, 4),
-           "decode_tokens_per_s": round(32 / (m_step * 1e-3), 1)}
-    print(f"[bench] MSE-only decode step {m_step * 1e3:.1f} us, split kernel avg {m_split * 1e3:.1f} us",
-          file=sys.stderr, flush=True)
-    for p in s["pools"]:
-        del p
-    s.clear()
-    torch.cuda.empty_cache()
-
-    print("[bench] quantise workload", file=sys.stderr, flush=True)
-    qres = bench_quantize(torch, tq, synth, steps=max(5, args.steps // 5), warmup=3)
-    print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-    cpu = cpu_baseline(synth)
+    workloads = {"deterministic_split": {"median_ms": round(det_ms, 5), "bit_identical_repeat": det_equal,
+                                         "hbm_frac": round(32 * 8 * 8192 * REC_BYTES_K3V4 / (det_ms * 1e-3) / 1e12
+                                                           / HBM_PEAK_TBS, 4)}}
+    if not args.decode_only:
+        log("decode workload, MSE-only keys")
+        s = setup_decode(torch, tq, synth, args.chunk, copies=3, mse_only=True)
+        m = time_decode(torch, tq, s, max(20, args.steps // 2), 3)
+        workloads["mse_only"] = {
+            "workload": "decode-b32-hq32-hkv8-d128-ctx8192-k3v4-mse-only: store 1 new token + attend 8192",
+            "kv_bytes_per_step": s["kv_bytes"], "ms_per_step": round(m["ms_per_step"], 5),
+            "tbs": round(s["kv_bytes"] / (m["ms_per_step"] * 1e-3) / 1e12, 4),
+            "split_median_ms": round(m["split_median_ms"], 5),
+            "split_hbm_frac": round(s["kv_bytes"] / (m["split_median_ms"] * 1e-3) / 1e12 / HBM_PEAK_TBS, 4)}
+        log(f"MSE-only step {m['ms_per_step'] * 1e3:.1f} us, split median {m['split_median_ms'] * 1e3:.1f} us")
+        s.clear()
+        torch.cuda.empty_cache()
+        for name, setup in (("long_d256", setup_long), ("ragged_hybrid", setup_ragged)):
+            log(f"workload {name}")
+            w = setup(torch, tq, synth)
+            workloads[name] = time_workload(torch, w, max(20, args.steps // 2))
+            log(f"{name}: {workloads[name]['median_ms'] * 1e3:.1f} us, {workloads[name]['tbs']:.3f} TB/s")
+            w.clear()
+            torch.cuda.empty_cache()
+        log("quantise workload")
+        workloads["quantize"] = bench_quantize(torch, tq, synth, reps=max(20, args.steps // 2))
+        log(f"quantise K3V4 {workloads['quantize']['k3v4']['median_ms'] * 1e3:.1f} us")
+    cpu = None
+    if not args.skip_cpu:
+        log("cpu baseline (oracle)")
+        cpu = cpu_baseline(synth)
 
     traffic = _traffic_record(None)
+    kv_bytes = 32 * 8 * 8192 * REC_BYTES_K3V4
     line = {
         "metric": METRIC,
         "value": round(value, 4),
@@ -270,18 +491,23 @@ def main():
         "vs_baseline": None,
         "dtype": "f32acc-bf16x2",
         "data": "synthetic",
-        "config": {"workload": "decode-b32-hq32-hkv8-d128-ctx8192-k3v4: store 1 new token + attend 8192",
+        "config": {"workload": "decode-b32-hq32-hkv8-d128-ctx8192-k3v4: store 1 new token + attend 8192 "
+                               "(HIP graph per step)",
                    "batch": 32, "q_heads": 32, "kv_heads": 8, "head_dim": 128, "context": 8192,
                    "k_bits": 3, "v_bits": 4, "chunk_tokens": args.chunk, "pool_copies": 3},
         "hbm_frac": round(value / HBM_PEAK_TBS, 4),
         "decode_tokens_per_s": round(32 / (ms_step * 1e-3), 1),
-        "kv_bytes_per_step": 32 * 8 * 8192 * REC_BYTES_K3V4,
-        "quantize": qres,
+        "kv_bytes_per_step": kv_bytes,
+        "median_ms_per_step": round(dec["median_ms_per_step"], 5),
+        "eager_ms_per_step": round(dec["eager_ms_per_step"], 5),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_TBS * 1000, "unit": "GB/s",
                      "frac": round(achieved / (HBM_PEAK_TBS * 1000), 4), "traffic": traffic,
-                     "kernel": "decode_split_kernel<128,4,3,4,true>", "bytes_per_launch": 32 * 8 * 8192 * REC_BYTES_K3V4,
-                     "avg_launch_ms": round(split_avg, 5)},
-        "mse_only": mse,
+                     "kernel": "decode_split_kernel<128,4,3,4,true>", "bytes_per_launch": kv_bytes,
+                     "median_launch_ms": round(split_ms, 5), "min_launch_ms": round(dec["split_min_ms"], 5),
+                     "timing": f"median over replays of graphs of {SPLIT_LAUNCHES_PER_GRAPH} back-to-back "
+                               f"split-only launches (3 pool copies in turn)",
+                     "consistent_with_step": bool(split_ms <= ms_step and achieved >= kv_bytes / (ms_step * 1e-3) / 1e9)},
+        "workloads": workloads,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

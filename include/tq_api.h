@@ -230,18 +230,33 @@ typedef struct {
   float* scores_out;         /* device fp32 [batch][num_q_heads][scores_stride] or NULL:
                                 raw scores, cached tokens first then recent ones */
   int32_t scores_stride;     /* >= max_seq_len + recent_window when scores_out != NULL */
-  void* split_events[2];     /* optional hipEvent_t pair (or NULLs): recorded on `stream`
-                                right before and right after the split launch(es), so a
-                                caller can time the streaming kernel alone */
+  int32_t flags;             /* a bitwise or of TQ_DECODE_* below (0 = defaults) */
 } tq_decode_args;
+
+/* Decode flags.
+ *   TQ_DECODE_DETERMINISTIC : the waves of a workgroup take the 32-token steps
+ *     of a split in a fixed order instead of claiming the next free step, so
+ *     every fp32 sum is formed in the same order on every call and the outputs
+ *     (and scores) are bit-identical from run to run and between eager and
+ *     graph-replayed launches.  Without it the step a wave takes depends on
+ *     issue timing and outputs differ run to run by fp32 reassociation
+ *     (~1e-5 relative); it is the faster schedule when the waves of a CU
+ *     progress unevenly.
+ * Other bits are rejected with TQ_EINVAL. */
+enum { TQ_DECODE_DETERMINISTIC = 1 };
 
 /* Workspace bytes the decode call needs for these arguments (only the shape
  * fields are read).  0 on invalid arguments. */
 size_t tq_decode_workspace_bytes(const tq_decode_args* args);
 
-/* Enqueue decode attention.  Device-side contents (seq_lens, block tables)
- * are trusted: seq_lens[b] <= min(max_seq_len, 16 * max_blocks_per_seq) and
- * every block id used must lie inside the pool. */
+/* Enqueue decode attention.  Device-side contents are clamped where a bad
+ * value would address memory: seq_lens[b] is clamped to [0, max_seq_len],
+ * recent_lens[b] to [0, recent_window], and a block id outside
+ * [0, pool_blocks) skips its 16 tokens.  The launch configuration (LDS of the
+ * recent window next to the kernel's own tables) is checked on the host:
+ * a recent_window whose buffers do not fit a compute unit's 160 KB of LDS for
+ * this head_dim and query-group size is rejected with TQ_EINVAL before
+ * anything is enqueued. */
 int tq_decode_attention(const tq_decode_args* args, void* stream);
 
 /* Thread-local message of the last failure ("" if none). */

@@ -14,7 +14,7 @@ import os
 
 __all__ = [
     "TQ_OK", "TQ_EINVAL", "TQ_EUNSUPPORTED", "TQ_EHIP", "TQ_ENOMEM", "TQ_DTYPE_F32", "TQ_DTYPE_BF16", "TQ_PRESET_MSE_ONLY",
-    "TQ_PRESET_UNIFORM", "TQ_PRESET_ROTATE_V", "tq_uniform_codebook", "tq_fold_output_projection",
+    "TQ_PRESET_UNIFORM", "TQ_PRESET_ROTATE_V", "TQ_DECODE_DETERMINISTIC", "tq_uniform_codebook", "tq_fold_output_projection",
     "TqError", "Context", "library_path", "load", "tq_codebook_init", "tq_ctx_destroy", "tq_ctx_tables",
     "tq_lloyd_max", "tq_record_layout", "tq_draw_params", "tq_block_bytes", "tq_quantize_store",
     "tq_decode_workspace_bytes", "tq_decode_attention", "tq_last_error", "EXPORTED_SYMBOLS",
@@ -25,6 +25,7 @@ TQ_DTYPE_F32, TQ_DTYPE_BF16 = 0, 1
 TQ_PRESET_MSE_ONLY = 1
 TQ_PRESET_UNIFORM = 2
 TQ_PRESET_ROTATE_V = 4
+TQ_DECODE_DETERMINISTIC = 1
 
 EXPORTED_SYMBOLS = [
     "tq_codebook_init", "tq_ctx_destroy", "tq_ctx_tables", "tq_ctx_preset", "tq_lloyd_max", "tq_uniform_codebook",
@@ -68,7 +69,7 @@ class tq_decode_args(ctypes.Structure):
         ("recent_lens", ctypes.c_void_p), ("recent_window", ctypes.c_int32), ("sm_scale", ctypes.c_float),
         ("chunk_tokens", ctypes.c_int32), ("max_seq_len", ctypes.c_int32), ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t), ("out", ctypes.c_void_p), ("scores_out", ctypes.c_void_p),
-        ("scores_stride", ctypes.c_int32), ("split_events", ctypes.c_void_p * 2),
+        ("scores_stride", ctypes.c_int32), ("flags", ctypes.c_int32),
     ]
 
 
@@ -274,15 +275,77 @@ def tq_quantize_store(ctx: Context, k, v, slot_mapping, pool, stream=None) -> No
                                     _ptr(pool), pool.shape[0], _stream(stream)), "tq_quantize_store")
 
 
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _on_device(t) -> bool:
+    return t.is_cuda
+
+
+def _check_dev(name, t, dtype=None, shape=None, dim=None):
+    """A CUDA tensor, contiguous, of the given dtype and (prefix of) shape."""
+    import torch
+    _need(isinstance(t, torch.Tensor), f"{name} must be a torch tensor")
+    _need(_on_device(t), f"{name} must be a device (CUDA) tensor")
+    _need(t.is_contiguous(), f"{name} must be contiguous")
+    if dtype is not None:
+        _need(t.dtype == dtype, f"{name} must be {dtype}, got {t.dtype}")
+    if dim is not None:
+        _need(t.dim() == dim, f"{name} must have {dim} dimensions, got shape {tuple(t.shape)}")
+    if shape is not None:
+        for i, n in enumerate(shape):
+            if n is not None:
+                _need(t.dim() > i and t.shape[i] == n, f"{name} has shape {tuple(t.shape)}, expected {shape}")
+
+
 def _decode_args(q, ctxs, pools, block_tables, seq_lens, out, workspace=None, seq_preset=None, recent_k=None,
                  recent_v=None, recent_lens=None, sm_scale=0.0, chunk_tokens=512, max_seq_len=None,
-                 scores_out=None, split_events=None):
+                 scores_out=None, deterministic=False, check_workspace=True):
+    """Marshal the decode arguments after checking every tensor's device,
+    dtype, layout and shape against the others (the library trusts device
+    pointers, so a mismatch here would otherwise address memory out of
+    bounds)."""
+    import torch
+    _need(1 <= len(ctxs) <= 2 and len(ctxs) == len(pools), "one or two contexts, one pool per context")
+    _check_dev("q", q, dim=3)
+    _need(q.dtype in (torch.bfloat16, torch.float32), "q must be bfloat16 or float32")
     B, Hq, d = q.shape
+    for i, (c, p) in enumerate(zip(ctxs, pools)):
+        _need(c.handle, f"context {i} is closed")
+        _need(c.head_dim == d, f"q has head_dim {d} but context {i} has {c.head_dim}")
+        _check_dev(f"pools[{i}]", p, torch.uint8, dim=3)
+        _need(p.shape[2] == c.block_bytes, f"pools[{i}] records are {p.shape[2]} bytes, context {i} needs {c.block_bytes}")
+    Hkv = pools[0].shape[1]
+    _need(all(p.shape[1] == Hkv for p in pools), "every pool must have the same number of KV heads")
+    _need(Hkv > 0 and Hq % Hkv == 0, f"num_q_heads {Hq} must be a multiple of num_kv_heads {Hkv}")
+    _check_dev("block_tables", block_tables, torch.int32, (B, None), dim=2)
+    _check_dev("seq_lens", seq_lens, torch.int32, (B,), dim=1)
+    _check_dev("out", out, torch.float32, (B, Hq, d), dim=3)
+    if len(ctxs) == 2:
+        _need(seq_preset is not None, "two presets need seq_preset")
+    if seq_preset is not None:
+        _check_dev("seq_preset", seq_preset, torch.int8, (B,), dim=1)
+    has_recent = recent_k is not None
+    _need(has_recent == (recent_v is not None) == (recent_lens is not None),
+          "recent_k, recent_v and recent_lens go together")
+    if has_recent:
+        _check_dev("recent_k", recent_k, torch.bfloat16, (B, Hkv, None, d), dim=4)
+        _check_dev("recent_v", recent_v, torch.bfloat16, tuple(recent_k.shape), dim=4)
+        _check_dev("recent_lens", recent_lens, torch.int32, (B,), dim=1)
+    W = recent_k.shape[2] if has_recent else 0
+    msl = block_tables.shape[1] * 16 if max_seq_len is None else int(max_seq_len)
+    if scores_out is not None:
+        _check_dev("scores_out", scores_out, torch.float32, (B, Hq, None), dim=3)
+        _need(scores_out.shape[2] >= msl + W, f"scores_out needs >= {msl + W} columns")
+    if check_workspace:
+        _check_dev("workspace", workspace, torch.uint8)
     a = tq_decode_args()
     a.q = _ptr(q)
     a.q_dtype = _dtype_code(q)
     a.batch, a.num_q_heads = B, Hq
-    a.num_kv_heads = pools[0].shape[1]
+    a.num_kv_heads = Hkv
     a.num_presets = len(ctxs)
     for i, (c, p) in enumerate(zip(ctxs, pools)):
         a.ctx[i] = c.handle
@@ -293,22 +356,21 @@ def _decode_args(q, ctxs, pools, block_tables, seq_lens, out, workspace=None, se
     a.max_blocks_per_seq = block_tables.shape[1]
     a.seq_lens = _ptr(seq_lens)
     a.recent_k, a.recent_v, a.recent_lens = _ptr(recent_k), _ptr(recent_v), _ptr(recent_lens)
-    a.recent_window = recent_k.shape[2] if recent_k is not None else 0
+    a.recent_window = W
     a.sm_scale = sm_scale
     a.chunk_tokens = chunk_tokens
-    a.max_seq_len = block_tables.shape[1] * 16 if max_seq_len is None else max_seq_len
+    a.max_seq_len = msl
     a.workspace = _ptr(workspace)
     a.workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     a.out = _ptr(out)
     a.scores_out = _ptr(scores_out)
     a.scores_stride = scores_out.shape[-1] if scores_out is not None else 0
-    if split_events is not None:
-        a.split_events[0], a.split_events[1] = split_events
+    a.flags = TQ_DECODE_DETERMINISTIC if deterministic else 0
     return a
 
 
 def tq_decode_workspace_bytes(q, ctxs, pools, block_tables, seq_lens, out, **kw) -> int:
-    a = _decode_args(q, ctxs, pools, block_tables, seq_lens, out, **kw)
+    a = _decode_args(q, ctxs, pools, block_tables, seq_lens, out, check_workspace=False, **kw)
     n = load().tq_decode_workspace_bytes(ctypes.byref(a))
     if n == 0:
         raise TqError(TQ_EINVAL, "tq_decode_workspace_bytes")
@@ -321,7 +383,7 @@ def tq_decode_attention(q, ctxs, pools, block_tables, seq_lens, out, workspace, 
     workspace: device uint8 tensor of tq_decode_workspace_bytes(...) bytes.
     Keyword arguments: seq_preset (int8 [B]), recent_k / recent_v (bf16
     [B, Hkv, W, d]) with recent_lens (int32 [B]), sm_scale, chunk_tokens,
-    max_seq_len, scores_out (float32 [B, Hq, stride]), split_events (a pair of
-    raw hipEvent_t handles recorded around the split launch)."""
+    max_seq_len, scores_out (float32 [B, Hq, stride]), deterministic (a fixed
+    step order per wave: bit-identical outputs run to run)."""
     a = _decode_args(q, ctxs, pools, block_tables, seq_lens, out, workspace, **kw)
     _check(load().tq_decode_attention(ctypes.byref(a), _stream(stream)), "tq_decode_attention")

@@ -34,6 +34,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include <type_traits>
 
@@ -83,6 +84,7 @@ struct DArgs {
   float* scores;
   int scores_stride;
   int direct;  // every sequence has at most one split: write the normalised output, no partials
+  int det;     // fixed step order per wave (bit-identical outputs run to run)
 };
 
 __device__ __forceinline__ int seq_cached(const DArgs& a, int b) {
@@ -580,13 +582,19 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h, int t0, int t1
   // more steps and the item's waves finish together.  Ring depth R::nslot;
   // stq[k] is the step held by slot k (-1: none).  Claims are increasing per
   // wave, and once the counter passes the last step every later claim fails.
+  // In deterministic mode (a.det) every wave claims from its own counter
+  // s_claim[1 + wave] instead, which starts at NW (nslot - 1) + wave and
+  // advances by NW: wave w takes steps w, w + NW, w + 2 NW, ... in order, so
+  // every wave sums the same steps in the same order on every call.
   const int nsteps = (t1 - t0 + 31) / 32;
   const bool exact_wait = a.scores == nullptr;  // score stores also count in vmcnt
   bool more = true;
-  auto claim = [&]() -> int {
+  int* const ctr = s_claim + (a.det ? 1 + wave : 0);
+  const int ctr_inc = a.det ? NW : 1;
+  auto claim = [&](int) -> int {
     if (!more) return -1;
     int v = 0;
-    if ((int)opaque_u32((uint32_t)lane) == 0) v = atomicAdd(s_claim, 1);
+    if ((int)opaque_u32((uint32_t)lane) == 0) v = atomicAdd(ctr, ctr_inc);
     v = __builtin_amdgcn_readfirstlane(v);
     more = v < nsteps;
     return more ? v : -1;
@@ -605,7 +613,7 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h, int t0, int t1
     constexpr int SL = decltype(slot_c)::value;
     constexpr int FREE = (SL + R::nslot - 1) % R::nslot;  // the slot of the step computed last
     if (stq[SL] < 0) return false;
-    stq[FREE] = claim();
+    stq[FREE] = claim(stq[SL]);
     if (stq[FREE] >= 0) {
       wait_lgkm0();  // ring slot reuse: the reads of the step that used it are complete
       issue(stq[FREE], FREE);
@@ -965,7 +973,9 @@ __global__ __launch_bounds__((split_waves<D, GP>() * 64)) void decode_split_kern
   __shared__ __attribute__((aligned(16))) float s_q[GP * D];
   __shared__ __attribute__((aligned(16))) float s_pq[GP * D];
   __shared__ int s_exp[GP];
-  __shared__ int s_claim;  // next unclaimed step of the current item
+  // next unclaimed step of the current item: [0] shared by the waves, [1 + w]
+  // wave w's own sequence in deterministic mode
+  __shared__ int s_claim[1 + split_waves<D, GP>()];
   const int tid = threadIdx.x, lane = tid & 63;
 
   // tables: centroid pairs of this preset, +-1 patterns of sign bytes
@@ -1024,7 +1034,8 @@ __global__ __launch_bounds__((split_waves<D, GP>() * 64)) void decode_split_kern
         if (i < nstage) s_blk[i] = (i < nblk && blk[r] >= 0 && (int64_t)blk[r] < pblocks) ? blk[r] : -1;
       }
       // steps wave + NW k, k < nslot - 1, are handed out statically
-      if (tid == 0) s_claim = NW * (R::nslot - 1);
+      if (tid == 0) s_claim[0] = NW * (R::nslot - 1);
+      if (tid < NW) s_claim[1 + tid] = NW * (R::nslot - 1) + tid;
       // every path through the masked stores above has its loads complete
       // here; otherwise the compiler keeps a load pending on the path that
       // skips a store and answers a later write of that register with a full
@@ -1081,7 +1092,7 @@ __global__ __launch_bounds__((split_waves<D, GP>() * 64)) void decode_split_kern
         ready_bh = bh;
       };
       split_cached_chunk<D, GP, KB, VB, QJ>(a, pr, h, t0, t1, s_blk, s_pair, s_sgn, s_p, s_main, s_stat, A1, A3,
-                                        s_m, s_l, b, &s_claim, setup);
+                                        s_m, s_l, b, s_claim, setup);
     } else if (!kDirect) {
       split_recent<D, GP>(a, b, h, seq_recent(a, b), s_p, s_merge, s_m, s_l);
     }
@@ -1237,73 +1248,116 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DArgs a
 #endif  // TQ_DECODE_QJL
 
 // ---------------------------------------------------------------------------
+// Launch configuration of one split kernel instantiation on one device,
+// cached: its static LDS (the tables declared in the kernel), the dynamic LDS
+// last granted with hipFuncSetAttribute, and workgroups per CU for the last
+// dynamic size (from the occupancy calculator, so registers count as well as
+// LDS).
+struct SplitLaunchCache {
+  std::mutex mu;
+  struct Dev {
+    bool init = false;
+    int static_lds = 0, lds_limit = 0, cus = 0, granted = -1, occ_for = -1, per_cu = 1;
+  } dev[16];
+};
+
 template <int D, int GP, int KB, int VB, bool QJ>
-static hipError_t launch_split(const DArgs& a, int pr, hipStream_t s) {
+static hipError_t launch_split(const DArgs& a, int pr, hipStream_t s, bool dry_run) {
   auto kern = decode_split_kernel<D, GP, KB, VB, QJ>;
   using SL = SplitLds<D, GP, KB, VB, QJ>;
+  static SplitLaunchCache cache;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 16) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(cache.mu);
+  auto& c = cache.dev[dev];
+  if (!c.init) {
+    hipFuncAttributes attr{};
+    if ((e = hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(kern))) != hipSuccess) return e;
+    c.static_lds = (int)attr.sharedSizeBytes;
+    c.lds_limit = 160 * 1024;
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) == hipSuccess && v > 0)
+      c.lds_limit = v;
+    c.cus = 256;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) c.cus = v;
+    c.init = true;
+  }
   size_t lds = SL::total;
   const size_t recent_need = SL::kMainOffset + (size_t)(GP * a.W + GP * D) * 4;
   if (recent_need > lds) lds = recent_need;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)lds);
-  if (e != hipSuccess) return e;
-  int dev = 0, cus = 256;
-  (void)hipGetDevice(&dev);
-  (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  // persistent workgroups: as many as fit on the chip at once (LDS bounds it)
-  const int per_cu = std::max(1, std::min(8, (int)((160 * 1024) / lds)));
-  hipLaunchKernelGGL(kern, dim3(cus * per_cu), dim3(SL::NW * 64), lds, s, a, pr);
+  if ((int64_t)lds + c.static_lds > c.lds_limit) {
+    set_error("decode: head_dim %d with %d query heads per KV head and recent_window %d needs %zu + %d bytes of LDS "
+              "per workgroup (limit %d)", D, a.G, a.W, lds, c.static_lds, c.lds_limit);
+    return hipErrorInvalidValue;
+  }
+  if (dry_run) return hipSuccess;
+  if (c.granted != (int)lds) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    c.granted = (int)lds;
+  }
+  if (c.occ_for != (int)lds) {
+    // persistent workgroups: as many as can be resident on the chip at once
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, SL::NW * 64, lds) != hipSuccess || nb < 1) nb = 1;
+    c.per_cu = std::min(nb, 8);
+    c.occ_for = (int)lds;
+  }
+  hipLaunchKernelGGL(kern, dim3(c.cus * c.per_cu), dim3(SL::NW * 64), lds, s, a, pr);
   return hipGetLastError();
 }
 
 template <int D, int GP, bool QJ>
-static hipError_t dispatch_preset(const DArgs& a, int pr, int kb, int vb, hipStream_t s) {
-  if (kb == 2) return vb == 2 ? launch_split<D, GP, 2, 2, QJ>(a, pr, s) : launch_split<D, GP, 2, 4, QJ>(a, pr, s);
-  if (kb == 3) return vb == 2 ? launch_split<D, GP, 3, 2, QJ>(a, pr, s) : launch_split<D, GP, 3, 4, QJ>(a, pr, s);
-  return vb == 2 ? launch_split<D, GP, 4, 2, QJ>(a, pr, s) : launch_split<D, GP, 4, 4, QJ>(a, pr, s);
+static hipError_t dispatch_preset(const DArgs& a, int pr, int kb, int vb, hipStream_t s, bool dry) {
+  if (kb == 2) return vb == 2 ? launch_split<D, GP, 2, 2, QJ>(a, pr, s, dry) : launch_split<D, GP, 2, 4, QJ>(a, pr, s, dry);
+  if (kb == 3) return vb == 2 ? launch_split<D, GP, 3, 2, QJ>(a, pr, s, dry) : launch_split<D, GP, 3, 4, QJ>(a, pr, s, dry);
+  return vb == 2 ? launch_split<D, GP, 4, 2, QJ>(a, pr, s, dry) : launch_split<D, GP, 4, 4, QJ>(a, pr, s, dry);
 }
 
 // The split launches of one key kind.  This source is compiled twice, with
 // TQ_DECODE_QJL = 1 (keys with the QJL sketch; this object also holds the
 // combine kernel and the entry point) and = 0 (MSE-only keys), so that no
 // kernel is instantiated in both objects.
-hipError_t launch_split_qjl(const DArgs& a, int pr, int d, int G, int kb, int vb, hipStream_t s);
-hipError_t launch_split_mse(const DArgs& a, int pr, int d, int G, int kb, int vb, hipStream_t s);
+// dry = true only checks that the launch fits (LDS) and enqueues nothing.
+hipError_t launch_split_qjl(const DArgs& a, int pr, int d, int G, int kb, int vb, hipStream_t s, bool dry);
+hipError_t launch_split_mse(const DArgs& a, int pr, int d, int G, int kb, int vb, hipStream_t s, bool dry);
 
 #if TQ_DECODE_QJL
-hipError_t launch_split_qjl(const DArgs& a, int pr, int d, int G, int kb, int vb, hipStream_t s) {
-  if (d == 128) return G <= 4 ? dispatch_preset<128, 4, true>(a, pr, kb, vb, s) : dispatch_preset<128, 8, true>(a, pr, kb, vb, s);
-  return G <= 4 ? dispatch_preset<256, 4, true>(a, pr, kb, vb, s) : dispatch_preset<256, 8, true>(a, pr, kb, vb, s);
+hipError_t launch_split_qjl(const DArgs& a, int pr, int d, int G, int kb, int vb, hipStream_t s, bool dry) {
+  if (d == 128) return G <= 4 ? dispatch_preset<128, 4, true>(a, pr, kb, vb, s, dry) : dispatch_preset<128, 8, true>(a, pr, kb, vb, s, dry);
+  return G <= 4 ? dispatch_preset<256, 4, true>(a, pr, kb, vb, s, dry) : dispatch_preset<256, 8, true>(a, pr, kb, vb, s, dry);
 }
 #else
-hipError_t launch_split_mse(const DArgs& a, int pr, int d, int G, int kb, int vb, hipStream_t s) {
-  if (d == 128) return G <= 4 ? dispatch_preset<128, 4, false>(a, pr, kb, vb, s) : dispatch_preset<128, 8, false>(a, pr, kb, vb, s);
-  return G <= 4 ? dispatch_preset<256, 4, false>(a, pr, kb, vb, s) : dispatch_preset<256, 8, false>(a, pr, kb, vb, s);
+hipError_t launch_split_mse(const DArgs& a, int pr, int d, int G, int kb, int vb, hipStream_t s, bool dry) {
+  if (d == 128) return G <= 4 ? dispatch_preset<128, 4, false>(a, pr, kb, vb, s, dry) : dispatch_preset<128, 8, false>(a, pr, kb, vb, s, dry);
+  return G <= 4 ? dispatch_preset<256, 4, false>(a, pr, kb, vb, s, dry) : dispatch_preset<256, 8, false>(a, pr, kb, vb, s, dry);
 }
 #endif
 
 #if TQ_DECODE_QJL
+// dry = true: only check that every split launch fits (no work enqueued).
 template <int D>
-static hipError_t launch_all(const DArgs& a0, const tq_decode_args* args, hipStream_t s) {
+static hipError_t launch_all(const DArgs& a0, const tq_decode_args* args, hipStream_t s, bool dry) {
   hipError_t e = hipSuccess;
   // with no recent window and max_seq_len <= chunk every sequence has at most
   // one split (cached lengths are clamped to max_seq_len): the split kernel
   // then writes the output itself and the combine pass is skipped
   DArgs a = a0;
   a.direct = (args->recent_k == nullptr && args->max_seq_len <= args->chunk_tokens) ? 1 : 0;
-  if (args->split_events[0] && (e = hipEventRecord((hipEvent_t)args->split_events[0], s)) != hipSuccess) return e;
   for (int pr = 0; pr < args->num_presets; ++pr) {
     const tq_ctx* c = args->ctx[pr];
-    e = c->qjl ? launch_split_qjl(a, pr, D, a.G, c->kb, c->vb, s) : launch_split_mse(a, pr, D, a.G, c->kb, c->vb, s);
+    e = c->qjl ? launch_split_qjl(a, pr, D, a.G, c->kb, c->vb, s, dry)
+               : launch_split_mse(a, pr, D, a.G, c->kb, c->vb, s, dry);
     if (e != hipSuccess) return e;
   }
-  if (args->split_events[1] && (e = hipEventRecord((hipEvent_t)args->split_events[1], s)) != hipSuccess) return e;
-  if (a.direct) return hipSuccess;
+  if (a.direct || dry) return hipSuccess;
   hipLaunchKernelGGL(decode_combine_kernel<D>, dim3(a.B * a.Hq), dim3(kCombineThreads), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_decode(const tq_decode_args* args, const DecodePlan& plan, hipStream_t stream) {
+static DArgs make_dargs(const tq_decode_args* args, const DecodePlan& plan) {
   DArgs a{};
   a.q = args->q;
   a.q_bf16 = args->q_dtype == TQ_DTYPE_BF16;
@@ -1338,7 +1392,18 @@ hipError_t launch_decode(const tq_decode_args* args, const DecodePlan& plan, hip
   a.out = args->out;
   a.scores = args->scores_out;
   a.scores_stride = args->scores_stride;
-  return plan.d == 128 ? launch_all<128>(a, args, stream) : launch_all<256>(a, args, stream);
+  a.det = (args->flags & TQ_DECODE_DETERMINISTIC) ? 1 : 0;
+  return a;
+}
+
+hipError_t check_decode_launch(const tq_decode_args* args, const DecodePlan& plan) {
+  const DArgs a = make_dargs(args, plan);
+  return plan.d == 128 ? launch_all<128>(a, args, nullptr, true) : launch_all<256>(a, args, nullptr, true);
+}
+
+hipError_t launch_decode(const tq_decode_args* args, const DecodePlan& plan, hipStream_t stream) {
+  const DArgs a = make_dargs(args, plan);
+  return plan.d == 128 ? launch_all<128>(a, args, stream, false) : launch_all<256>(a, args, stream, false);
 }
 #endif  // TQ_DECODE_QJL
 

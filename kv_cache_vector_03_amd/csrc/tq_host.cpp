@@ -573,6 +573,10 @@ int check_decode_shape(const tq_decode_args* a) {
     set_error("decode: recent_k, recent_v and recent_lens must be all set or all NULL");
     return TQ_EINVAL;
   }
+  if (a->flags & ~(int32_t)TQ_DECODE_DETERMINISTIC) {
+    set_error("decode: unknown flags 0x%x", (unsigned)a->flags);
+    return TQ_EINVAL;
+  }
   if (a->recent_k && (a->recent_window <= 0 || a->recent_window > 4096)) {
     set_error("decode: recent_window %d out of range 1..4096", a->recent_window);
     return TQ_EINVAL;
@@ -626,6 +630,7 @@ extern "C" int tq_decode_attention(const tq_decode_args* a, void* stream) {
               a->workspace_bytes);
     return TQ_EINVAL;
   }
+  if (check_decode_launch(a, plan) != hipSuccess) return TQ_EINVAL;  // message set by the check
   hipError_t e = launch_decode(a, plan, (hipStream_t)stream);
   if (e != hipSuccess) {
     set_error("decode: launch failed: %s", hipGetErrorString(e));

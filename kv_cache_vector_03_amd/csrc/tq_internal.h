@@ -71,5 +71,9 @@ struct DecodePlan {
 };
 DecodePlan plan_decode(const tq_decode_args* a);
 hipError_t launch_decode(const tq_decode_args* a, const DecodePlan& plan, hipStream_t stream);
+// Host-side check that every kernel of the decode fits a compute unit (LDS of
+// the recent window beside the kernel's own tables); on failure the message is
+// set with set_error and an error is returned.  Enqueues nothing.
+hipError_t check_decode_launch(const tq_decode_args* a, const DecodePlan& plan);
 
 }  // namespace tq

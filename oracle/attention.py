@@ -56,21 +56,22 @@ def decode_one_sequence(q, fields_per_head, ctx, recent_k=None, recent_v=None, s
     G = Hq // Hkv
     scale = (1.0 / np.sqrt(d)) if sm_scale is None else float(sm_scale)
     outs, scores = [], []
-    for h in range(Hq):
-        f = fields_per_head[h // G]
-        est = _keys.estimate_scores(q[h], f["idx"], f["sign"], f["n16"], f["g16"],
+    for hk in range(Hkv):
+        f = fields_per_head[hk]
+        heads = q[hk * G:(hk + 1) * G]  # the query heads that read KV head hk
+        est = _keys.estimate_scores(heads, f["idx"], f["sign"], f["n16"], f["g16"],
                                     ctx["d1"], ctx["d2"], ctx["S"], ctx["c32"], qjl=ctx.get("qjl", True))
         vhat = _values.dequantize_values(f["q"], f["s16"], f["z16"])
         if recent_k is not None:
-            rk = np.asarray(recent_k[h // G], dtype=np.float64)
-            rv = np.asarray(recent_v[h // G], dtype=np.float64)
-            exact = rk @ q[h]
-            s_all = np.concatenate([est, exact])
+            rk = np.asarray(recent_k[hk], dtype=np.float64)
+            rv = np.asarray(recent_v[hk], dtype=np.float64)
             v_all = np.concatenate([vhat, rv], axis=0)
         else:
-            s_all, v_all = est, vhat
-        outs.append(softmax_attend(scale * s_all, v_all))
-        scores.append(s_all)
+            v_all = vhat
+        for g in range(G):
+            s_all = np.concatenate([est[g], rk @ heads[g]]) if recent_k is not None else est[g]
+            outs.append(softmax_attend(scale * s_all, v_all))
+            scores.append(s_all)
     return np.stack(outs), np.stack(scores)
 
 

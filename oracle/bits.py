@@ -38,8 +38,11 @@ def unpack(packed, b: int, m: int) -> np.ndarray:
     """Inverse of :func:`pack`: ``m`` b-bit integers from each row of bytes."""
     p = np.asarray(packed, dtype=np.uint8)
     stream = np.unpackbits(p, axis=-1, bitorder="little")[..., : m * b]
-    planes = stream.reshape(p.shape[:-1] + (m, b)).astype(np.int64)
-    return np.sum(planes << np.arange(b), axis=-1)
+    planes = stream.reshape(p.shape[:-1] + (m, b))
+    out = np.zeros(p.shape[:-1] + (m,), dtype=np.uint16 if b > 8 else np.uint8)
+    for k in range(b):  # stream bit b*j + k is bit k of element j
+        out |= planes[..., k].astype(out.dtype) << k
+    return out.astype(np.int64)
 
 
 def to_fp16_bits(x) -> np.ndarray:

@@ -113,21 +113,27 @@ def query_tables(q, d1, d2, S):
 
 
 def estimate_scores(q, idx, sign, n16, g16, d1, d2, S, c32, qjl=True):
-    """Estimated <q, k_t> for one query q [d] against stored keys:
+    """Estimated <q, k_t> for a query q [d] (or several queries [G, d] against
+    the same keys) against stored keys:
 
       est_t = n_t * ( sum_j q~_j c[idx_tj]
                       + sqrt(pi/2)/d * gamma_t * sum_i p_i (2 sigma_ti - 1) ),
 
     with q~ = Pi q, p = S q~ and the stored binary16 n_t, gamma_t.  MSE-only
-    keys (``qjl=False``) drop the second term: est_t = n_t <q~, c[idx_t]>."""
+    keys (``qjl=False``) drop the second term: est_t = n_t <q~, c[idx_t]>.
+    Returns [T] for one query, [G, T] for several."""
     q = np.asarray(q, dtype=np.float64)
+    one = q.ndim == 1
+    q = np.atleast_2d(q)
     d = q.shape[-1]
     qt, p = query_tables(q, d1, d2, S)
     c = np.asarray(c32, dtype=np.float32).astype(np.float64)
     n = _bits.from_fp16_bits(n16)
     g = _bits.from_fp16_bits(g16)
-    mse = (c[np.asarray(idx)] * qt[None, :]).sum(axis=1)
+    mse = (c[np.asarray(idx)] @ qt.T).T  # [G, T]: sum_j c[idx_tj] q~_j
     if not qjl:
-        return n * mse
-    pm = (2.0 * np.asarray(sign, dtype=np.float64) - 1.0) @ p
-    return n * (mse + QJL_SCALE(d) * g * pm)
+        est = n * mse
+    else:
+        pm = ((2.0 * np.asarray(sign, dtype=np.float64) - 1.0) @ p.T).T  # [G, T]
+        est = n * (mse + QJL_SCALE(d) * g * pm)
+    return est[0] if one else est

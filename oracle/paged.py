@@ -98,33 +98,46 @@ def write_tokens(pool, slot_mapping, head: int, kenc: dict, venc: dict, lay: dic
 def read_tokens(pool, block_table_row, length: int, head: int, lay: dict) -> dict:
     """Read the first ``length`` tokens of one sequence and KV head back into
     fields: idx [L, d], sign [L, d], n16, g16 [L], q [L, d], s16, z16 [L, d/32]
-    (sign and g16 are zeros for MSE-only keys)."""
+    (sign and g16 are zeros for MSE-only keys).
+
+    The records of the sequence's blocks are gathered whole, then each region
+    is cut out of them as the layout above describes: slot-major regions are
+    [16][width] per record, the value codes are [width/4][16][4] (dword
+    columns), the value metadata [d/32][16] pairs of fp16."""
     d, b_k, b_v = lay["d"], lay["b_k"], lay["b_v"]
     ng = d // 32
-    t = np.arange(length, dtype=np.int64)
-    blk = np.asarray(block_table_row, dtype=np.int64)[t // BLOCK][:, None]
-    slot = t % BLOCK
+    nblk = (length + BLOCK - 1) // BLOCK
+    recs = pool[np.asarray(block_table_row, dtype=np.int64)[:nblk], head]  # [nblk, record bytes]
     qjl = lay["qjl"]
-    kcodes = pool[blk, head, _region_index(lay, "kcodes", slot, b_k * d // 8, True)]
+
+    def region(name, width):
+        o, size = lay[name]
+        assert size == BLOCK * width
+        return recs[:, o:o + size]
+
+    def slot_major(name, width):
+        return region(name, width).reshape(nblk * BLOCK, width)[:length]
+
+    def dword_columns(name, width):
+        r = region(name, width).reshape(nblk, width // 4, BLOCK, 4)  # [block, dword, slot, byte]
+        return r.transpose(0, 2, 1, 3).reshape(nblk * BLOCK, width)[:length]
+
+    kcodes = slot_major("kcodes", b_k * d // 8)
     if qjl:
-        sign = _bits.unpack(pool[blk, head, _region_index(lay, "kqjl", slot, d // 8, True)], 1, d).astype(np.uint8)
+        sign = _bits.unpack(slot_major("kqjl", d // 8), 1, d).astype(np.uint8)
     else:
         sign = np.zeros((length, d), dtype=np.uint8)
-    kmeta = np.ascontiguousarray(pool[blk, head, _region_index(lay, "kmeta", slot, 4 if qjl else 2, True)]).view(np.uint16)
-    vcodes = pool[blk, head, _region_index(lay, "vcodes", slot, b_v * d // 8, False)]
-    o, _ = lay["vmeta"]
-    s16 = np.zeros((length, ng), np.uint16)
-    z16 = np.zeros((length, ng), np.uint16)
-    for g in range(ng):
-        idx = o + (g * BLOCK + slot[:, None]) * 4 + np.arange(4)[None, :]
-        pair = np.ascontiguousarray(pool[blk, head, idx]).view(np.uint16)
-        s16[:, g], z16[:, g] = pair[:, 0], pair[:, 1]
+    kmeta = np.ascontiguousarray(slot_major("kmeta", 4 if qjl else 2)).view(np.uint16)
+    vcodes = dword_columns("vcodes", b_v * d // 8)
+    o, size = lay["vmeta"]
+    vm = np.ascontiguousarray(recs[:, o:o + size]).view(np.uint16).reshape(nblk, ng, BLOCK, 2)
+    vm = vm.transpose(0, 2, 1, 3).reshape(nblk * BLOCK, ng, 2)[:length]  # [token, group, (s, z)]
     return {
         "idx": _bits.unpack(kcodes, b_k, d),
         "sign": sign,
         "n16": kmeta[:, 0].copy(),
         "g16": kmeta[:, 1].copy() if qjl else np.zeros(length, dtype=np.uint16),
         "q": _bits.unpack(vcodes, b_v, d),
-        "s16": s16,
-        "z16": z16,
+        "s16": np.ascontiguousarray(vm[:, :, 0]),
+        "z16": np.ascontiguousarray(vm[:, :, 1]),
     }

@@ -78,8 +78,8 @@ def compare_pools(gpu, expected, mask, select=None):
     if select is not None:
         g, e, m = g[select], e[select], m[select]
     diff = g ^ e
-    outside = np.unpackbits(diff & ~m).sum()
-    inside = np.unpackbits(diff & m).sum()
+    outside = np.bitwise_count(diff & ~m).sum(dtype=np.int64)
+    inside = np.bitwise_count(diff & m).sum(dtype=np.int64)
     return int(outside), int(inside)
 
 

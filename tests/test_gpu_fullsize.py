@@ -1,17 +1,18 @@
 """GPU parity at the workloads' full sizes, in the launch configuration the
-benchmark uses (chunk_tokens = 8192), on sampled outputs.
+benchmark uses (chunk_tokens = 8192), on every output.
 
 The whole cache is written by tq_quantize_store from seeded inputs generated
-on the device; the records of the sampled (sequence, KV head) pairs are then
-replaced by the oracle's encoding of the same inputs, so that the decode of
-those pairs can be checked against the oracle's fp64 attention exactly as in
-the small parity tests (scores within 1e-3 of max(|ref|, rms(ref row)),
-outputs within 1e-3 relative per row).  The other pairs stay as the GPU
-quantiser wrote them: they are decoded in the same launch but not compared.
+on the device.  The decode reads that pool; the oracle reads the same pool
+back (``paged.read_tokens`` on a host copy) and runs its fp64 attention for
+every (sequence, KV head) pair, so both sides decode the same GPU-written
+records.  Every pair's outputs (within 1e-3 relative per row) and every score
+(within 1e-3 of max(|ref|, rms(ref row))) are compared, including the recent
+bf16 window's.  The pairs run on a host thread pool with one BLAS thread each.
 
 Workloads:
   * decode: B=32, Hq=32, Hkv=8, d=128, 8192 cached tokens, K3V4, a
-    16384-block pool through a permuted block table;
+    16384-block pool through a permuted block table (QJL and MSE-only keys,
+    and the deterministic schedule);
   * long: B=8, Hq=16, Hkv=4, d=256, 131072 cached tokens, K4V4, a
     65536-block pool;
   * ragged: B=64, Hq=32, Hkv=8, d=128, lognormal lengths (median 16384,
@@ -19,100 +20,91 @@ Workloads:
     last 128 tokens of each sequence as a bf16 window, 0.5% x20 outliers.
 """
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
+from threadpoolctl import threadpool_limits
 
 import kv_cache_vector_03_amd as tq
 import synth
-from oracle import attention, keys, paged, values
+from oracle import attention, paged
 from parity import oracle_params, output_errors, score_errors
 
 pytestmark = pytest.mark.gpu
 
 TOL = 1e-3
 CHUNK = 8192
+WORKERS = max(1, min(16, len(os.sched_getaffinity(0))))
 
 
-def _seq_inputs(seed, b, L, Hkv, d, p, factor):
-    k = synth.torch_normal_bf16((L, Hkv, d), seed * 1000003 + 2 * b, p=p, factor=factor)
-    v = synth.torch_normal_bf16((L, Hkv, d), seed * 1000003 + 2 * b + 1, p=p, factor=factor)
-    return k, v
-
-
-def _fill(ctx, pool, bt, lens, Hkv, d, seed, p, factor, sample):
-    """Quantise every sequence into ``pool`` on the GPU; return the host fp32
-    copies of the sampled (b, h) inputs."""
-    kept = {}
+def _fill(ctx, pool, bt, lens, Hkv, d, seed, p, factor, only=None):
+    """Quantise every sequence (of ``only``, if given) into ``pool`` on the GPU."""
     for b in range(len(lens)):
         L = int(lens[b])
-        if L == 0:
+        if L == 0 or (only is not None and b not in only):
             continue
-        k, v = _seq_inputs(seed, b, L, Hkv, d, p, factor)
+        k = synth.torch_normal_bf16((L, Hkv, d), seed * 1000003 + 2 * b, p=p, factor=factor)
+        v = synth.torch_normal_bf16((L, Hkv, d), seed * 1000003 + 2 * b + 1, p=p, factor=factor)
         t = torch.arange(L, device="cuda")
         slots = (bt[b][t // 16].long() * 16 + t % 16).to(torch.int32)
         tq.tq_quantize_store(ctx, k, v, slots, pool)
-        for (sb, sh) in sample:
-            if sb == b:
-                kept[(b, sh)] = (k[:, sh].float().cpu().numpy(), v[:, sh].float().cpu().numpy())
         del k, v
     torch.cuda.synchronize()
-    return kept
 
 
-def _oracle_records(pool, bt_np, b, h, K, V, prm, d, kb, vb, qjl=True):
-    """Overwrite the records of (b, h) in the device pool with the oracle's
-    encoding of K, V; return the oracle fields for the decode reference."""
-    L = K.shape[0]
-    lay = paged.layout(d, kb, vb, qjl=qjl)
-    nblk = (L + 15) // 16
-    tmp = paged.new_pool(nblk, pool.shape[1], lay)
-    ke = keys.encode_keys(K.astype(np.float64), prm["d1"], prm["d2"], prm["S"], prm["c32"], prm["t32"], qjl=qjl)
-    ve = values.encode_values(V, vb)
-    t = np.arange(L)
-    paged.write_tokens(tmp, (t // 16) * 16 + t % 16, h, ke, ve, lay)
-    dst = torch.from_numpy(bt_np[b][:nblk].astype(np.int64)).cuda()
-    pool[dst, h] = torch.from_numpy(tmp[:, h]).cuda()
-    return {"idx": ke["idx"], "sign": ke["sign"], "n16": ke["n16"], "g16": ke["g16"],
-            "q": ve["q"], "s16": ve["s16"], "z16": ve["z16"]}
-
-
-def _decode(qd, ctxs, pools, btd, lensd, msl, W=0, want_scores=True, **kw):
+def _decode(qd, ctxs, pools, btd, lensd, msl, W=0, **kw):
     B, Hq, d = qd.shape
     out = torch.full((B, Hq, d), float("nan"), dtype=torch.float32, device="cuda")
-    scores = torch.full((B, Hq, msl + W), float("nan"), dtype=torch.float32, device="cuda") if want_scores else None
+    scores = torch.full((B, Hq, msl + W), float("nan"), dtype=torch.float32, device="cuda")
     nbytes = tq.tq_decode_workspace_bytes(qd, ctxs, pools, btd, lensd, out, chunk_tokens=CHUNK, max_seq_len=msl, **kw)
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     tq.tq_decode_attention(qd, ctxs, pools, btd, lensd, out, ws, chunk_tokens=CHUNK, max_seq_len=msl,
                            scores_out=scores, **kw)
     torch.cuda.synchronize()
-    return out, scores
+    return out.cpu().numpy(), scores.cpu().numpy()
 
 
-def _check_pair(label, out, scores, q, b, h, G, fields, prm, L, rk=None, rv=None):
-    qh = q[b, h * G:(h + 1) * G].astype(np.float64)
-    ref_out, ref_sc = attention.decode_one_sequence(qh, [fields], prm, rk, rv)
-    got = out[b, h * G:(h + 1) * G].cpu().numpy().astype(np.float64)
-    oe = output_errors(got, ref_out)
-    msg = f"[full-size parity {label} b={b} h={h}] out err {oe:.2e}"
-    if scores is not None:
-        n = ref_sc.shape[1]
-        sc = scores[b, h * G:(h + 1) * G, :n].cpu().numpy().astype(np.float64)
-        if rk is not None:  # the window's scores follow the cached tokens at offset L
-            sc = np.concatenate([scores[b, h * G:(h + 1) * G, :L].cpu().numpy(),
-                                 scores[b, h * G:(h + 1) * G, L:L + rk.shape[1]].cpu().numpy()], axis=1)
-        se = score_errors(sc.astype(np.float64), ref_sc)
-        msg += f"  score err {se:.2e}"
-        assert se <= TOL, msg
-    print(msg, flush=True)
-    assert np.all(np.isfinite(got))
-    assert oe <= TOL, msg
+def _check_all_pairs(label, pools_host, lays, prms, bt_np, cached, q, G, out, scores, seq_preset=None,
+                     rk=None, rv=None, rlens=None):
+    """Oracle decode of every (sequence, KV head) from the GPU-written pools;
+    asserts every output row and every score."""
+    B, Hq, d = q.shape
+    Hkv = Hq // G
+
+    def pair(i):
+        b, h = divmod(i, Hkv)
+        pr = int(seq_preset[b]) if seq_preset is not None else 0
+        L = int(cached[b])
+        fields = paged.read_tokens(pools_host[pr], bt_np[b], L, h, lays[pr])
+        R = int(rlens[b]) if rk is not None else 0
+        rkk = rk[b, h:h + 1, :R].astype(np.float64) if rk is not None else None
+        rvv = rv[b, h:h + 1, :R].astype(np.float64) if rk is not None else None
+        ref_out, ref_sc = attention.decode_one_sequence(q[b, h * G:(h + 1) * G].astype(np.float64), [fields],
+                                                        prms[pr], rkk, rvv)
+        got = out[b, h * G:(h + 1) * G].astype(np.float64)
+        oe = output_errors(got, ref_out) if np.all(np.isfinite(got)) else np.inf
+        sc = scores[b, h * G:(h + 1) * G, :L + R].astype(np.float64)
+        se = score_errors(sc, ref_sc) if np.all(np.isfinite(sc)) else np.inf
+        return b, h, L + R, oe, se
+
+    with threadpool_limits(limits=1), ThreadPoolExecutor(max_workers=WORKERS) as ex:
+        res = list(ex.map(pair, range(B * Hkv)))
+    worst_o = max(res, key=lambda r: r[3])
+    worst_s = max(res, key=lambda r: r[4])
+    print(f"[full-size parity {label}] {len(res)} (sequence, KV head) pairs, {sum(r[2] for r in res) * G} "
+          f"scores: max out err {worst_o[3]:.2e} (b={worst_o[0]} h={worst_o[1]} len={worst_o[2]}), "
+          f"max score err {worst_s[4]:.2e} (b={worst_s[0]} h={worst_s[1]})", flush=True)
+    bad = [r for r in res if not (r[3] <= TOL and r[4] <= TOL)]
+    assert not bad, f"{len(bad)} pairs out of tolerance, first {bad[:4]}"
 
 
-@pytest.mark.parametrize("mse_only", [False, True])
-def test_decode_workload_full_size_sampled(mse_only):
+@pytest.mark.parametrize("mse_only,deterministic", [(False, False), (True, False), (False, True)])
+def test_decode_workload_full_size_all_pairs(mse_only, deterministic):
     """The benchmark's decode workload, with QJL keys and with MSE-only keys
-    (the benchmark's mse_only section)."""
+    (the benchmark's mse_only section), and on the deterministic schedule."""
     d, B, Hq, Hkv, L, kb, vb, nb, seed = 128, 32, 32, 8, 8192, 3, 4, 16384, 3
     G = Hq // Hkv
     prm = oracle_params(seed, d, kb)
@@ -122,19 +114,18 @@ def test_decode_workload_full_size_sampled(mse_only):
     bt = torch.from_numpy(bt_np).cuda()
     pool = torch.zeros((nb, Hkv, ctx.block_bytes), dtype=torch.uint8, device="cuda")
     lens = np.full(B, L)
-    sample = [(5, 3), (31, 0)]
-    kept = _fill(ctx, pool, bt, lens, Hkv, d, seed, 0.0, 20.0, sample)
-    fields = {s: _oracle_records(pool, bt_np, s[0], s[1], *kept[s], prm, d, kb, vb, qjl=not mse_only) for s in sample}
+    _fill(ctx, pool, bt, lens, Hkv, d, seed, 0.0, 20.0)
     q = synth.bf16_round(synth.queries(seed, B, Hq, d))
     qd = torch.from_numpy(q).to(torch.bfloat16).cuda()
-    out, scores = _decode(qd, [ctx], [pool], bt, torch.from_numpy(lens.astype(np.int32)).cuda(), L)
-    for (b, h) in sample:
-        _check_pair(f"decode b32 ctx8192 k3v4{' mse-only' if mse_only else ''}", out, scores, q, b, h, G,
-                    fields[(b, h)], prm, L)
+    out, scores = _decode(qd, [ctx], [pool], bt, torch.from_numpy(lens.astype(np.int32)).cuda(), L,
+                          deterministic=deterministic)
+    label = f"decode b32 ctx8192 k3v4{' mse-only' if mse_only else ''}{' deterministic' if deterministic else ''}"
+    _check_all_pairs(label, [pool.cpu().numpy()], [paged.layout(d, kb, vb, qjl=not mse_only)], [prm], bt_np, lens,
+                     q, G, out, scores)
     ctx.close()
 
 
-def test_long_context_d256_full_size_sampled():
+def test_long_context_d256_full_size_all_pairs():
     d, B, Hq, Hkv, L, kb, vb, nb, seed = 256, 8, 16, 4, 131072, 4, 4, 65536, 4
     G = Hq // Hkv
     prm = oracle_params(seed, d, kb)
@@ -143,18 +134,16 @@ def test_long_context_d256_full_size_sampled():
     bt = torch.from_numpy(bt_np).cuda()
     pool = torch.zeros((nb, Hkv, ctx.block_bytes), dtype=torch.uint8, device="cuda")
     lens = np.full(B, L)
-    sample = [(6, 1)]
-    kept = _fill(ctx, pool, bt, lens, Hkv, d, seed, 0.0, 20.0, sample)
-    fields = {s: _oracle_records(pool, bt_np, s[0], s[1], *kept[s], prm, d, kb, vb) for s in sample}
+    _fill(ctx, pool, bt, lens, Hkv, d, seed, 0.0, 20.0)
     q = synth.bf16_round(synth.queries(seed, B, Hq, d))
     qd = torch.from_numpy(q).to(torch.bfloat16).cuda()
     out, scores = _decode(qd, [ctx], [pool], bt, torch.from_numpy(lens.astype(np.int32)).cuda(), L)
-    for (b, h) in sample:
-        _check_pair("long d256 ctx131072 k4v4", out, scores, q, b, h, G, fields[(b, h)], prm, L)
+    _check_all_pairs("long d256 ctx131072 k4v4", [pool.cpu().numpy()], [paged.layout(d, kb, vb)], [prm], bt_np,
+                     lens, q, G, out, scores)
     ctx.close()
 
 
-def test_ragged_mixed_presets_recent_window_full_size_sampled():
+def test_ragged_mixed_presets_recent_window_full_size_all_pairs():
     d, B, Hq, Hkv, W, seed = 128, 64, 32, 8, 128, 5
     G = Hq // Hkv
     presets = [(3, 2), (4, 4)]
@@ -179,20 +168,8 @@ def test_ragged_mixed_presets_recent_window_full_size_sampled():
             off += n
         pools.append(torch.zeros((nbp, Hkv, ctxs[pr].block_bytes), dtype=torch.uint8, device="cuda"))
     bt = torch.from_numpy(bt_np).cuda()
-    even = [b for b in range(B) if seq_preset[b] == 0]
-    odd = [b for b in range(B) if seq_preset[b] == 1]
-    longest = int(np.argmax(cached))
-    sample = [(longest, 2), (max(odd if seq_preset[longest] == 0 else even, key=lambda b: -abs(cached[b] - 20000)), 5)]
-    kept = {}
     for pr in range(2):
-        sub = [s for s in sample if seq_preset[s[0]] == pr]
-        lens_pr = np.where(seq_preset == pr, cached, 0)
-        kept.update(_fill(ctxs[pr], pools[pr], bt, lens_pr, Hkv, d, seed, 0.005, 20.0, sub))
-    fields = {}
-    for s in sample:
-        pr = seq_preset[s[0]]
-        kb, vb = presets[pr]
-        fields[s] = _oracle_records(pools[pr], bt_np, s[0], s[1], *kept[s], prms[pr], d, kb, vb)
+        _fill(ctxs[pr], pools[pr], bt, np.where(seq_preset == pr, cached, 0), Hkv, d, seed, 0.005, 20.0)
     rng = np.random.default_rng([seed, 0x3EC])
     rk32 = synth.bf16_round(rng.standard_normal((B, Hkv, W, d)).astype(np.float32))
     rv32 = synth.bf16_round(rng.standard_normal((B, Hkv, W, d)).astype(np.float32))
@@ -204,11 +181,9 @@ def test_ragged_mixed_presets_recent_window_full_size_sampled():
     qd = torch.from_numpy(q).to(torch.bfloat16).cuda()
     msl = mb * 16
     out, scores = _decode(qd, ctxs, pools, bt, torch.from_numpy(cached.astype(np.int32)).cuda(), msl, W=W, **kw)
-    for (b, h) in sample:
-        R = int(rlens[b])
-        pr = seq_preset[b]
-        _check_pair(f"ragged k{presets[pr][0]}v{presets[pr][1]} L={cached[b]}+{R}", out, scores, q, b, h, G,
-                    fields[(b, h)], prms[pr], int(cached[b]),
-                    rk=rk32[b, h:h + 1, :R].astype(np.float64), rv=rv32[b, h:h + 1, :R].astype(np.float64))
+    # the window's scores follow each sequence's cached tokens (columns L .. L+R-1)
+    _check_all_pairs("ragged k3v2|k4v4 + bf16 window", [p.cpu().numpy() for p in pools],
+                     [paged.layout(d, kb, vb) for kb, vb in presets], prms, bt_np, cached, q, G, out, scores,
+                     seq_preset=seq_preset, rk=rk32, rv=rv32, rlens=rlens)
     for c in ctxs:
         c.close()

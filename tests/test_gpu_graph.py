@@ -11,12 +11,14 @@ current inputs.  Both launch shapes are covered: one split per sequence
 (direct output) and several splits with the combine launch, with one preset
 and with two (one split launch per preset, both captured).
 
-The kernel's waves claim cache steps dynamically, so two runs associate
-the fp32 sums differently: they agree to rounding, not bit for bit.  The
-outputs are averages of many values of both signs, so that rounding shows
-up amplified relative to their norm (~3e-5 measured with 4-bit values,
-~1e-4 with 2-bit ones); the bar is the parity tolerance, 1e-3 relative per
-row, which a stale replay (new queries) misses by orders of magnitude.
+By default the kernel's waves claim cache steps dynamically, so two runs
+associate the fp32 sums differently: they agree to rounding, not bit for
+bit.  The outputs are averages of many values of both signs, so that
+rounding shows up amplified relative to their norm (~3e-5 measured with
+4-bit values, ~1e-4 with 2-bit ones); the bar is then the parity tolerance,
+1e-3 relative per row, which a stale replay (new queries) misses by orders of
+magnitude.  With TQ_DECODE_DETERMINISTIC every replay must equal the eager
+run bit for bit.
 """
 
 import numpy as np
@@ -29,9 +31,10 @@ import synth
 pytestmark = pytest.mark.gpu
 
 
+@pytest.mark.parametrize("deterministic", [False, True])
 @pytest.mark.parametrize("two_presets", [False, True])
 @pytest.mark.parametrize("chunk", [8192, 256])
-def test_captured_decode_step_replays_match_eager(chunk, two_presets):
+def test_captured_decode_step_replays_match_eager(chunk, two_presets, deterministic):
     d, B, Hq, Hkv, L, kb, vb, seed = 128, 4, 8, 2, 1024, 3, 4, 160
     s1, s2, S = synth.method_params(seed, d)
     ctx = tq.tq_codebook_init(d, kb, vb, signs=np.stack([s1, s2]), S=S)
@@ -55,7 +58,7 @@ def test_captured_decode_step_replays_match_eager(chunk, two_presets):
     slot_new = (bt[:, (L - 1) // 16].long() * 16 + (L - 1) % 16).to(torch.int32).contiguous()
     # the new token of each preset's sequences goes to that preset's pool
     sel = [torch.tensor([b for b in range(B) if preset_of[b] == p], dtype=torch.long, device="cuda") for p in (0, 1)]
-    kw = {}
+    kw = {"deterministic": deterministic}
     if two_presets:
         kw["seq_preset"] = torch.tensor(preset_of, dtype=torch.int8, device="cuda")
     ctxs = [ctx, ctx2] if two_presets else [ctx]
@@ -98,9 +101,11 @@ def test_captured_decode_step_replays_match_eager(chunk, two_presets):
         g.replay()
         torch.cuda.synchronize()
         got = out.clone()
-        print(f"[graph chunk {chunk} presets {len(ctxs)}] replay {r}: max |replay - eager| = {float((got - ref).abs().max()):.3e}",
-              flush=True)
+        print(f"[graph chunk {chunk} presets {len(ctxs)} deterministic {deterministic}] replay {r}: "
+              f"max |replay - eager| = {float((got - ref).abs().max()):.3e}", flush=True)
         assert torch.isfinite(got).all()
+        if deterministic:
+            assert torch.equal(got, ref)
         # equal to rounding, not bit for bit (see the module docstring)
         err = ((got - ref).norm(dim=-1) / ref.norm(dim=-1)).max()
         assert float(err) <= 1e-3

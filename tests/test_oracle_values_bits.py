@@ -142,3 +142,32 @@ def test_value_bytes_are_stored_in_dword_columns():
     assert pool[0, 0, off + (0 * 16 + 3) * 4 + 0] == 0xA7
     assert pool[0, 0, off + (1 * 16 + 5) * 4 + 2] == 0x13
     assert np.count_nonzero(pool[0, 0, off:off + lay["vcodes"][1]]) == 2
+
+
+@pytest.mark.parametrize("d,bk,bv,qjl", [(128, 3, 4, True), (128, 4, 2, False), (256, 4, 4, True)])
+def test_reader_follows_the_block_table_and_stops_at_the_length(d, bk, bv, qjl):
+    """Tokens written through a permuted block table with a ragged length come
+    back in token order from read_tokens, and nothing of other heads or of
+    the unused slots of the last block leaks into the fields."""
+    rng = np.random.default_rng(77 + d + bk)
+    lay = paged.layout(d, bk, bv, qjl=qjl)
+    nb, Hkv, L = 9, 2, 37  # 3 blocks, the last one partial
+    pool = paged.new_pool(nb, Hkv, lay)
+    pool[:] = rng.integers(0, 256, pool.shape, dtype=np.uint8)  # garbage everywhere else
+    bt = rng.permutation(nb)[:3]
+    t = np.arange(L)
+    slots = bt[t // 16].astype(np.int64) * 16 + t % 16
+    ng = d // 32
+    kenc = {"idx": rng.integers(0, 1 << bk, (L, d)), "sign": rng.integers(0, 2, (L, d)).astype(np.uint8),
+            "n16": rng.integers(0, 1 << 15, L).astype(np.uint16), "g16": rng.integers(0, 1 << 15, L).astype(np.uint16)}
+    venc = {"q": rng.integers(0, 1 << bv, (L, d)), "s16": rng.integers(0, 1 << 15, (L, ng)).astype(np.uint16),
+            "z16": rng.integers(0, 1 << 16, (L, ng)).astype(np.uint16)}
+    paged.write_tokens(pool, slots, 1, kenc, venc, lay)
+    f = paged.read_tokens(pool, bt, L, 1, lay)
+    keys_ = ("idx", "sign", "n16", "g16") if qjl else ("idx", "n16")
+    for key in keys_:
+        assert f[key].shape[0] == L and np.array_equal(f[key], kenc[key]), key
+    for key in ("q", "s16", "z16"):
+        assert f[key].shape[0] == L and np.array_equal(f[key], venc[key]), key
+    if not qjl:
+        assert not f["sign"].any() and not f["g16"].any()
