@@ -5,17 +5,18 @@ A step is one decode step of the whole path on the decode workload (batch 32,
 32 query / 8 KV heads, head_dim 128, 8192 cached tokens per sequence,
 3-bit Lloyd-Max keys + 1-bit QJL, 4-bit group-32 values, paged through a
 permuted block table): tq_quantize_store of the step's new token for every
-sequence and KV head, then tq_decode_attention over the 8192 cached tokens.
-The step is captured once per cache copy in a HIP graph and replayed.
+sequence and KV head, then tq_decode_attention over the 8192 cached tokens,
+launched eagerly (the same step replayed from a HIP graph is reported beside
+it).
 
 Printed as ONE JSON line:
   value     = KV bytes the decode must read per step (every packed record byte
               of every cached token-head, 148 B each) / mean step time over
               the K timed steps, in TB/s;
   roofline  = the split kernel (the streaming kernel): median time of one
-              launch from graphs of back-to-back split-only launches, against
-              the 8 TB/s HBM peak;
-  workloads = the other workloads timed the same way (median of replays):
+              launch over back-to-back split-only launches, against the
+              8 TB/s HBM peak;
+  workloads = the other workloads timed the same way (median of launches):
               the long-context d=256 decode, the ragged mixed-preset decode
               with a bf16 window, the quantise workload (65536 new bf16
               tokens x 8 KV heads, K3V4 and K3V2), MSE-only keys, and the
@@ -41,7 +42,6 @@ sys.path.insert(0, ROOT)
 METRIC = "TQ decode attn: KV-bytes TB/s (% HBM peak) + tokens/s; quantize Mtok/s"
 HBM_PEAK_TBS = 8.0
 REC_BYTES_K3V4 = 148  # per token-head: 48 code + 16 sign + 4 meta + 64 value + 16 value-meta bytes
-SPLIT_LAUNCHES_PER_GRAPH = 6
 
 
 def _kernel_source_sha():
@@ -105,20 +105,6 @@ def time_total(torch, graphs, reps):
     return e0.elapsed_time(e1) / reps
 
 
-def time_each(torch, graphs, reps):
-    """ms of every replay, each bracketed by its own event pair on the stream
-    the graph is launched on (the host runs ahead of the GPU, so the events do
-    not wait for the host)."""
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    torch.cuda.synchronize()
-    for i in range(reps):
-        evs[i][0].record()
-        graphs[i % len(graphs)].replay()
-        evs[i][1].record()
-    torch.cuda.synchronize()
-    return [a.elapsed_time(b) for a, b in evs]
-
-
 # --------------------------------------------------------- decode workload --
 def setup_decode(torch, tq, synth, chunk, copies, mse_only=False):
     d, B, Hq, Hkv, L, kb, vb, nb, seed = 128, 32, 32, 8, 8192, 3, 4, 16384, 3
@@ -162,63 +148,66 @@ def decode_step(tq, s, i):
     decode_only(tq, s, i)
 
 
-def split_graphs(torch, tq, s, deterministic=False):
-    """One graph per pool copy, each with SPLIT_LAUNCHES_PER_GRAPH back-to-back
-    decode launches over the copies in turn (no store between them)."""
-    n = len(s["pools"])
-
-    def make(j):
-        def fn():
-            for k in range(SPLIT_LAUNCHES_PER_GRAPH):
-                decode_only(tq, s, j + k, deterministic)
-        return fn
-
-    return [capture(torch, make(j)) for j in range(n)]
+def time_eager(torch, fn, reps):
+    """Eager launches of ``fn`` (one step each): the mean over ``reps``
+    back-to-back steps between two events and two synchronisations, then the
+    median of a second pass with an event between consecutive steps (the
+    host enqueues ahead of the GPU, so an event marks where one step's
+    kernels end and the next one's begin)."""
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    mean = e0.elapsed_time(e1) / reps
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    torch.cuda.synchronize()
+    evs[0].record()
+    for i in range(reps):
+        fn(i)
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    each = [evs[i].elapsed_time(evs[i + 1]) for i in range(reps)]
+    return mean, each
 
 
 def time_decode(torch, tq, s, steps, warmup):
-    """Step timing (graph replays of store + decode; mean over exactly
-    ``steps`` steps, and the median of per-step events in a second pass), the
-    eager step for comparison, and the split kernel's median launch time."""
+    """The step (store + decode, eager launches): mean over exactly ``steps``
+    steps and the median step; the same step replayed from HIP graphs for
+    comparison; the split kernel's median launch time from back-to-back
+    decode-only launches."""
     for i in range(warmup):
         decode_step(tq, s, i)
     torch.cuda.synchronize()
+    # the timed region: exactly `steps` steps between two synchronisations
+    ms_step, each = time_eager(torch, lambda i: decode_step(tq, s, i), steps)
     n = len(s["pools"])
     step_graphs = [capture(torch, (lambda j: (lambda: decode_step(tq, s, j)))(j)) for j in range(n)]
     for g in step_graphs * 2:
         g.replay()
-    # the timed region: exactly `steps` steps between two synchronisations
-    ms_step = time_total(torch, step_graphs, steps)
-    med_step = _median(time_each(torch, step_graphs, steps))
-    # eager launches of the same step (host-paced launch gaps included)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        decode_step(tq, s, i)
-    torch.cuda.synchronize()
-    eager_ms = (time.perf_counter() - t0) * 1e3 / steps
-    sg = split_graphs(torch, tq, s)
-    for g in sg:
-        g.replay()
-    reps = max(10, steps // 2)
-    per = [t / SPLIT_LAUNCHES_PER_GRAPH for t in time_each(torch, sg, reps)]
-    del step_graphs, sg
-    return {"ms_per_step": ms_step, "median_ms_per_step": med_step, "eager_ms_per_step": eager_ms,
-            "split_median_ms": _median(per), "split_min_ms": min(per), "split_max_ms": max(per)}
+    graph_ms = time_total(torch, step_graphs, steps)
+    del step_graphs
+    for i in range(warmup):
+        decode_only(tq, s, i)
+    split_mean, split_each = time_eager(torch, lambda i: decode_only(tq, s, i), steps)
+    return {"ms_per_step": ms_step, "median_ms_per_step": _median(each), "graph_ms_per_step": graph_ms,
+            "split_mean_ms": split_mean, "split_median_ms": _median(split_each), "split_min_ms": min(split_each),
+            "split_max_ms": max(split_each)}
 
 
 def time_split_deterministic(torch, tq, s, steps):
-    sg = split_graphs(torch, tq, s, deterministic=True)
-    for g in sg:
-        g.replay()
-    per = [t / SPLIT_LAUNCHES_PER_GRAPH for t in time_each(torch, sg, max(10, steps // 2))]
+    for i in range(3):
+        decode_only(tq, s, i, deterministic=True)
+    _, each = time_eager(torch, lambda i: decode_only(tq, s, i, deterministic=True), steps)
     # repeated launches give bit-identical outputs on this schedule
     outs = []
     for i in range(2):
         decode_only(tq, s, 0, deterministic=True)
         torch.cuda.synchronize()
         outs.append(s["out"].clone())
-    return _median(per), bool(torch.equal(outs[0], outs[1]))
+    return _median(each), bool(torch.equal(outs[0], outs[1]))
 
 
 # ----------------------------------------------------- long / ragged decode --
@@ -307,10 +296,10 @@ def setup_ragged(torch, tq, synth):
 
 
 def time_workload(torch, w, reps):
-    g = capture(torch, w["fn"])
-    g.replay()
-    ms = _median(time_each(torch, [g], reps))
-    del g
+    for _ in range(3):
+        w["fn"]()
+    _, each = time_eager(torch, lambda i: w["fn"](), reps)
+    ms = _median(each)
     tbs = w["kv_bytes"] / (ms * 1e-3) / 1e12
     res = {"workload": w["workload"], "kv_bytes_per_call": w["kv_bytes"], "median_ms": round(ms, 5),
            "tbs": round(tbs, 4), "hbm_frac": round(tbs / HBM_PEAK_TBS, 4),
@@ -335,20 +324,21 @@ def bench_quantize(torch, tq, synth, reps):
     for kb, vb in ((3, 4), (3, 2)):
         ctx = tq.tq_codebook_init(d, kb, vb, signs=np.stack([signs1, signs2]), S=S)
         pool = torch.zeros((nb, Hkv, ctx.block_bytes), dtype=torch.uint8, device="cuda")
-        gs = [capture(torch, (lambda c: (lambda: tq.tq_quantize_store(ctx, ks[c], vs[c], slots, pool)))(c))
-              for c in range(copies)]
-        ms = _median(time_each(torch, gs, reps))
+        fn = lambda i: tq.tq_quantize_store(ctx, ks[i % copies], vs[i % copies], slots, pool)  # noqa: E731
+        for i in range(3):
+            fn(i)
+        _, each = time_eager(torch, fn, reps)
+        ms = _median(each)
         hbm = T * Hkv * (2 * d * 2 + ctx.block_bytes // 16) + T * 4
         res[f"k{kb}v{vb}"] = {"median_ms": round(ms, 5), "mtok_per_s": round(T / ms / 1e3, 2),
                               "hbm_bytes": hbm, "hbm_tbs": round(hbm / ms / 1e9, 3),
                               "hbm_frac": round(hbm / ms / 1e9 / HBM_PEAK_TBS, 4)}
-        del gs
         ctx.close()
     return {"workload": "quantize-65536tok-hkv8-d128-bf16-outliers0.5%x20", **res}
 
 
 # --------------------------------------------------------------- oracle --
-def cpu_baseline(synth, seqs=24, quant_tokens=2048):
+def cpu_baseline(synth, seqs=32, quant_tokens=16384):
     """The oracle on bounded samples: its decode of ``seqs`` sequences of the
     decode workload (cache encoded by the oracle first, not timed), and its
     encoding of ``quant_tokens`` tokens x 8 KV heads of the quantise workload."""
@@ -365,13 +355,18 @@ def cpu_baseline(synth, seqs=24, quant_tokens=2048):
     lay = paged.layout(d, kb, vb)
     bt = synth.block_table(seed, seqs, L // 16, seqs * L // 16)
     pool = paged.new_pool(seqs * L // 16, Hkv, lay)
-    for b in range(seqs):
-        for h in range(Hkv):
-            K, V = synth.seq_kv(seed, b, h, L, d)
-            ke = keys.encode_keys(K.astype(np.float64), prm["d1"], prm["d2"], S, c32, t32)
-            ve = values.encode_values(V, vb)
-            tt = np.arange(L)
-            paged.write_tokens(pool, bt[b][tt // 16].astype(np.int64) * 16 + tt % 16, h, ke, ve, lay)
+
+    def encode(i):  # untimed set-up: the oracle writes the cache (disjoint records per (b, h))
+        b, h = divmod(i, Hkv)
+        K, V = synth.seq_kv(seed, b, h, L, d)
+        ke = keys.encode_keys(K.astype(np.float64), prm["d1"], prm["d2"], S, c32, t32)
+        ve = values.encode_values(V, vb)
+        tt = np.arange(L)
+        paged.write_tokens(pool, bt[b][tt // 16].astype(np.int64) * 16 + tt % 16, h, ke, ve, lay)
+
+    from concurrent.futures import ThreadPoolExecutor
+    with threadpool_limits(limits=1), ThreadPoolExecutor(max_workers=min(16, cores)) as ex:
+        list(ex.map(encode, range(seqs * Hkv)))
     q = synth.queries(seed, seqs, Hq, d)
     with threadpool_limits(limits=cores):
         t0 = time.perf_counter()
@@ -395,7 +390,8 @@ def cpu_baseline(synth, seqs=24, quant_tokens=2048):
     kv = seqs * Hkv * L * REC_BYTES_K3V4
     return {"value": kv / dt / 1e12, "unit": "TB/s", "cores": cores, "kind": "oracle",
             "sample": f"{seqs} of the 32 sequences of the decode workload (all 8 KV heads x 8192 tokens, "
-                      f"32 query heads), oracle decode from an oracle-written pool: {dt:.2f} s, "
+                      f"32 query heads; the oracle reads the records back from an oracle-written pool and "
+                      f"decodes them, one sequence at a time): {dt:.2f} s, "
                       f"{seqs / dt:.3f} sequences/s; BLAS threads = cores, numpy elementwise work single-threaded",
             "decode_tokens_per_s": seqs / dt,
             "quantize": {"mtok_per_s": quant_tokens / dq / 1e6, "seconds": dq,
@@ -436,8 +432,9 @@ def main():
     value = s["kv_bytes"] / (ms_step * 1e-3) / 1e12
     split_ms = dec["split_median_ms"]
     achieved = s["kv_bytes"] / (split_ms * 1e-3) / 1e9
-    log(f"decode step {ms_step * 1e3:.1f} us (median {dec['median_ms_per_step'] * 1e3:.1f}, eager "
-        f"{dec['eager_ms_per_step'] * 1e3:.1f}), split kernel median {split_ms * 1e3:.1f} us")
+    log(f"decode step {ms_step * 1e3:.1f} us (median {dec['median_ms_per_step'] * 1e3:.1f}, graph replay "
+        f"{dec['graph_ms_per_step'] * 1e3:.1f}), split kernel median {split_ms * 1e3:.1f} us "
+        f"(mean {dec['split_mean_ms'] * 1e3:.1f})")
     det_ms, det_equal = time_split_deterministic(torch, tq, s, args.steps)
     log(f"deterministic split median {det_ms * 1e3:.1f} us, repeat bit-identical: {det_equal}")
     for p in s["pools"]:
@@ -491,21 +488,21 @@ def main():
         "vs_baseline": None,
         "dtype": "f32acc-bf16x2",
         "data": "synthetic",
-        "config": {"workload": "decode-b32-hq32-hkv8-d128-ctx8192-k3v4: store 1 new token + attend 8192 "
-                               "(HIP graph per step)",
+        "config": {"workload": "decode-b32-hq32-hkv8-d128-ctx8192-k3v4: store 1 new token + attend 8192",
                    "batch": 32, "q_heads": 32, "kv_heads": 8, "head_dim": 128, "context": 8192,
                    "k_bits": 3, "v_bits": 4, "chunk_tokens": args.chunk, "pool_copies": 3},
         "hbm_frac": round(value / HBM_PEAK_TBS, 4),
         "decode_tokens_per_s": round(32 / (ms_step * 1e-3), 1),
         "kv_bytes_per_step": kv_bytes,
         "median_ms_per_step": round(dec["median_ms_per_step"], 5),
-        "eager_ms_per_step": round(dec["eager_ms_per_step"], 5),
+        "graph_replay_ms_per_step": round(dec["graph_ms_per_step"], 5),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_TBS * 1000, "unit": "GB/s",
                      "frac": round(achieved / (HBM_PEAK_TBS * 1000), 4), "traffic": traffic,
                      "kernel": "decode_split_kernel<128,4,3,4,true>", "bytes_per_launch": kv_bytes,
-                     "median_launch_ms": round(split_ms, 5), "min_launch_ms": round(dec["split_min_ms"], 5),
-                     "timing": f"median over replays of graphs of {SPLIT_LAUNCHES_PER_GRAPH} back-to-back "
-                               f"split-only launches (3 pool copies in turn)",
+                     "median_launch_ms": round(split_ms, 5), "mean_launch_ms": round(dec["split_mean_ms"], 5),
+                     "min_launch_ms": round(dec["split_min_ms"], 5),
+                     "timing": "median of per-launch event intervals over back-to-back eager split-only "
+                               "launches (3 pool copies in turn), events recorded between the library calls",
                      "consistent_with_step": bool(split_ms <= ms_step and achieved >= kv_bytes / (ms_step * 1e-3) / 1e9)},
         "workloads": workloads,
         "cpu_baseline": cpu,
