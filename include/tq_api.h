@@ -259,6 +259,23 @@ size_t tq_decode_workspace_bytes(const tq_decode_args* args);
  * anything is enqueued. */
 int tq_decode_attention(const tq_decode_args* args, void* stream);
 
+/* ------------------------------------------------- decode, no allocation --
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, validation and results as tq_decode_attention, except that
+ * args->workspace and args->workspace_bytes are ignored: the split partials
+ * go to a scratch array of TQ_NOALLOC_SCRATCH_BYTES bytes that the library
+ * holds in device memory (one per GPU, reserved with the library's code
+ * object and kept until the process ends).  A call whose partials need more
+ * than that (tq_decode_workspace_bytes(args) > TQ_NOALLOC_SCRATCH_BYTES) is
+ * rejected with TQ_EINVAL before anything is enqueued.  Nothing is allocated,
+ * freed or cleared: every partial is written before it is read.  Calls on one
+ * GPU share its scratch array, so calls whose launches overlap (two streams,
+ * or two host threads, on the same device) race and may corrupt each other's
+ * outputs; serialise them on one stream. */
+#define TQ_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int tq_decode_attention_noalloc(const tq_decode_args* args, void* stream);
+
 /* Thread-local message of the last failure ("" if none). */
 const char* tq_last_error(void);
 

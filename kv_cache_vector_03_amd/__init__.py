@@ -17,7 +17,8 @@ __all__ = [
     "TQ_PRESET_UNIFORM", "TQ_PRESET_ROTATE_V", "TQ_DECODE_DETERMINISTIC", "tq_uniform_codebook", "tq_fold_output_projection",
     "TqError", "Context", "library_path", "load", "tq_codebook_init", "tq_ctx_destroy", "tq_ctx_tables",
     "tq_lloyd_max", "tq_record_layout", "tq_draw_params", "tq_block_bytes", "tq_quantize_store",
-    "tq_decode_workspace_bytes", "tq_decode_attention", "tq_last_error", "EXPORTED_SYMBOLS",
+    "tq_decode_workspace_bytes", "tq_decode_attention", "tq_decode_attention_noalloc", "NOALLOC_SCRATCH_BYTES",
+    "tq_last_error", "EXPORTED_SYMBOLS",
 ]
 
 TQ_OK, TQ_EINVAL, TQ_EUNSUPPORTED, TQ_EHIP, TQ_ENOMEM = 0, -1, -2, -3, -4
@@ -26,12 +27,13 @@ TQ_PRESET_MSE_ONLY = 1
 TQ_PRESET_UNIFORM = 2
 TQ_PRESET_ROTATE_V = 4
 TQ_DECODE_DETERMINISTIC = 1
+NOALLOC_SCRATCH_BYTES = 32 << 20  # TQ_NOALLOC_SCRATCH_BYTES of include/tq_api.h
 
 EXPORTED_SYMBOLS = [
     "tq_codebook_init", "tq_ctx_destroy", "tq_ctx_tables", "tq_ctx_preset", "tq_lloyd_max", "tq_uniform_codebook",
     "tq_record_layout", "tq_fold_output_projection",
     "tq_draw_params", "tq_block_bytes", "tq_quantize_store", "tq_decode_workspace_bytes", "tq_decode_attention",
-    "tq_last_error",
+    "tq_decode_attention_noalloc", "tq_last_error",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -98,6 +100,7 @@ def load(path: str | None = None):
         "tq_quantize_store": (c.c_int, [P, P, P, c.c_int32, c.c_int64, c.c_int32, P, P, c.c_int64, P]),
         "tq_decode_workspace_bytes": (c.c_size_t, [c.POINTER(tq_decode_args)]),
         "tq_decode_attention": (c.c_int, [c.POINTER(tq_decode_args), P]),
+        "tq_decode_attention_noalloc": (c.c_int, [c.POINTER(tq_decode_args), P]),
         "tq_last_error": (c.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -387,3 +390,12 @@ def tq_decode_attention(q, ctxs, pools, block_tables, seq_lens, out, workspace, 
     step order per wave: bit-identical outputs run to run)."""
     a = _decode_args(q, ctxs, pools, block_tables, seq_lens, out, workspace, **kw)
     _check(load().tq_decode_attention(ctypes.byref(a), _stream(stream)), "tq_decode_attention")
+
+
+def tq_decode_attention_noalloc(q, ctxs, pools, block_tables, seq_lens, out, stream=None, **kw) -> None:
+    """tq_decode_attention without a workspace argument: the split partials go
+    to the library's static device scratch (NOALLOC_SCRATCH_BYTES per GPU),
+    so the call allocates nothing.  Calls on one GPU share that scratch:
+    keep them on one stream."""
+    a = _decode_args(q, ctxs, pools, block_tables, seq_lens, out, None, check_workspace=False, **kw)
+    _check(load().tq_decode_attention_noalloc(ctypes.byref(a), _stream(stream)), "tq_decode_attention_noalloc")

@@ -1396,6 +1396,31 @@ static DArgs make_dargs(const tq_decode_args* args, const DecodePlan& plan) {
   return a;
 }
 
+// Split partials of tq_decode_attention_noalloc: a file-scope device array
+// (each GPU holds its own copy at its own address until the process ends).
+// Host code never uses the array's name as an address: the per-device
+// address comes from hipGetSymbolAddress, with that device current.
+static __device__ __align__(256) unsigned char scratch[TQ_NOALLOC_SCRATCH_BYTES];
+
+hipError_t noalloc_scratch(void** out) {
+  static std::mutex mu;
+  static void* addr[16] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 16) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
+
 hipError_t check_decode_launch(const tq_decode_args* args, const DecodePlan& plan) {
   const DArgs a = make_dargs(args, plan);
   return plan.d == 128 ? launch_all<128>(a, args, nullptr, true) : launch_all<256>(a, args, nullptr, true);

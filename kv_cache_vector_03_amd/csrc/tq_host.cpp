@@ -604,37 +604,62 @@ extern "C" size_t tq_decode_workspace_bytes(const tq_decode_args* a) {
   return plan_decode(a).bytes;
 }
 
-extern "C" int tq_decode_attention(const tq_decode_args* a, void* stream) {
+// Shared by tq_decode_attention and tq_decode_attention_noalloc; with
+// noalloc the workspace fields are ignored and the library's static scratch
+// array takes their place.
+static int decode_entry(const tq_decode_args* a, void* stream, bool noalloc) {
+  const char* who = noalloc ? "tq_decode_attention_noalloc" : "tq_decode_attention";
   int rc = check_decode_shape(a);
   if (rc) return rc;
   if (a->batch == 0) return TQ_OK;
   if (!a->q || !a->block_tables || !a->seq_lens || !a->out || !a->pool[0] || (a->num_presets == 2 && !a->pool[1])) {
-    set_error("decode: NULL device pointer");
+    set_error("%s: NULL device pointer", who);
     return TQ_EINVAL;
   }
   if (a->q_dtype != TQ_DTYPE_BF16 && a->q_dtype != TQ_DTYPE_F32) {
-    set_error("decode: q_dtype %d invalid", a->q_dtype);
+    set_error("%s: q_dtype %d invalid", who, a->q_dtype);
     return TQ_EINVAL;
   }
   if (((uintptr_t)a->pool[0] | (uintptr_t)a->pool[1] | (uintptr_t)a->q) & 15) {
-    set_error("decode: q and pools must be 16-byte aligned");
+    set_error("%s: q and pools must be 16-byte aligned", who);
     return TQ_EINVAL;
   }
   if (a->scores_out && a->scores_stride < a->max_seq_len + (a->recent_k ? a->recent_window : 0)) {
-    set_error("decode: scores_stride %d too small", a->scores_stride);
+    set_error("%s: scores_stride %d too small", who, a->scores_stride);
     return TQ_EINVAL;
   }
   DecodePlan plan = plan_decode(a);
-  if (!a->workspace || a->workspace_bytes < plan.bytes || ((uintptr_t)a->workspace & 255)) {
+  tq_decode_args args = *a;
+  if (noalloc) {
+    if (plan.bytes > TQ_NOALLOC_SCRATCH_BYTES) {
+      set_error("%s: the split partials need %zu bytes, above the %zu-byte static scratch", who, plan.bytes,
+                (size_t)TQ_NOALLOC_SCRATCH_BYTES);
+      return TQ_EINVAL;
+    }
+    void* p = nullptr;
+    hipError_t e = noalloc_scratch(&p);
+    if (e != hipSuccess) {
+      set_error("%s: hipGetSymbolAddress of the scratch array failed: %s", who, hipGetErrorString(e));
+      return TQ_EHIP;
+    }
+    args.workspace = p;
+    args.workspace_bytes = TQ_NOALLOC_SCRATCH_BYTES;
+  } else if (!a->workspace || a->workspace_bytes < plan.bytes || ((uintptr_t)a->workspace & 255)) {
     set_error("decode: workspace must be 256-byte aligned and hold %zu bytes (got %zu)", plan.bytes,
               a->workspace_bytes);
     return TQ_EINVAL;
   }
-  if (check_decode_launch(a, plan) != hipSuccess) return TQ_EINVAL;  // message set by the check
-  hipError_t e = launch_decode(a, plan, (hipStream_t)stream);
+  if (check_decode_launch(&args, plan) != hipSuccess) return TQ_EINVAL;  // message set by the check
+  hipError_t e = launch_decode(&args, plan, (hipStream_t)stream);
   if (e != hipSuccess) {
-    set_error("decode: launch failed: %s", hipGetErrorString(e));
+    set_error("%s: launch failed: %s", who, hipGetErrorString(e));
     return TQ_EHIP;
   }
   return TQ_OK;
+}
+
+extern "C" int tq_decode_attention(const tq_decode_args* a, void* stream) { return decode_entry(a, stream, false); }
+
+extern "C" int tq_decode_attention_noalloc(const tq_decode_args* a, void* stream) {
+  return decode_entry(a, stream, true);
 }

@@ -75,5 +75,8 @@ hipError_t launch_decode(const tq_decode_args* a, const DecodePlan& plan, hipStr
 // the recent window beside the kernel's own tables); on failure the message is
 // set with set_error and an error is returned.  Enqueues nothing.
 hipError_t check_decode_launch(const tq_decode_args* a, const DecodePlan& plan);
+// Device address of the current device's static scratch array of
+// TQ_NOALLOC_SCRATCH_BYTES bytes (looked up once per device, then cached).
+hipError_t noalloc_scratch(void** out);
 
 }  // namespace tq
