@@ -136,16 +136,34 @@ def setup_decode(torch, tq, synth, chunk, copies, mse_only=False):
                 units=B * Hkv * L)
 
 
+def _prepared(tq, s):
+    """Prepared (validated-once) store and decode calls per pool copy: the
+    timed loop's host cost per launch is one ctypes call, so the launches
+    queue up ahead of the GPU."""
+    if "prep" not in s:
+        s["prep"] = {det: [tq.PreparedDecode(s["q"], [s["ctx"]], [p], s["bt"], s["lens"], s["out"], s["ws"],
+                                             chunk_tokens=s["chunk"], max_seq_len=s["L"], deterministic=det)
+                           for p in s["pools"]] for det in (False, True)}
+        s["prep_store"] = [tq.PreparedQuantize(s["ctx"], s["knew"], s["vnew"], s["slot_new"], p) for p in s["pools"]]
+    return s
+
+
 def decode_only(tq, s, i, deterministic=False):
-    pool = s["pools"][i % len(s["pools"])]
-    tq.tq_decode_attention(s["q"], [s["ctx"]], [pool], s["bt"], s["lens"], s["out"], s["ws"],
-                           chunk_tokens=s["chunk"], max_seq_len=s["L"], deterministic=deterministic)
+    _prepared(tq, s)["prep"][deterministic][i % len(s["pools"])]()
 
 
 def decode_step(tq, s, i):
+    _prepared(tq, s)["prep_store"][i % len(s["pools"])]()
+    decode_only(tq, s, i)
+
+
+def decode_step_current_stream(tq, s, i):
+    """The same step through the plain calls, which launch on torch's current
+    stream (the form a HIP graph capture records)."""
     pool = s["pools"][i % len(s["pools"])]
     tq.tq_quantize_store(s["ctx"], s["knew"], s["vnew"], s["slot_new"], pool)
-    decode_only(tq, s, i)
+    tq.tq_decode_attention(s["q"], [s["ctx"]], [pool], s["bt"], s["lens"], s["out"], s["ws"],
+                           chunk_tokens=s["chunk"], max_seq_len=s["L"])
 
 
 def time_eager(torch, fn, reps):
@@ -184,7 +202,7 @@ def time_decode(torch, tq, s, steps, warmup):
     # the timed region: exactly `steps` steps between two synchronisations
     ms_step, each = time_eager(torch, lambda i: decode_step(tq, s, i), steps)
     n = len(s["pools"])
-    step_graphs = [capture(torch, (lambda j: (lambda: decode_step(tq, s, j)))(j)) for j in range(n)]
+    step_graphs = [capture(torch, (lambda j: (lambda: decode_step_current_stream(tq, s, j)))(j)) for j in range(n)]
     for g in step_graphs * 2:
         g.replay()
     graph_ms = time_total(torch, step_graphs, steps)
@@ -234,7 +252,7 @@ def setup_long(torch, tq, synth):
     ws = torch.empty(tq.tq_decode_workspace_bytes(q, [ctx], [pool], bt, lens, out, **kw), dtype=torch.uint8,
                      device="cuda")
     torch.cuda.synchronize()
-    fn = lambda: tq.tq_decode_attention(q, [ctx], [pool], bt, lens, out, ws, **kw)  # noqa: E731
+    fn = tq.PreparedDecode(q, [ctx], [pool], bt, lens, out, ws, **kw)
     return dict(keep=[ctx, bt, pool, q, lens, out, ws], fn=fn, B=B,
                 kv_bytes=B * Hkv * L * (ctx.block_bytes // 16),
                 workload="decode-b8-hq16-hkv4-d256-ctx131072-k4v4", chunk_tokens=8192)
@@ -287,7 +305,7 @@ def setup_ragged(torch, tq, synth):
     ws = torch.empty(tq.tq_decode_workspace_bytes(q, ctxs, pools, bt, lens, out, **kw), dtype=torch.uint8,
                      device="cuda")
     torch.cuda.synchronize()
-    fn = lambda: tq.tq_decode_attention(q, ctxs, pools, bt, lens, out, ws, **kw)  # noqa: E731
+    fn = tq.PreparedDecode(q, ctxs, pools, bt, lens, out, ws, **kw)
     rec = [ctxs[p].block_bytes // 16 for p in range(2)]
     kv = int(sum(Hkv * (int(cached[b]) * rec[seq_preset[b]] + int(rlens[b]) * 2 * d * 2) for b in range(B)))
     return dict(keep=[ctxs, bt, pools, rk, rv, q, lens, out, ws, kw], fn=fn, B=B, kv_bytes=kv,
@@ -324,7 +342,8 @@ def bench_quantize(torch, tq, synth, reps):
     for kb, vb in ((3, 4), (3, 2)):
         ctx = tq.tq_codebook_init(d, kb, vb, signs=np.stack([signs1, signs2]), S=S)
         pool = torch.zeros((nb, Hkv, ctx.block_bytes), dtype=torch.uint8, device="cuda")
-        fn = lambda i: tq.tq_quantize_store(ctx, ks[i % copies], vs[i % copies], slots, pool)  # noqa: E731
+        prep = [tq.PreparedQuantize(ctx, ks[c], vs[c], slots, pool) for c in range(copies)]
+        fn = lambda i: prep[i % copies]()  # noqa: E731
         for i in range(3):
             fn(i)
         _, each = time_eager(torch, fn, reps)

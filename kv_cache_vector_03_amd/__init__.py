@@ -18,6 +18,7 @@ __all__ = [
     "TqError", "Context", "library_path", "load", "tq_codebook_init", "tq_ctx_destroy", "tq_ctx_tables",
     "tq_lloyd_max", "tq_record_layout", "tq_draw_params", "tq_block_bytes", "tq_quantize_store",
     "tq_decode_workspace_bytes", "tq_decode_attention", "tq_decode_attention_noalloc", "NOALLOC_SCRATCH_BYTES",
+    "PreparedDecode", "PreparedQuantize",
     "tq_last_error", "EXPORTED_SYMBOLS",
 ]
 
@@ -262,7 +263,16 @@ def tq_block_bytes(ctx: Context) -> int:
 def tq_quantize_store(ctx: Context, k, v, slot_mapping, pool, stream=None) -> None:
     """k, v: device tensors [T, Hkv, d] (bf16 or f32, same dtype);
     slot_mapping: device int32 [T]; pool: device uint8 [num_blocks, Hkv, record]."""
+    _check(load().tq_quantize_store(*_quantize_args(ctx, k, v, slot_mapping, pool), _stream(stream)),
+           "tq_quantize_store")
+
+
+def _quantize_args(ctx, k, v, slot_mapping, pool):
     import torch
+    _check_dev("k", k)
+    _check_dev("v", v)
+    _check_dev("slot_mapping", slot_mapping)
+    _check_dev("pool", pool)
     if k.shape != v.shape or k.dtype != v.dtype or k.dim() != 3:
         raise ValueError("k and v must be [T, Hkv, d] tensors of one dtype")
     if slot_mapping.dtype != torch.int32 or pool.dtype != torch.uint8:
@@ -274,8 +284,7 @@ def tq_quantize_store(ctx: Context, k, v, slot_mapping, pool, stream=None) -> No
         raise ValueError("shape mismatch between k/v, pool and context")
     if slot_mapping.numel() != T:
         raise ValueError("slot_mapping must have one entry per token")
-    _check(load().tq_quantize_store(ctx.handle, _ptr(k), _ptr(v), _dtype_code(k), T, Hkv, _ptr(slot_mapping),
-                                    _ptr(pool), pool.shape[0], _stream(stream)), "tq_quantize_store")
+    return (ctx.handle, _ptr(k), _ptr(v), _dtype_code(k), T, Hkv, _ptr(slot_mapping), _ptr(pool), pool.shape[0])
 
 
 def _need(cond, msg):
@@ -399,3 +408,39 @@ def tq_decode_attention_noalloc(q, ctxs, pools, block_tables, seq_lens, out, str
     keep them on one stream."""
     a = _decode_args(q, ctxs, pools, block_tables, seq_lens, out, None, check_workspace=False, **kw)
     _check(load().tq_decode_attention_noalloc(ctypes.byref(a), _stream(stream)), "tq_decode_attention_noalloc")
+
+
+class PreparedDecode:
+    """A decode call validated and marshalled once, launched many times (the
+    serving loop's form of tq_decode_attention: the per-launch host cost is
+    one ctypes call).  The tensors' storage is captured, so their contents may
+    change between launches but they must stay allocated and in place; ``ctxs``
+    must stay open.  ``noalloc=True`` launches tq_decode_attention_noalloc
+    (then no workspace is passed)."""
+
+    def __init__(self, q, ctxs, pools, block_tables, seq_lens, out, workspace=None, stream=None, noalloc=False, **kw):
+        self._args = _decode_args(q, ctxs, pools, block_tables, seq_lens, out, workspace,
+                                  check_workspace=not noalloc, **kw)
+        self._keep = (q, list(ctxs), list(pools), block_tables, seq_lens, out, workspace, dict(kw))
+        self._stream = _stream(stream)
+        lib = load()
+        self._fn = lib.tq_decode_attention_noalloc if noalloc else lib.tq_decode_attention
+        self._name = "tq_decode_attention_noalloc" if noalloc else "tq_decode_attention"
+        self._ref = ctypes.byref(self._args)
+
+    def __call__(self) -> None:
+        _check(self._fn(self._ref, self._stream), self._name)
+
+
+class PreparedQuantize:
+    """A tq_quantize_store call validated and marshalled once, launched many
+    times (same storage rules as PreparedDecode)."""
+
+    def __init__(self, ctx: Context, k, v, slot_mapping, pool, stream=None):
+        self._a = _quantize_args(ctx, k, v, slot_mapping, pool)
+        self._keep = (ctx, k, v, slot_mapping, pool)
+        self._stream = _stream(stream)
+        self._fn = load().tq_quantize_store
+
+    def __call__(self) -> None:
+        _check(self._fn(*self._a, self._stream), "tq_quantize_store")

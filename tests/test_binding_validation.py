@@ -101,3 +101,34 @@ def test_two_presets_need_int8_seq_preset(on_device):
     kw["seq_preset"] = torch.zeros(2, dtype=torch.int32)
     with pytest.raises(ValueError):
         _call(kw)
+
+
+def test_prepared_decode_validates_once_and_keeps_its_tensors(on_device, monkeypatch):
+    """PreparedDecode marshals (and validates) at construction; launching it
+    only calls the library with the stored argument struct."""
+    calls = []
+
+    class _Lib:
+        def tq_decode_attention(self, ref, stream):
+            calls.append(("ws", stream))
+            return tq.TQ_OK
+
+        def tq_decode_attention_noalloc(self, ref, stream):
+            calls.append(("noalloc", stream))
+            return tq.TQ_OK
+
+    monkeypatch.setattr(tq, "load", lambda path=None: _Lib())
+    kw = _valid()
+    q = kw.pop("q")
+    ctxs, pools, bt, lens, out = kw.pop("ctxs"), kw.pop("pools"), kw.pop("block_tables"), kw.pop("seq_lens"), kw.pop("out")
+    ws = kw.pop("workspace")
+    p = tq.PreparedDecode(q, ctxs, pools, bt, lens, out, ws, stream=7, **kw)
+    p()
+    p()
+    assert calls == [("ws", 7), ("ws", 7)]
+    assert p._args.q == q.data_ptr() and p._args.workspace == ws.data_ptr()
+    pn = tq.PreparedDecode(q, ctxs, pools, bt, lens, out, stream=9, noalloc=True, **kw)
+    pn()
+    assert calls[-1] == ("noalloc", 9) and not pn._args.workspace
+    with pytest.raises(ValueError):
+        tq.PreparedDecode(q, ctxs, pools, bt, lens, out, None, stream=7, **kw)  # workspace required
