@@ -23,7 +23,7 @@ from . import keys as _keys
 from . import rotation as _rot
 from . import values as _values
 
-__all__ = ["decode_one_sequence", "softmax_attend", "fold_output_projection"]
+__all__ = ["decode_one_sequence", "extend_one_sequence", "softmax_attend", "fold_output_projection"]
 
 
 def softmax_attend(logits, values) -> np.ndarray:
@@ -73,6 +73,50 @@ def decode_one_sequence(q, fields_per_head, ctx, recent_k=None, recent_v=None, s
             outs.append(softmax_attend(scale * s_all, v_all))
             scores.append(s_all)
     return np.stack(outs), np.stack(scores)
+
+
+def extend_one_sequence(q, fields_per_head, k_chunk, v_chunk, ctx, sm_scale=None):
+    """Extend (chunked prefill) attention for one sequence: a chunk of C new
+    tokens attends to the sequence's compressed prefix and, causally, to the
+    chunk itself.
+
+    Roadmap §4.1: SGLang's extend (prefill) stage is a fused kernel over the
+    compressed pool, like its decode kernel; Roadmap §4.4: prefill is where
+    the rotation / quantisation cost shows.  Reading (the pages give no
+    formula for it): query token i of the chunk (position P + i) scores the P
+    prefix tokens with the same estimator as decode (rotated query, codes,
+    QJL correction, stored fp16 n and gamma) and the chunk tokens j <= i
+    exactly, <q_i, k_j> with the bf16 key and unrotated query; its values are
+    the dequantised q s + z of the prefix and the bf16 values of the chunk;
+    one softmax runs over all P + i + 1 logits.  The chunk's own keys and
+    values are stored compressed by the store path (tq_quantize_store), not
+    read back from the cache here.
+
+    ``q``: [C, Hq, d]; ``fields_per_head``: list over KV heads of the
+    ``paged.read_tokens`` fields of the prefix (all of length P);
+    ``k_chunk``, ``v_chunk``: [C, Hkv, d]; ``ctx`` as for
+    ``decode_one_sequence``.  Returns out [C, Hq, d] in fp64."""
+    q = np.asarray(q, dtype=np.float64)
+    C, Hq, d = q.shape
+    Hkv = len(fields_per_head)
+    G = Hq // Hkv
+    scale = (1.0 / np.sqrt(d)) if sm_scale is None else float(sm_scale)
+    out = np.zeros((C, Hq, d))
+    for hk in range(Hkv):
+        f = fields_per_head[hk]
+        kc = np.asarray(k_chunk[:, hk], dtype=np.float64)
+        vc = np.asarray(v_chunk[:, hk], dtype=np.float64)
+        vhat = _values.dequantize_values(f["q"], f["s16"], f["z16"])
+        for g in range(G):
+            hq = hk * G + g
+            est = _keys.estimate_scores(q[:, hq], f["idx"], f["sign"], f["n16"], f["g16"],
+                                        ctx["d1"], ctx["d2"], ctx["S"], ctx["c32"], qjl=ctx.get("qjl", True))
+            exact = q[:, hq] @ kc.T   # [C, C]: <q_i, k_j>
+            for i in range(C):
+                logits = np.concatenate([est[i], exact[i, :i + 1]])
+                vals = np.concatenate([vhat, vc[:i + 1]], axis=0)
+                out[i, hq] = softmax_attend(scale * logits, vals)
+    return out
 
 
 def fold_output_projection(w_o, d1, d2, num_heads: int) -> np.ndarray:
