@@ -327,6 +327,63 @@ def time_workload(torch, w, reps):
     return res
 
 
+# ---------------------------------------------------------- prefill workload --
+EXTEND_FLOPS_PER_PREFIX = 6 * 128  # per (query row, prefix token): q~.c, p.sign and the value product, 2 flops per MAC
+EXTEND_FLOPS_PER_CHUNK = 4 * 128   # per (query row, visible chunk token): q.k and the value product
+
+
+def setup_prefill(torch, tq, synth):
+    """B=4, Hq=32, Hkv=8, d=128: an 8192-token K3V4 prefix per sequence in the
+    paged pool and a 512-token bf16 chunk per sequence (0.5% x20 outliers).
+    A step stores the chunk compressed (tq_quantize_store into positions
+    8192..8703) and runs the extend attention of its 512 x 32 query rows."""
+    import numpy as np
+    d, B, Hq, Hkv, P, C, kb, vb, seed = 128, 4, 32, 8, 8192, 512, 3, 4, 6
+    s1, s2, S = synth.method_params(seed, d)
+    ctx = tq.tq_codebook_init(d, kb, vb, signs=np.stack([s1, s2]), S=S)
+    mb = (P + C) // 16
+    bt = torch.from_numpy(synth.block_table(seed, B, mb, B * mb)).cuda()
+    pool = torch.zeros((B * mb, Hkv, ctx.block_bytes), dtype=torch.uint8, device="cuda")
+    t = torch.arange(P, device="cuda")
+    for b in range(B):
+        slots = (bt[b][t // 16].long() * 16 + t % 16).to(torch.int32)
+        k = synth.torch_normal_bf16((P, Hkv, d), seed * 1000003 + 2 * b, p=0.005)
+        v = synth.torch_normal_bf16((P, Hkv, d), seed * 1000003 + 2 * b + 1, p=0.005)
+        tq.tq_quantize_store(ctx, k, v, slots, pool)
+    q = synth.torch_normal_bf16((B * C, Hq, d), seed * 7 + 1)
+    kc = synth.torch_normal_bf16((B * C, Hkv, d), seed * 7 + 2, p=0.005)
+    vc = synth.torch_normal_bf16((B * C, Hkv, d), seed * 7 + 3, p=0.005)
+    tc = torch.arange(P, P + C, device="cuda")
+    slot_chunk = torch.cat([(bt[b][tc // 16].long() * 16 + tc % 16) for b in range(B)]).to(torch.int32).contiguous()
+    cu = (torch.arange(B + 1, dtype=torch.int32, device="cuda") * C).contiguous()
+    plen = torch.full((B,), P, dtype=torch.int32, device="cuda")
+    out = torch.empty((B * C, Hq, d), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    store = tq.PreparedQuantize(ctx, kc, vc, slot_chunk, pool)
+    ext = tq.PreparedExtend(q, kc, vc, cu, ctx, pool, bt, plen, out, max_chunk=C, max_prefix_len=P)
+    rows = B * C * Hq
+    flops = rows * P * EXTEND_FLOPS_PER_PREFIX + B * Hq * (C * (C + 1) // 2) * EXTEND_FLOPS_PER_CHUNK
+    return dict(keep=[ctx, bt, pool, q, kc, vc, slot_chunk, cu, plen, out], store=store, ext=ext, B=B, C=C,
+                flops=flops)
+
+
+def time_prefill(torch, w, reps):
+    for _ in range(2):
+        w["store"]()
+        w["ext"]()
+    _, each = time_eager(torch, lambda i: w["ext"](), reps)
+    ext_ms = _median(each)
+    _, each = time_eager(torch, lambda i: (w["store"](), w["ext"]()), reps)
+    step_ms = _median(each)
+    tflops = w["flops"] / (ext_ms * 1e-3) / 1e12
+    return {"workload": "prefill-b4-hq32-hkv8-d128-prefix8192-chunk512-k3v4: store the chunk + extend attention",
+            "chunk_tokens_per_step": w["B"] * w["C"], "median_ms_per_step": round(step_ms, 5),
+            "prefill_tokens_per_s": round(w["B"] * w["C"] / (step_ms * 1e-3), 1),
+            "extend_median_ms": round(ext_ms, 5), "extend_algorithmic_flops": w["flops"],
+            "extend_tflops": round(tflops, 2), "mfma_peak_tflops": 2500.0,
+            "extend_mfma_frac": round(tflops / 2500.0, 4)}
+
+
 # ------------------------------------------------------- quantise workload --
 def bench_quantize(torch, tq, synth, reps):
     import numpy as np
@@ -484,6 +541,13 @@ def main():
             log(f"{name}: {workloads[name]['median_ms'] * 1e3:.1f} us, {workloads[name]['tbs']:.3f} TB/s")
             w.clear()
             torch.cuda.empty_cache()
+        log("prefill workload (extend attention)")
+        w = setup_prefill(torch, tq, synth)
+        workloads["prefill_extend"] = time_prefill(torch, w, max(10, args.steps // 5))
+        log(f"prefill: extend {workloads['prefill_extend']['extend_median_ms'] * 1e3:.1f} us, "
+            f"{workloads['prefill_extend']['extend_tflops']:.1f} TFLOP/s")
+        w.clear()
+        torch.cuda.empty_cache()
         log("quantise workload")
         workloads["quantize"] = bench_quantize(torch, tq, synth, reps=max(20, args.steps // 2))
         log(f"quantise K3V4 {workloads['quantize']['k3v4']['median_ms'] * 1e3:.1f} us")

@@ -259,6 +259,55 @@ size_t tq_decode_workspace_bytes(const tq_decode_args* args);
  * anything is enqueued. */
 int tq_decode_attention(const tq_decode_args* args, void* stream);
 
+/* ------------------------------------------------------------- extend ----
+ * Extend (chunked prefill) attention: a chunk of new tokens per sequence
+ * attends to that sequence's compressed prefix in the paged pool and,
+ * causally, to the chunk itself (Roadmap §4.1: the fused extend kernel over
+ * the compressed pool beside the fused decode kernel; §4.4: prefill is where
+ * the rotation and quantisation cost shows).  Query token i of sequence b's
+ * chunk sits at position prefix_lens[b] + i; its query head h (KV head
+ * h / G) scores
+ *   the prefix tokens t < prefix_lens[b] with the decode estimator
+ *     est_t = n_t ( sum_j q~_j c[idx_tj] + sqrt(pi/2)/d gamma_t sum_i p_i (2 sign_ti - 1) )
+ *     (MSE-only presets: the first term alone), values q s + z;
+ *   the chunk tokens j <= i exactly, <q_i, k_j>, values v_j (bf16);
+ * out = softmax(sm_scale * scores) . values.  The chunk's keys and values are
+ * not read from the pool: store them with tq_quantize_store (before or after
+ * this call; the order does not matter).
+ *   q       : device bf16 [num_tokens][num_q_heads][head_dim], the chunks of
+ *             all sequences one after another (rows cu_chunk[b] ..
+ *             cu_chunk[b+1] - 1 for sequence b); 16-byte aligned.
+ *   k, v    : device bf16 [num_tokens][num_kv_heads][head_dim], same rows.
+ *   cu_chunk: device int32 [batch + 1], non-decreasing, cu_chunk[0] = 0;
+ *             chunk lengths are clamped to max_chunk.
+ *   prefix_lens : device int32 [batch]; clamped to [0, max_prefix_len].
+ *   block_tables: device int32 [batch][max_blocks_per_seq]; block ids outside
+ *             [0, pool_blocks) make their 16 prefix tokens drop out.
+ *   out     : device fp32 [num_tokens][num_q_heads][head_dim].
+ * Supported: head_dim 128 and query heads per KV head G in {1, 2, 4, 8}
+ * (others: TQ_EUNSUPPORTED).  One launch, no workspace, no allocation. */
+typedef struct {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* cu_chunk;
+  int32_t batch;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t max_chunk;          /* >= every chunk length; sizes the grid */
+  const tq_ctx* ctx;
+  const void* pool;
+  int64_t pool_blocks;
+  const int32_t* block_tables;
+  int32_t max_blocks_per_seq;
+  const int32_t* prefix_lens;
+  int32_t max_prefix_len;     /* <= 16 * max_blocks_per_seq */
+  float sm_scale;             /* <= 0 selects 1/sqrt(head_dim) */
+  float* out;
+} tq_extend_args;
+
+int tq_extend_attention(const tq_extend_args* args, void* stream);
+
 /* ------------------------------------------------- decode, no allocation --
  * For callers that cannot allocate device memory: code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc.  Same

@@ -18,7 +18,7 @@ __all__ = [
     "TqError", "Context", "library_path", "load", "tq_codebook_init", "tq_ctx_destroy", "tq_ctx_tables",
     "tq_lloyd_max", "tq_record_layout", "tq_draw_params", "tq_block_bytes", "tq_quantize_store",
     "tq_decode_workspace_bytes", "tq_decode_attention", "tq_decode_attention_noalloc", "NOALLOC_SCRATCH_BYTES",
-    "PreparedDecode", "PreparedQuantize",
+    "PreparedDecode", "PreparedQuantize", "PreparedExtend", "tq_extend_attention",
     "tq_last_error", "EXPORTED_SYMBOLS",
 ]
 
@@ -34,7 +34,7 @@ EXPORTED_SYMBOLS = [
     "tq_codebook_init", "tq_ctx_destroy", "tq_ctx_tables", "tq_ctx_preset", "tq_lloyd_max", "tq_uniform_codebook",
     "tq_record_layout", "tq_fold_output_projection",
     "tq_draw_params", "tq_block_bytes", "tq_quantize_store", "tq_decode_workspace_bytes", "tq_decode_attention",
-    "tq_decode_attention_noalloc", "tq_last_error",
+    "tq_decode_attention_noalloc", "tq_extend_attention", "tq_last_error",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -76,6 +76,17 @@ class tq_decode_args(ctypes.Structure):
     ]
 
 
+class tq_extend_args(ctypes.Structure):
+    _fields_ = [
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("cu_chunk", ctypes.c_void_p),
+        ("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+        ("max_chunk", ctypes.c_int32), ("ctx", ctypes.c_void_p), ("pool", ctypes.c_void_p),
+        ("pool_blocks", ctypes.c_int64), ("block_tables", ctypes.c_void_p), ("max_blocks_per_seq", ctypes.c_int32),
+        ("prefix_lens", ctypes.c_void_p), ("max_prefix_len", ctypes.c_int32), ("sm_scale", ctypes.c_float),
+        ("out", ctypes.c_void_p),
+    ]
+
+
 def load(path: str | None = None):
     """Load the library once; raises if it has not been built."""
     global _LIB
@@ -102,6 +113,7 @@ def load(path: str | None = None):
         "tq_decode_workspace_bytes": (c.c_size_t, [c.POINTER(tq_decode_args)]),
         "tq_decode_attention": (c.c_int, [c.POINTER(tq_decode_args), P]),
         "tq_decode_attention_noalloc": (c.c_int, [c.POINTER(tq_decode_args), P]),
+        "tq_extend_attention": (c.c_int, [c.POINTER(tq_extend_args), P]),
         "tq_last_error": (c.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -444,3 +456,65 @@ class PreparedQuantize:
 
     def __call__(self) -> None:
         _check(self._fn(*self._a, self._stream), "tq_quantize_store")
+
+
+def _extend_args(q, k, v, cu_chunk, ctx, pool, block_tables, prefix_lens, out, max_chunk, max_prefix_len=None,
+                 sm_scale=0.0):
+    """Marshal the extend arguments after checking every tensor against the
+    others (device, dtype, layout, shape)."""
+    import torch
+    _check_dev("q", q, torch.bfloat16, dim=3)
+    T, Hq, d = q.shape
+    _need(ctx.handle, "context is closed")
+    _need(ctx.head_dim == d, f"q has head_dim {d} but the context has {ctx.head_dim}")
+    _check_dev("pool", pool, torch.uint8, dim=3)
+    _need(pool.shape[2] == ctx.block_bytes, f"pool records are {pool.shape[2]} bytes, the context needs {ctx.block_bytes}")
+    Hkv = pool.shape[1]
+    _need(Hkv > 0 and Hq % Hkv == 0, f"num_q_heads {Hq} must be a multiple of num_kv_heads {Hkv}")
+    _check_dev("k", k, torch.bfloat16, (T, Hkv, d), dim=3)
+    _check_dev("v", v, torch.bfloat16, (T, Hkv, d), dim=3)
+    _check_dev("cu_chunk", cu_chunk, torch.int32, dim=1)
+    B = cu_chunk.shape[0] - 1
+    _need(B >= 0, "cu_chunk needs batch + 1 entries")
+    _check_dev("prefix_lens", prefix_lens, torch.int32, (B,), dim=1)
+    _check_dev("block_tables", block_tables, torch.int32, (B, None), dim=2)
+    _check_dev("out", out, torch.float32, (T, Hq, d), dim=3)
+    _need(int(max_chunk) >= 0, "max_chunk must be >= 0")
+    a = tq_extend_args()
+    a.q, a.k, a.v, a.cu_chunk = _ptr(q), _ptr(k), _ptr(v), _ptr(cu_chunk)
+    a.batch, a.num_q_heads, a.num_kv_heads, a.max_chunk = B, Hq, Hkv, int(max_chunk)
+    a.ctx = ctx.handle
+    a.pool, a.pool_blocks = _ptr(pool), pool.shape[0]
+    a.block_tables, a.max_blocks_per_seq = _ptr(block_tables), block_tables.shape[1]
+    a.prefix_lens = _ptr(prefix_lens)
+    a.max_prefix_len = block_tables.shape[1] * 16 if max_prefix_len is None else int(max_prefix_len)
+    a.sm_scale = sm_scale
+    a.out = _ptr(out)
+    return a
+
+
+def tq_extend_attention(q, k, v, cu_chunk, ctx, pool, block_tables, prefix_lens, out, max_chunk, stream=None,
+                        **kw) -> None:
+    """Extend (chunked prefill) attention: the chunks' queries q (bf16
+    [T, Hq, 128], sequence after sequence as cu_chunk (int32 [B + 1]) says)
+    attend to each sequence's compressed prefix (prefix_lens int32 [B] tokens
+    through block_tables into pool) and causally to the chunk's own bf16 keys
+    and values k, v [T, Hkv, 128]; out float32 [T, Hq, 128].  ``max_chunk``
+    bounds every chunk length; keyword arguments: max_prefix_len, sm_scale."""
+    a = _extend_args(q, k, v, cu_chunk, ctx, pool, block_tables, prefix_lens, out, max_chunk, **kw)
+    _check(load().tq_extend_attention(ctypes.byref(a), _stream(stream)), "tq_extend_attention")
+
+
+class PreparedExtend:
+    """tq_extend_attention validated and marshalled once, launched many times
+    (same storage rules as PreparedDecode)."""
+
+    def __init__(self, q, k, v, cu_chunk, ctx, pool, block_tables, prefix_lens, out, max_chunk, stream=None, **kw):
+        self._args = _extend_args(q, k, v, cu_chunk, ctx, pool, block_tables, prefix_lens, out, max_chunk, **kw)
+        self._keep = (q, k, v, cu_chunk, ctx, pool, block_tables, prefix_lens, out)
+        self._stream = _stream(stream)
+        self._fn = load().tq_extend_attention
+        self._ref = ctypes.byref(self._args)
+
+    def __call__(self) -> None:
+        _check(self._fn(self._ref, self._stream), "tq_extend_attention")

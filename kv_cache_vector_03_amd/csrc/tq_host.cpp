@@ -368,13 +368,22 @@ extern "C" int tq_codebook_init(const tq_preset* p, const int8_t* signs, const f
     pair[2 * idx] = (uint32_t)ha | ((uint32_t)hb << 16);
     pair[2 * idx + 1] = (uint32_t)la | ((uint32_t)lb << 16);
   }
+  std::vector<uint32_t> pair16((size_t)P * 2);
+  for (int idx = 0; idx < P; ++idx) {
+    int a = idx & (L - 1), b = idx >> kb;
+    uint16_t ha = f32_to_f16_bits(c->c32[a]), hb = f32_to_f16_bits(c->c32[b]);
+    uint16_t la = f32_to_f16_bits(c->c32[a] - f16_bits_to_f32(ha));
+    uint16_t lb = f32_to_f16_bits(c->c32[b] - f16_bits_to_f32(hb));
+    pair16[2 * idx] = (uint32_t)ha | ((uint32_t)hb << 16);
+    pair16[2 * idx + 1] = (uint32_t)la | ((uint32_t)lb << 16);
+  }
 
   // ---- one device allocation, 256-byte aligned pieces
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   size_t o_c = 0, o_t = up(o_c + 4 * L), o_s1 = up(o_t + 4 * L), o_s2 = up(o_s1 + 4 * d), o_S = up(o_s2 + 4 * d),
          o_tiles = up(o_S + 4 * (size_t)d * d), o_tiles2 = up(o_tiles + 2 * tiles.size()),
-         o_pair = up(o_tiles2 + 2 * tiles_d2.size()),
-         total = up(o_pair + 4 * pair.size());
+         o_pair = up(o_tiles2 + 2 * tiles_d2.size()), o_pair16 = up(o_pair + 4 * pair.size()),
+         total = up(o_pair16 + 4 * pair16.size());
   if (hipGetDevice(&c->device) != hipSuccess) {
     set_error("tq_codebook_init: no HIP device");
     delete c;
@@ -395,6 +404,7 @@ extern "C" int tq_codebook_init(const tq_preset* p, const int8_t* signs, const f
   std::memcpy(img.data() + o_tiles, tiles.data(), 2 * tiles.size());
   std::memcpy(img.data() + o_tiles2, tiles_d2.data(), 2 * tiles_d2.size());
   std::memcpy(img.data() + o_pair, pair.data(), 4 * pair.size());
+  std::memcpy(img.data() + o_pair16, pair16.data(), 4 * pair16.size());
   if (hipMemcpy(base, img.data(), total, hipMemcpyHostToDevice) != hipSuccess) {
     set_error("tq_codebook_init: upload failed");
     (void)hipFree(c->dev_block);
@@ -409,6 +419,7 @@ extern "C" int tq_codebook_init(const tq_preset* p, const int8_t* signs, const f
   c->dev.s_tiles = (const uint16_t*)(base + o_tiles);
   c->dev.s_tiles_d2 = (const uint16_t*)(base + o_tiles2);
   c->dev.pair_lut = (const uint32_t*)(base + o_pair);
+  c->dev.pair_lut_f16 = (const uint32_t*)(base + o_pair16);
   *out = c;
   return TQ_OK;
 }
@@ -662,4 +673,43 @@ extern "C" int tq_decode_attention(const tq_decode_args* a, void* stream) { retu
 
 extern "C" int tq_decode_attention_noalloc(const tq_decode_args* a, void* stream) {
   return decode_entry(a, stream, true);
+}
+
+// ---------------------------------------------------------------------------
+// Extend
+// ---------------------------------------------------------------------------
+extern "C" int tq_extend_attention(const tq_extend_args* a, void* stream) {
+  if (!a || !a->ctx) {
+    set_error("tq_extend_attention: NULL arguments or context");
+    return TQ_EINVAL;
+  }
+  if (a->batch < 0 || a->num_q_heads <= 0 || a->num_kv_heads <= 0 || a->num_q_heads % a->num_kv_heads ||
+      a->max_chunk < 0 || a->max_prefix_len < 0 || a->max_blocks_per_seq < 0 ||
+      (int64_t)a->max_prefix_len > 16ll * a->max_blocks_per_seq || a->pool_blocks < 0) {
+    set_error("tq_extend_attention: batch %d, heads %d / %d, max_chunk %d, max_prefix_len %d, max_blocks %d invalid",
+              a->batch, a->num_q_heads, a->num_kv_heads, a->max_chunk, a->max_prefix_len, a->max_blocks_per_seq);
+    return TQ_EINVAL;
+  }
+  const int G = a->num_q_heads / a->num_kv_heads;
+  if (a->ctx->d != 128 || (G != 1 && G != 2 && G != 4 && G != 8)) {
+    set_error("tq_extend_attention: head_dim %d with %d query heads per KV head is not supported (head_dim 128, "
+              "G in {1, 2, 4, 8})", a->ctx->d, G);
+    return TQ_EUNSUPPORTED;
+  }
+  if (a->batch == 0 || a->max_chunk == 0) return TQ_OK;
+  if (!a->q || !a->k || !a->v || !a->cu_chunk || !a->prefix_lens || !a->out ||
+      (a->max_prefix_len > 0 && (!a->pool || !a->block_tables))) {
+    set_error("tq_extend_attention: NULL device pointer");
+    return TQ_EINVAL;
+  }
+  if (((uintptr_t)a->q | (uintptr_t)a->k | (uintptr_t)a->v | (uintptr_t)a->pool) & 15) {
+    set_error("tq_extend_attention: q, k, v and pool must be 16-byte aligned");
+    return TQ_EINVAL;
+  }
+  hipError_t e = launch_extend(a, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    set_error("tq_extend_attention: launch failed: %s", hipGetErrorString(e));
+    return TQ_EHIP;
+  }
+  return TQ_OK;
 }

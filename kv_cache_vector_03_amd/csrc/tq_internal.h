@@ -28,6 +28,9 @@ struct DevTables {
   // Decode pair table: entry a | b << k_bits = (bf16 hi c[a], bf16 hi c[b]),
   // (bf16 lo c[a], bf16 lo c[b]) as two dwords; [2^(2 k_bits)][2] uint32.
   const uint32_t* pair_lut = nullptr;
+  // The same pair table in fp16 (extend attention): entry a | b << k_bits =
+  // (fp16 hi c[a], fp16 hi c[b]), (fp16 lo c[a], fp16 lo c[b]); [2^(2 k_bits)][2].
+  const uint32_t* pair_lut_f16 = nullptr;
 };
 
 struct Layout {
@@ -75,6 +78,8 @@ hipError_t launch_decode(const tq_decode_args* a, const DecodePlan& plan, hipStr
 // the recent window beside the kernel's own tables); on failure the message is
 // set with set_error and an error is returned.  Enqueues nothing.
 hipError_t check_decode_launch(const tq_decode_args* a, const DecodePlan& plan);
+// Extend attention (tq_extend.hip).
+hipError_t launch_extend(const tq_extend_args* a, hipStream_t stream);
 // Device address of the current device's static scratch array of
 // TQ_NOALLOC_SCRATCH_BYTES bytes (looked up once per device, then cached).
 hipError_t noalloc_scratch(void** out);
