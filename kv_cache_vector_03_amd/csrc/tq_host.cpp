@@ -358,6 +358,24 @@ extern "C" int tq_codebook_init(const tq_preset* p, const int8_t* signs, const f
           tiles_d2[base + (size_t)l * 8 + e] = h ^ flip;
           tiles_d2[base + 64 * 8 + (size_t)l * 8 + e] = lo ^ flip;
         }
+  // the same S diag(D2) tiles with the k index permuted the way the
+  // head_dim-128 store kernel holds its residual (d = 128 only)
+  std::vector<uint16_t> tiles_perm(d == 128 ? tiles.size() : 0);
+  if (d == 128)
+    for (int nt = 0; nt < NT; ++nt)
+      for (int kt = 0; kt < KT; ++kt)
+        for (int l = 0; l < 64; ++l)
+          for (int e = 0; e < 8; ++e) {
+            int row = 16 * nt + (l % 16);
+            int col = 32 * kt + 16 * (e / 4) + 4 * (l / 16) + e % 4;
+            float v = c->S[(size_t)row * d + col] * sscale;
+            uint16_t h = f32_to_f16_bits(v);
+            uint16_t lo = f32_to_f16_bits(v - f16_bits_to_f32(h));
+            const uint16_t flip = sg2[col] < 0.f ? 0x8000u : 0u;
+            size_t base = (((size_t)nt * KT + kt) * 2) * 64 * 8;
+            tiles_perm[base + (size_t)l * 8 + e] = h ^ flip;
+            tiles_perm[base + 64 * 8 + (size_t)l * 8 + e] = lo ^ flip;
+          }
   const int P = 1 << (2 * kb);
   std::vector<uint32_t> pair((size_t)P * 2);
   for (int idx = 0; idx < P; ++idx) {
@@ -383,7 +401,7 @@ extern "C" int tq_codebook_init(const tq_preset* p, const int8_t* signs, const f
   size_t o_c = 0, o_t = up(o_c + 4 * L), o_s1 = up(o_t + 4 * L), o_s2 = up(o_s1 + 4 * d), o_S = up(o_s2 + 4 * d),
          o_tiles = up(o_S + 4 * (size_t)d * d), o_tiles2 = up(o_tiles + 2 * tiles.size()),
          o_pair = up(o_tiles2 + 2 * tiles_d2.size()), o_pair16 = up(o_pair + 4 * pair.size()),
-         total = up(o_pair16 + 4 * pair16.size());
+         o_perm = up(o_pair16 + 4 * pair16.size()), total = up(o_perm + 2 * tiles_perm.size());
   if (hipGetDevice(&c->device) != hipSuccess) {
     set_error("tq_codebook_init: no HIP device");
     delete c;
@@ -405,6 +423,7 @@ extern "C" int tq_codebook_init(const tq_preset* p, const int8_t* signs, const f
   std::memcpy(img.data() + o_tiles2, tiles_d2.data(), 2 * tiles_d2.size());
   std::memcpy(img.data() + o_pair, pair.data(), 4 * pair.size());
   std::memcpy(img.data() + o_pair16, pair16.data(), 4 * pair16.size());
+  if (!tiles_perm.empty()) std::memcpy(img.data() + o_perm, tiles_perm.data(), 2 * tiles_perm.size());
   if (hipMemcpy(base, img.data(), total, hipMemcpyHostToDevice) != hipSuccess) {
     set_error("tq_codebook_init: upload failed");
     (void)hipFree(c->dev_block);
@@ -420,6 +439,7 @@ extern "C" int tq_codebook_init(const tq_preset* p, const int8_t* signs, const f
   c->dev.s_tiles_d2 = (const uint16_t*)(base + o_tiles2);
   c->dev.pair_lut = (const uint32_t*)(base + o_pair);
   c->dev.pair_lut_f16 = (const uint32_t*)(base + o_pair16);
+  c->dev.s_tiles_perm_d2 = tiles_perm.empty() ? nullptr : (const uint16_t*)(base + o_perm);
   *out = c;
   return TQ_OK;
 }

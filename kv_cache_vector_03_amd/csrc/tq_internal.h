@@ -31,6 +31,12 @@ struct DevTables {
   // The same pair table in fp16 (extend attention): entry a | b << k_bits =
   // (fp16 hi c[a], fp16 hi c[b]), (fp16 lo c[a], fp16 lo c[b]); [2^(2 k_bits)][2].
   const uint32_t* pair_lut_f16 = nullptr;
+  // S diag(D2) as MFMA A-operand tiles for the head_dim-128 store kernel whose
+  // residual operand comes straight from the rotation's output registers:
+  // tile (nt, kt) lane l element e = 16 S[16 nt + l % 16][j] D2[j] with
+  // j = 32 kt + 16 (e / 4) + 4 (l / 16) + e % 4, fp16 hi / lo;
+  // layout [nt][kt][hi, lo][64][8] fp16 (empty for head_dim 256).
+  const uint16_t* s_tiles_perm_d2 = nullptr;
 };
 
 struct Layout {
@@ -67,6 +73,11 @@ Layout make_layout(int d, int kb, int vb, bool qjl);
 hipError_t launch_quantize(const tq_ctx* c, const void* k, const void* v, int in_dtype, int64_t num_tokens,
                            int num_kv_heads, const int32_t* slot_mapping, void* pool, int64_t num_blocks,
                            hipStream_t stream);
+
+// The head_dim-128 bf16 store kernel with the rotation and the QJL projection
+// on the matrix cores (tq_quantize_mfma.hip); values not rotated.
+hipError_t launch_quantize_mfma(const tq_ctx* c, const void* k, const void* v, int64_t num_tokens, int num_kv_heads,
+                                const int32_t* slot_mapping, void* pool, int64_t num_blocks, hipStream_t stream);
 
 struct DecodePlan {
   int d, G, num_splits_max, chunk;

@@ -816,6 +816,10 @@ hipError_t launch_quantize(const tq_ctx* c, const void* k, const void* v, int in
   a.dev = c->dev;
   a.num_tiles = (a.num_th + 15) / 16;
   const bool bf = in_dtype == TQ_DTYPE_BF16;
+  // large bf16 batches at head_dim 128 (values not rotated): rotation and
+  // projection on the matrix cores
+  if (c->d == 128 && bf && !c->rotv && a.num_th > kRowPathMaxTokenHeads)
+    return launch_quantize_mfma(c, k, v, num_tokens, num_kv_heads, slot_mapping, pool, num_blocks, stream);
   if (c->d == 128)
     return bf ? dispatch_kind<128, true>(a, c->qjl, c->rotv, c->kb, c->vb, stream)
               : dispatch_kind<128, false>(a, c->qjl, c->rotv, c->kb, c->vb, stream);

@@ -1,0 +1,458 @@
+// Fused quantise + pack + paged store for large batches of bf16 keys and
+// values at head_dim 128 (Roadmap §3.1: the rotation fused with the quantiser
+// in the store launch; Hub, technical principle steps 1-5), with both dense
+// products of the key path on the matrix cores.
+//
+// A wave owns a tile of 16 consecutive tokens of one KV head.  In the MFMA
+// layout lane l plays row n = l % 16 (a token) and group g = l / 16:
+//   rotation  y = H D1 k on v_mfma_f32_16x16x32_bf16, computed transposed:
+//             C[j][n] = sum_k H[j][k] (D1 k_n)[k].  The B operand is the bf16
+//             key itself (lane (n, g) loads coordinates 32 kt + 8 g .. + 7 of
+//             its row, D1 applied as a sign-bit xor), products are exact and
+//             the sums fp32.  The A operand is the Sylvester Hadamard matrix:
+//             H[16 nt + m][32 kt + k] = (-1)^popcount(nt & (2 kt + k / 16))
+//             (-1)^popcount(m & (k % 16)), so every A tile is one of four
+//             per-lane sign patterns held in registers.  Lane (n, g) receives
+//             coordinates 16 nt + 4 g + r (nt < 8, r < 4) of row n.
+//   quantise  as the other store kernels: norm, Lloyd-Max index of the
+//             D2-free coordinate from its magnitude, residual, gamma.
+//   QJL       z = S r on v_mfma_f32_16x16x32_f16 with the residual as the B
+//             operand straight from the registers the rotation left it in:
+//             k-slice kt, element e of lane (n, g) is coordinate
+//             32 kt + 16 (e / 4) + 4 g + e % 4, and the context's S tiles are
+//             laid out with the same permutation of the k index (D2 folded in,
+//             fp16 hi / lo of 16 S, three products per slice).  Lane (n, g)
+//             gets z_i for i = 16 nt + 4 g + r and packs its sign bits.
+//   pack      code and sign-bit fields are placed at their stream offsets in
+//             the lane and or-ed over the four lanes of a row (permlane swaps).
+// Values are quantised in the row-part layout (lane: row l / 4, 32-channel
+// group l % 4), one group per lane.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <mutex>
+
+#include "tq_common.hip.h"
+#include "tq_internal.h"
+
+namespace tq {
+namespace {
+
+constexpr int MD = 128, MKT = 4, MNT = 8;
+// waves per workgroup: with the QJL tiles (64 KB of LDS) one workgroup fills a
+// CU at three waves per SIMD; MSE-only keys need no tiles and run 8-wave
+// workgroups, several per CU
+template <bool QJ>
+constexpr int mwaves() {
+  return QJ ? 12 : 8;
+}
+
+struct QMArgs {
+  const uint16_t* k;
+  const uint16_t* v;
+  int64_t num_tokens;
+  int32_t hkv;
+  const int32_t* slot_mapping;
+  int64_t slots_total;
+  uint8_t* pool;
+  int64_t rec;
+  Layout lay;
+  DevTables dev;
+  int64_t num_tiles;
+};
+
+// or / sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the lanes of one row)
+__device__ __forceinline__ uint32_t row_or4(uint32_t x) {
+  auto a = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  x = a[0] | a[1];
+  auto b = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  return b[0] | b[1];
+}
+__device__ __forceinline__ float row_sum4(float x) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+constexpr int parity(int x) { return __builtin_popcount(x) & 1; }
+
+template <int KB, int VB, bool QJ>
+__global__ __launch_bounds__(mwaves<QJ>() * 64) void quantize_mfma_kernel(QMArgs a) {
+  constexpr int MW = mwaves<QJ>();
+  constexpr int L = 1 << KB, H = L / 2;
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  const u32x4* s_st = reinterpret_cast<const u32x4*>(lds);          // [nt][kt][hi, lo][64] (QJL)
+  float* s_c = reinterpret_cast<float*>(lds + (QJ ? 65536 : 0));     // c[H .. L-1]
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int n = lane & 15, g = lane >> 4;
+
+  if constexpr (QJ) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(a.dev.s_tiles_perm_d2);
+    for (int i = tid; i < 4096; i += MW * 64) const_cast<u32x4*>(s_st)[i] = src[i];
+  }
+  if (tid < H) s_c[tid] = a.dev.centroids[H + tid];
+  float tU[H - 1];
+#pragma unroll
+  for (int i = 0; i < H - 1; ++i) tU[i] = a.dev.thresholds[H + i];
+  // D1 as bf16 sign-bit masks of the key operand: element e of slice kt is
+  // coordinate 32 kt + 8 g + e
+  u32x4 d1m[MKT];
+#pragma unroll
+  for (int kt = 0; kt < MKT; ++kt)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int c0 = 32 * kt + 8 * g + 2 * w;
+      d1m[kt][w] = (a.dev.signs1[c0] < 0.f ? 0x8000u : 0u) | (a.dev.signs1[c0 + 1] < 0.f ? 0x80000000u : 0u);
+    }
+  // Hadamard A patterns: element e of lane (m = n, g) is (-1)^popcount(m & (8 (g & 1) + e)),
+  // times the tile sign of the lane's half (g >> 1): hv[s0][s1] takes sign s0
+  // on lanes g < 2 and s1 on lanes g >= 2
+  u32x4 hv[2][2];
+  {
+    u32x4 pos;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      uint32_t d = 0;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int e = 2 * w + u;
+        const uint32_t neg = (uint32_t)(__builtin_popcount(n & (8 * (g & 1) + e)) & 1);
+        d |= (neg ? 0xBF80u : 0x3F80u) << (16 * u);
+      }
+      pos[w] = d;
+    }
+#pragma unroll
+    for (int s0 = 0; s0 < 2; ++s0)
+#pragma unroll
+      for (int s1 = 0; s1 < 2; ++s1) {
+        const uint32_t flip = ((g >> 1) ? s1 : s0) ? 0x80008000u : 0u;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) hv[s0][s1][w] = pos[w] ^ flip;
+      }
+  }
+  // D2 as code-word xor patterns of this lane's stored code dwords (index
+  // ^ (L - 1) where D2 = -1; the kernel works on D2-free coordinates)
+  constexpr int CWD = KB * MD / 32;   // code dwords per row
+  constexpr int CPL = CWD / 4;        // code dwords stored per lane
+  uint32_t m2c[CPL];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const int wd = KB == 4 ? 2 * (CPL * (g & 1) + i) + (g >> 1) : CPL * g + i;  // the stream dword this lane stores
+    uint32_t m = 0;
+    for (int j = 0; j < MD; ++j) {
+      if (a.dev.signs2[j] < 0.f) {
+        const int bp = j * KB;
+        if (bp / 32 == wd) m |= (uint32_t)(L - 1) << (bp % 32);
+        if (bp / 32 + 1 == wd && (bp % 32) + KB > 32) m |= (uint32_t)(L - 1) >> (32 - bp % 32);
+      }
+    }
+    m2c[i] = m;
+  }
+  __syncthreads();
+
+  const float inv_sqrt_d = 1.0f / __builtin_sqrtf((float)MD);
+  const float rscale = (float)(1 << kRScaleLog2);
+  const int64_t tstride = (int64_t)gridDim.x * MW;
+  for (int64_t tile = (int64_t)blockIdx.x * MW + wave; tile < a.num_tiles; tile += tstride) {
+    // A tile is 16 consecutive tokens of one KV head (so that, when their slots
+    // fill a paged block in order, every region of the block's record is
+    // written by this wave in contiguous runs).
+    const int64_t t0 = (tile / a.hkv) * 16;
+    const int hh = (int)(tile % a.hkv);
+    // ---------------------------------------------------------------- key
+    const int64_t tk = t0 + n;
+    const bool valid = tk < a.num_tokens;
+    const int64_t th = tk * a.hkv + hh;
+    bf16x8 kbv[MKT];
+    {
+      const u32x4* pk = reinterpret_cast<const u32x4*>(a.k + (valid ? th : 0) * MD + 8 * g);
+#pragma unroll
+      for (int kt = 0; kt < MKT; ++kt) {
+        u32x4 w = valid ? __builtin_nontemporal_load(pk + 4 * kt) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] ^= d1m[kt][i];
+        kbv[kt] = __builtin_bit_cast(bf16x8, w);
+      }
+    }
+    f32x4 y[MNT];
+#pragma unroll
+    for (int nt = 0; nt < MNT; ++nt) {
+      y[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kt = 0; kt < MKT; ++kt) {
+        const u32x4 hp = hv[parity(nt & (2 * kt))][parity(nt & (2 * kt + 1))];
+        y[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, hp), kbv[kt], y[nt], 0, 0, 0);
+      }
+    }
+    // norm: sum of squares of the rotated row (H H^T = d I) over the row's lanes
+    float ss = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < MNT; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ss = __builtin_fmaf(y[nt][r], y[nt][r], ss);
+    ss = row_sum4(ss);
+    const float nrm = __builtin_sqrtf(ss * (1.0f / MD));
+    const bool zero = !(nrm > 0.f);
+    const float inv = zero ? 0.f : inv_sqrt_d / nrm;
+    // Lloyd-Max index of the D2-free coordinate from its magnitude, and the residual
+    uint32_t field[MNT];
+    float r2 = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < MNT; ++nt) {
+      field[nt] = 0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float u = y[nt][r] * inv;
+        const float m = fabsf(u);
+        uint32_t cnt = 0;
+#pragma unroll
+        for (int i = 0; i < H - 1; ++i) cnt += m > tU[i] ? 1u : 0u;
+        const float dd = m - s_c[cnt];
+        const bool pos = u > 0.f;
+        const uint32_t code = cnt ^ (pos ? (uint32_t)H : (uint32_t)H - 1u);
+        float res = pos ? dd : -dd;
+        res = zero ? 0.f : res;
+        r2 = __builtin_fmaf(res, res, r2);
+        y[nt][r] = res;
+        field[nt] |= code << (KB * r);
+      }
+    }
+    const float gamma = __builtin_sqrtf(row_sum4(r2));
+
+    // ---- QJL sign bits of S r (MSE-only keys skip the sketch)
+    uint32_t qw = 0;  // the sign dword this lane stores (dword g of the row's d / 8 bytes)
+    if constexpr (QJ) {
+      f16x8 rbh[MKT], rbl[MKT];
+#pragma unroll
+      for (int kt = 0; kt < MKT; ++kt)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = y[2 * kt + (e >> 2)][e & 3] * rscale;
+          const _Float16 hh = (_Float16)x;
+          rbh[kt][e] = hh;
+          rbl[kt][e] = (_Float16)(x - (float)hh);
+        }
+      // one column tile of z at a time (the S tiles come from LDS per tile);
+      // bit i = 16 nt + 4 g + r of the row's stream is bit 16 (nt % 2) + 4 g + r
+      // of dword nt / 2, which lane g = nt / 2 keeps
+      uint32_t dw = 0;
+#pragma unroll 1
+      for (int nt = 0; nt < MNT; ++nt) {
+        f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        const u32x4* tp = s_st + (nt * MKT * 2) * 64 + lane;
+#pragma unroll
+        for (int kt = 0; kt < MKT; ++kt) {
+          const f16x8 ah = __builtin_bit_cast(f16x8, tp[(2 * kt) * 64]);
+          const f16x8 al = __builtin_bit_cast(f16x8, tp[(2 * kt + 1) * 64]);
+          z = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, rbh[kt], z, 0, 0, 0);
+          z = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, rbl[kt], z, 0, 0, 0);
+          z = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, rbh[kt], z, 0, 0, 0);
+        }
+        uint32_t nib = 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) nib |= (z[r] >= 0.f ? 1u : 0u) << r;
+        dw |= nib << (16 * (nt & 1) + 4 * g);
+        if (nt & 1) {  // uniform
+          dw = row_or4(dw);
+          if (g == (nt >> 1)) qw = dw;
+          dw = 0;
+        }
+      }
+      qw = zero ? 0u : qw;
+    }
+
+    // ---- code stream of the row: field nt (4 codes) at bit KB (16 nt + 4 g)
+    uint32_t cst[CPL];
+    if constexpr (KB == 2) {
+      // 8-bit fields: dword nt, byte g; lane g stores dwords 2 g, 2 g + 1
+      uint32_t wds[MNT];
+#pragma unroll
+      for (int nt = 0; nt < MNT; ++nt) wds[nt] = row_or4(field[nt] << (8 * g));
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) cst[i] = g == 0 ? wds[i] : g == 1 ? wds[2 + i] : g == 2 ? wds[4 + i] : wds[6 + i];
+    } else if constexpr (KB == 3) {
+      // pairs of 12-bit fields in three dwords 3 p .. 3 p + 2: F_2p at bit 12 g,
+      // F_2p+1 at bit 48 + 12 g; lane g stores dwords 3 g .. 3 g + 2
+      uint32_t wds[12];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const uint64_t x = (uint64_t)field[2 * p] | ((uint64_t)field[2 * p + 1] << 48);
+        const uint64_t lo = x << (12 * g);
+        const uint32_t hi = (uint32_t)(((uint64_t)field[2 * p + 1] << (12 * g + 16)) >> 32);
+        wds[3 * p] = row_or4((uint32_t)lo);
+        wds[3 * p + 1] = row_or4((uint32_t)(lo >> 32));
+        wds[3 * p + 2] = row_or4(hi);
+      }
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) cst[i] = g == 0 ? wds[i] : g == 1 ? wds[3 + i] : g == 2 ? wds[6 + i] : wds[9 + i];
+    } else {
+      // 16-bit fields: dword 2 nt + (g >> 1), half g & 1; or over the pair
+      // (g, g ^ 1); lane g stores dwords 2 (4 (g & 1) + i) + (g >> 1), i < 4
+      uint32_t wds[MNT];
+#pragma unroll
+      for (int nt = 0; nt < MNT; ++nt) {
+        uint32_t x = field[nt] << (16 * (g & 1));
+        auto b = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+        wds[nt] = b[0] | b[1];
+      }
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) cst[i] = (g & 1) ? wds[4 + i] : wds[i];
+    }
+
+    // ---- store the key record
+    const int32_t slot = valid ? a.slot_mapping[tk] : -1;
+    if (valid && slot >= 0 && (int64_t)slot < a.slots_total) {
+      uint8_t* base = a.pool + ((int64_t)(slot >> 4) * a.hkv + hh) * a.rec;
+      const int s = slot & 15;
+      uint8_t* kc = base + a.lay.kcodes + s * (KB * MD / 8);
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        const int wd = KB == 4 ? 2 * (CPL * (g & 1) + i) + (g >> 1) : CPL * g + i;
+        *reinterpret_cast<uint32_t*>(kc + 4 * wd) = zero ? 0u : (cst[i] ^ m2c[i]);
+      }
+      if constexpr (QJ) {
+        *reinterpret_cast<uint32_t*>(base + a.lay.kqjl + s * (MD / 8) + 4 * g) = qw;
+        if (g == 0)
+          *reinterpret_cast<uint32_t*>(base + a.lay.kmeta + s * 4) =
+              (uint32_t)f32_to_f16_bits(zero ? 0.f : nrm) | ((uint32_t)f32_to_f16_bits(gamma) << 16);
+      } else if (g == 0) {
+        *reinterpret_cast<uint16_t*>(base + a.lay.kmeta + s * 2) = f32_to_f16_bits(zero ? 0.f : nrm);
+      }
+    }
+
+    // -------------------------------------------------------------- value
+    // row-part layout: lane l holds channels 32 (l % 4) .. + 31 of row l / 4
+    {
+      const int vrow = lane >> 2, part = lane & 3;
+      const int64_t tv = t0 + vrow;
+      const bool vvalid = tv < a.num_tokens;
+      const int64_t thv = tv * a.hkv + hh;
+      float x[32];
+      {
+        const u32x4* pv = reinterpret_cast<const u32x4*>(a.v + (vvalid ? thv : 0) * MD + 32 * part);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const u32x4 w = vvalid ? __builtin_nontemporal_load(pv + i) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            x[8 * i + 2 * j] = __uint_as_float(w[j] << 16);
+            x[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+          }
+        }
+      }
+      constexpr float LV = (float)((1 << VB) - 1);
+      float mn = x[0], mx = x[0];
+#pragma unroll
+      for (int e = 1; e < 32; ++e) {
+        mn = fminf(mn, x[e]);
+        mx = fmaxf(mx, x[e]);
+      }
+      const uint16_t s16 = f32_to_f16_bits((mx - mn) / LV);
+      const uint16_t z16 = f32_to_f16_bits(mn);
+      const float sc = f16_bits_to_f32(s16), zz = f16_bits_to_f32(z16);
+      // q = rint((v - z) / s) with the IEEE quotient: the product with the
+      // rounded reciprocal is within 3e-6 of it (|q| <= 16), so only lanes
+      // with a value within kVBand of a half-integer redo their group with
+      // the division
+      constexpr float kVBand = 8e-6f;
+      const float rs = 1.0f / sc;
+      uint32_t vw[VB];
+#pragma unroll
+      for (int i = 0; i < VB; ++i) vw[i] = 0;
+      bool near = false;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) {
+        const float t = (x[e] - zz) * rs;
+        const float q0 = __builtin_rintf(t);
+        near |= fabsf(t - q0) >= 0.5f - kVBand;
+        const float q = fminf(fmaxf(q0, 0.f), LV);
+        const uint32_t qi = (sc != 0.f) ? (uint32_t)q : 0u;
+        vw[(e * VB) / 32] |= qi << ((e * VB) % 32);
+      }
+      if (near && sc != 0.f) {
+#pragma unroll
+        for (int i = 0; i < VB; ++i) vw[i] = 0;
+#pragma unroll
+        for (int e = 0; e < 32; ++e) {
+          float q = __builtin_rintf((x[e] - zz) / sc);
+          q = fminf(fmaxf(q, 0.f), LV);
+          vw[(e * VB) / 32] |= (uint32_t)q << ((e * VB) % 32);
+        }
+      }
+      const int32_t vslot = vvalid ? a.slot_mapping[tv] : -1;
+      if (vvalid && vslot >= 0 && (int64_t)vslot < a.slots_total) {
+        uint8_t* base = a.pool + ((int64_t)(vslot >> 4) * a.hkv + hh) * a.rec;
+        const int s = vslot & 15;
+#pragma unroll
+        for (int i = 0; i < VB; ++i)
+          *reinterpret_cast<uint32_t*>(base + a.lay.vcodes + ((part * VB + i) * 16 + s) * 4) = vw[i];
+        *reinterpret_cast<uint32_t*>(base + a.lay.vmeta + (part * 16 + s) * 4) = (uint32_t)s16 | ((uint32_t)z16 << 16);
+      }
+    }
+  }
+}
+
+template <int KB, int VB, bool QJ>
+hipError_t launch_m(const QMArgs& a, hipStream_t stream) {
+  constexpr int MW = mwaves<QJ>();
+  auto kern = quantize_mfma_kernel<KB, VB, QJ>;
+  const int lds = (QJ ? 65536 : 0) + 64;
+  struct Cache {
+    std::mutex mu;
+    bool init[16] = {};
+    int grid[16] = {};
+  };
+  static Cache cache;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 16) return hipErrorInvalidDevice;
+  int slots;
+  {
+    std::lock_guard<std::mutex> lock(cache.mu);
+    if (!cache.init[dev]) {
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+      if (e != hipSuccess) return e;
+      int cus = 256, per = 1;
+      (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kern, MW * 64, lds) != hipSuccess || per < 1) per = 1;
+      cache.grid[dev] = cus * per;
+      cache.init[dev] = true;
+    }
+    slots = cache.grid[dev];
+  }
+  // persistent workgroups: as many as are resident at once, or fewer
+  const int64_t want = (a.num_tiles + MW - 1) / MW;
+  const int grid = (int)std::min<int64_t>(want, (int64_t)slots);
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(MW * 64), lds, stream, a);
+  return hipGetLastError();
+}
+
+template <bool QJ>
+hipError_t dispatch_m(const QMArgs& a, int kb, int vb, hipStream_t s) {
+  if (kb == 2) return vb == 2 ? launch_m<2, 2, QJ>(a, s) : launch_m<2, 4, QJ>(a, s);
+  if (kb == 3) return vb == 2 ? launch_m<3, 2, QJ>(a, s) : launch_m<3, 4, QJ>(a, s);
+  return vb == 2 ? launch_m<4, 2, QJ>(a, s) : launch_m<4, 4, QJ>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_quantize_mfma(const tq_ctx* c, const void* k, const void* v, int64_t num_tokens, int num_kv_heads,
+                                const int32_t* slot_mapping, void* pool, int64_t num_blocks, hipStream_t stream) {
+  QMArgs a;
+  a.k = reinterpret_cast<const uint16_t*>(k);
+  a.v = reinterpret_cast<const uint16_t*>(v);
+  a.num_tokens = num_tokens;
+  a.hkv = num_kv_heads;
+  a.slot_mapping = slot_mapping;
+  a.slots_total = num_blocks * 16;
+  a.pool = reinterpret_cast<uint8_t*>(pool);
+  a.rec = c->lay.bytes;
+  a.lay = c->lay;
+  a.dev = c->dev;
+  a.num_tiles = (num_tokens + 15) / 16 * num_kv_heads;
+  return c->qjl ? dispatch_m<true>(a, c->kb, c->vb, stream) : dispatch_m<false>(a, c->kb, c->vb, stream);
+}
+
+}  // namespace tq

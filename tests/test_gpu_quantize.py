@@ -179,3 +179,51 @@ def test_full_size_llama_layer_whole_pool():
             print(f"[quantize parity whole pool k{kb}v{vb} head {h}] {T} tokens: differing bits outside band="
                   f"{outside} inside={inside}; band counts {bands[h]}", flush=True)
         assert total_out == 0
+
+
+@pytest.mark.parametrize("kb,vb,mse_only", [(3, 4, False), (3, 2, False), (2, 4, False), (4, 2, False), (4, 4, False),
+                                            (2, 2, True), (3, 4, True), (4, 4, True)])
+def test_large_batch_store_kernel_edges(kb, vb, mse_only):
+    """Batches above 2048 token-heads at head_dim 128 with bf16 inputs run the
+    store kernel whose rotation and QJL projection are on the matrix cores:
+    every preset, with and without QJL, a ragged last tile (2107 token-heads),
+    zero, one-hot and constant keys, constant value groups, huge values and
+    skipped slots, all compared bit for bit with the oracle (outside the
+    1e-6 band)."""
+    T, Hkv, d = 301, 7, 128
+    rng = np.random.default_rng(40 + kb + 10 * vb + (100 if mse_only else 0))
+    K = synth.normal_with_outliers(rng, (T, Hkv, d), 0.005, 20.0)
+    V = synth.normal_with_outliers(rng, (T, Hkv, d), 0.005, 20.0)
+    K[3] = 0.0
+    K[4, 0] = 0.0
+    K[5, 1, :] = 0.0
+    K[5, 1, 7] = 3.0
+    K[6, 0] = synth.bf16_round(np.full(d, 300.0, np.float32))
+    K[300, 6] = 0.0                               # the last token-head of the ragged tile
+    V[7] = 1.5
+    V[8, 0, 32:64] = -2.25
+    V[9, 1] = synth.bf16_round(rng.standard_normal(d).astype(np.float32) * 1000)
+    nb = 40
+    slots = rng.permutation(nb * 16)[:T].astype(np.int64)
+    slots[10] = -1
+    slots[299] = -3
+    prm = oracle_params(40 + kb, d, kb)
+    ctx = tq.tq_codebook_init(d, kb, vb, signs=prm["signs"], S=prm["S"], mse_only=mse_only)
+    k = torch.from_numpy(np.ascontiguousarray(K)).to(torch.bfloat16).cuda()
+    v = torch.from_numpy(np.ascontiguousarray(V)).to(torch.bfloat16).cuda()
+    pool = torch.full((nb, Hkv, ctx.block_bytes), 0xAB, dtype=torch.uint8, device="cuda")
+    tq.tq_quantize_store(ctx, k, v, torch.from_numpy(slots.astype(np.int32)).cuda(), pool)
+    torch.cuda.synchronize()
+    gpu = pool.cpu().numpy()
+    ctx.close()
+    lay = paged.layout(d, kb, vb, qjl=not mse_only)
+    exp = np.full((nb, Hkv, lay["bytes"]), 0xAB, np.uint8)
+    mask = paged.new_pool(nb, Hkv, lay)
+    keep = slots >= 0
+    bands = [expected_records(K[keep, h].astype(np.float64), V[keep, h], slots[keep], h, prm, d, kb, vb, exp, mask,
+                              qjl=not mse_only) for h in range(Hkv)]
+    outside, inside = compare_pools(gpu, exp, mask)
+    print(f"[quantize parity large-batch kernel k{kb}v{vb}{' mse-only' if mse_only else ''}] {T * Hkv} token-heads: "
+          f"differing bits outside band={outside} inside={inside}; codes in band "
+          f"{sum(b['codes'] for b in bands)}", flush=True)
+    assert outside == 0
