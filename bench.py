@@ -106,11 +106,11 @@ def time_total(torch, graphs, reps):
 
 
 # --------------------------------------------------------- decode workload --
-def setup_decode(torch, tq, synth, chunk, copies, mse_only=False):
-    d, B, Hq, Hkv, L, kb, vb, nb, seed = 128, 32, 32, 8, 8192, 3, 4, 16384, 3
+def setup_decode(torch, tq, synth, chunk, copies, mse_only=False, kb=3, vb=4, uniform=False):
+    d, B, Hq, Hkv, L, nb, seed = 128, 32, 32, 8, 8192, 16384, 3
     signs1, signs2, S = synth.method_params(seed, d)
     import numpy as np
-    ctx = tq.tq_codebook_init(d, kb, vb, signs=np.stack([signs1, signs2]), S=S, mse_only=mse_only)
+    ctx = tq.tq_codebook_init(d, kb, vb, signs=np.stack([signs1, signs2]), S=S, mse_only=mse_only, uniform=uniform)
     bt_np = synth.block_table(seed, B, L // 16, nb)
     bt = torch.from_numpy(bt_np).cuda()
     pools = [torch.zeros((nb, Hkv, ctx.block_bytes), dtype=torch.uint8, device="cuda") for _ in range(copies)]
@@ -166,6 +166,23 @@ def decode_step_current_stream(tq, s, i):
                            chunk_tokens=s["chunk"], max_seq_len=s["L"])
 
 
+def spin_up(torch, fn, seconds=0.25, batch=50):
+    """Untimed launches of ``fn`` for at least ``seconds`` of wall time.  The
+    GPU's clocks ramp up under load: after set-up or a pause of a second or
+    two, the first ~150-300 decode launches run 15-25 % slower than the
+    steady state (measured on the split kernel), which a warm-up of a few
+    steps does not cover."""
+    t0 = time.perf_counter()
+    i = 0
+    while True:
+        for _ in range(batch):
+            fn(i)
+            i += 1
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            return
+
+
 def time_eager(torch, fn, reps):
     """Eager launches of ``fn`` (one step each): the mean over ``reps``
     back-to-back steps between two events and two synchronisations, then the
@@ -196,6 +213,7 @@ def time_decode(torch, tq, s, steps, warmup):
     steps and the median step; the same step replayed from HIP graphs for
     comparison; the split kernel's median launch time from back-to-back
     decode-only launches."""
+    spin_up(torch, lambda i: decode_step(tq, s, i))
     for i in range(warmup):
         decode_step(tq, s, i)
     torch.cuda.synchronize()
@@ -203,10 +221,10 @@ def time_decode(torch, tq, s, steps, warmup):
     ms_step, each = time_eager(torch, lambda i: decode_step(tq, s, i), steps)
     n = len(s["pools"])
     step_graphs = [capture(torch, (lambda j: (lambda: decode_step_current_stream(tq, s, j)))(j)) for j in range(n)]
-    for g in step_graphs * 2:
-        g.replay()
+    spin_up(torch, lambda i: step_graphs[i % n].replay(), seconds=0.05)
     graph_ms = time_total(torch, step_graphs, steps)
     del step_graphs
+    spin_up(torch, lambda i: decode_only(tq, s, i), seconds=0.1)
     for i in range(warmup):
         decode_only(tq, s, i)
     split_mean, split_each = time_eager(torch, lambda i: decode_only(tq, s, i), steps)
@@ -216,8 +234,7 @@ def time_decode(torch, tq, s, steps, warmup):
 
 
 def time_split_deterministic(torch, tq, s, steps):
-    for i in range(3):
-        decode_only(tq, s, i, deterministic=True)
+    spin_up(torch, lambda i: decode_only(tq, s, i, deterministic=True), seconds=0.05)
     _, each = time_eager(torch, lambda i: decode_only(tq, s, i, deterministic=True), steps)
     # repeated launches give bit-identical outputs on this schedule
     outs = []
@@ -314,8 +331,7 @@ def setup_ragged(torch, tq, synth):
 
 
 def time_workload(torch, w, reps):
-    for _ in range(3):
-        w["fn"]()
+    spin_up(torch, lambda i: w["fn"](), batch=10)
     _, each = time_eager(torch, lambda i: w["fn"](), reps)
     ms = _median(each)
     tbs = w["kv_bytes"] / (ms * 1e-3) / 1e12
@@ -368,9 +384,7 @@ def setup_prefill(torch, tq, synth):
 
 
 def time_prefill(torch, w, reps):
-    for _ in range(2):
-        w["store"]()
-        w["ext"]()
+    spin_up(torch, lambda i: (w["store"](), w["ext"]()), batch=10)
     _, each = time_eager(torch, lambda i: w["ext"](), reps)
     ext_ms = _median(each)
     _, each = time_eager(torch, lambda i: (w["store"](), w["ext"]()), reps)
@@ -401,8 +415,7 @@ def bench_quantize(torch, tq, synth, reps):
         pool = torch.zeros((nb, Hkv, ctx.block_bytes), dtype=torch.uint8, device="cuda")
         prep = [tq.PreparedQuantize(ctx, ks[c], vs[c], slots, pool) for c in range(copies)]
         fn = lambda i: prep[i % copies]()  # noqa: E731
-        for i in range(3):
-            fn(i)
+        spin_up(torch, fn, batch=20)
         _, each = time_eager(torch, fn, reps)
         ms = _median(each)
         hbm = T * Hkv * (2 * d * 2 + ctx.block_bytes // 16) + T * 4
@@ -534,6 +547,23 @@ def main():
         log(f"MSE-only step {m['ms_per_step'] * 1e3:.1f} us, split median {m['split_median_ms'] * 1e3:.1f} us")
         s.clear()
         torch.cuda.empty_cache()
+        # the same decode workload at K4V4 with the Lloyd-Max codebook (scores
+        # through the LDS pair table) and with the equally spaced one (scores
+        # from the codes arithmetically)
+        cmp = {}
+        for name, uni in (("lloyd_max", False), ("uniform", True)):
+            s = setup_decode(torch, tq, synth, args.chunk, copies=3, kb=4, vb=4, uniform=uni)
+            m = time_decode(torch, tq, s, max(20, args.steps // 2), 3)
+            cmp[name] = {"split_median_ms": round(m["split_median_ms"], 5),
+                         "tbs": round(s["kv_bytes"] / (m["split_median_ms"] * 1e-3) / 1e12, 4)}
+            cmp["kv_bytes_per_call"] = s["kv_bytes"]
+            s.clear()
+            torch.cuda.empty_cache()
+        cmp["workload"] = "decode-b32-hq32-hkv8-d128-ctx8192-k4v4, Lloyd-Max (pair table) vs uniform (arithmetic)"
+        cmp["uniform_speedup"] = round(cmp["lloyd_max"]["split_median_ms"] / cmp["uniform"]["split_median_ms"], 4)
+        workloads["codebook_k4v4"] = cmp
+        log(f"K4V4 split median: Lloyd-Max {cmp['lloyd_max']['split_median_ms'] * 1e3:.1f} us, "
+            f"uniform {cmp['uniform']['split_median_ms'] * 1e3:.1f} us")
         for name, setup in (("long_d256", setup_long), ("ragged_hybrid", setup_ragged)):
             log(f"workload {name}")
             w = setup(torch, tq, synth)

@@ -239,10 +239,10 @@ __device__ __forceinline__ uint32_t opaque_u32(uint32_t x) {
 constexpr int kWaitVm0 = 0x0F70;
 __device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory"); }
 
-template <int D, int GP, int KB, int VB, bool QJ, class Setup>
+template <int D, int GP, int KB, int VB, bool QJ, bool UN, class Setup>
 __device__ void split_cached_chunk(const DArgs& a, int pr, int h, int t0, int t1, const int32_t* s_blk,
                                    const uint2* s_pair, const u32x4* s_sgn, float* s_p, unsigned char* s_main,
-                                   float* s_stat, bf16x8 (&A1)[D / 32][2], bf16x8 (&A3)[D / 32],
+                                   float* s_stat, bf16x8 (&A1)[D / 32][2], bf16x8 (&A3)[D / 32], const f32x4& ucst,
                                    float* m_out, float* l_out, int b, int* s_claim, Setup&& setup) {
   using R = Rec<D, KB, VB, QJ>;
   constexpr int NW = split_waves<D, GP>();
@@ -321,6 +321,7 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h, int t0, int t1
   for (int g = 0; g < GP; ++g) m_run[g] = -INFINITY;
   float lsum[4] = {0.f, 0.f, 0.f, 0.f};  // per-lane partial sums (rows of lanes 0..31)
   const uint32_t c1024 = opaque_u32(0x64006400u);  // two fp16 1024.0
+  const uint32_t k4300 = UN ? opaque_u32(0x43004300u) : 0u;  // two bf16 128.0
   const f16x8 k1024 = __builtin_bit_cast(f16x8, u32x4{c1024, c1024, c1024, c1024});
   const int arow = lane & 15;
   // VB = 2: lane column j takes bytes 2 (j >> 3) and 2 (j >> 3) + 1 of its dword column
@@ -359,7 +360,9 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h, int t0, int t1
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const unsigned char* hb = sb + half * R::bytes;
-      f32x4 am = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
+      // equally spaced codebook: the accumulator starts at the rows' offset
+      // constant (see the arithmetic operands below)
+      f32x4 am = UN ? ucst : f32x4{0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
       uint32_t cw[QW + 1];
 #pragma unroll
       for (int i = 0; i < QW; ++i) cw[i] = *reinterpret_cast<const uint32_t*>(hb + off_kc + 4 * i);
@@ -377,14 +380,29 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h, int t0, int t1
         const int bp = kt * TB;
         const uint32_t win =
             bp % 32 == 0 ? cw[bp / 32] : __builtin_amdgcn_alignbit(cw[bp / 32 + 1], cw[bp / 32], bp % 32);
-        // pair entries {hi, lo}: MFMA m takes pairs 2m, 2m+1 (coordinates 4m .. 4m+3)
-        uint2 pe[4];
+        if constexpr (UN) {
+          // c[idx] = c0 + step idx needs no table: B element = bf16 of
+          // 128 + idx (0x4300 | idx, exact), built from the code bits alone.
+          // Dword j holds codes j and j + 4 of the slice: y has codes 0-3 in
+          // its low half and codes 4-7 in its high half, so one shift and one
+          // and-or place both.
+          constexpr uint32_t m4 = (1u << (4 * KB)) - 1u;
+          const uint32_t y = (win & m4) | ((win << (16 - 4 * KB)) & (m4 << 16));
+          constexpr uint32_t m2 = ((1u << KB) - 1u) * 0x00010001u;
+          u32x4 bu;
 #pragma unroll
-        for (int pi = 0; pi < 4; ++pi) pe[pi] = s_pair[(win >> (2 * KB * pi)) & ((1u << (2 * KB)) - 1u)];
-        const u32x4 b0 = {pe[0].x, pe[0].y, pe[1].x, pe[1].y};
-        const u32x4 b1 = {pe[2].x, pe[2].y, pe[3].x, pe[3].y};
-        am = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1[kt][0], __builtin_bit_cast(bf16x8, b0), am, 0, 0, 0);
-        am = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1[kt][1], __builtin_bit_cast(bf16x8, b1), am, 0, 0, 0);
+          for (int j = 0; j < 4; ++j) bu[j] = and_or(y >> (KB * j), m2, k4300);
+          am = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1[kt][0], __builtin_bit_cast(bf16x8, bu), am, 0, 0, 0);
+        } else {
+          // pair entries {hi, lo}: MFMA m takes pairs 2m, 2m+1 (coordinates 4m .. 4m+3)
+          uint2 pe[4];
+#pragma unroll
+          for (int pi = 0; pi < 4; ++pi) pe[pi] = s_pair[(win >> (2 * KB * pi)) & ((1u << (2 * KB)) - 1u)];
+          const u32x4 b0 = {pe[0].x, pe[0].y, pe[1].x, pe[1].y};
+          const u32x4 b1 = {pe[2].x, pe[2].y, pe[3].x, pe[3].y};
+          am = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1[kt][0], __builtin_bit_cast(bf16x8, b0), am, 0, 0, 0);
+          am = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1[kt][1], __builtin_bit_cast(bf16x8, b1), am, 0, 0, 0);
+        }
         if constexpr (QJ) {
           const u32x4 bq = s_sgn[(kj[kt / 4] >> (8 * (kt % 4))) & 0xFFu];
           aq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A3[kt], __builtin_bit_cast(bf16x8, bq), aq, 0, 0, 0);
@@ -956,7 +974,9 @@ __device__ __forceinline__ void rotate_project(const DArgs& a, const DevTables& 
 // every workgroup runs at start-up; workgroup w takes the contiguous range
 // [w total / grid, (w + 1) total / grid), so consecutive items mostly share
 // (b, h) and reuse its rotated query operands.
-template <int D, int GP, int KB, int VB, bool QJ>
+// UN: the preset's codebook is equally spaced (c_k = c0 + k step) and the
+// score takes c[idx] arithmetically instead of from the pair table.
+template <int D, int GP, int KB, int VB, bool QJ, bool UN>
 __global__ __launch_bounds__((split_waves<D, GP>() * 64)) void decode_split_kernel(DArgs a, int pr) {
   constexpr int NW = split_waves<D, GP>();
   constexpr int KT = D / 32;
@@ -983,7 +1003,8 @@ __global__ __launch_bounds__((split_waves<D, GP>() * 64)) void decode_split_kern
   static_assert((1 << (2 * KB)) <= NW * 64, "one centroid pair per thread");
   // loaded here, stored after the scan's first loads are issued, so the two
   // global round trips overlap
-  const uint2 pair_v = tid < (1 << (2 * KB)) ? make_uint2(dv.pair_lut[2 * tid], dv.pair_lut[2 * tid + 1]) : make_uint2(0u, 0u);
+  const uint2 pair_v = !UN && tid < (1 << (2 * KB)) ? make_uint2(dv.pair_lut[2 * tid], dv.pair_lut[2 * tid + 1])
+                                                     : make_uint2(0u, 0u);
   {
     u32x4 w;
 #pragma unroll
@@ -993,7 +1014,8 @@ __global__ __launch_bounds__((split_waves<D, GP>() * 64)) void decode_split_kern
   }
 
   bf16x8 A1[KT][2], A3[KT];
-  int ready_bh = -1;  // (b, h) whose query operands A1 / A3 hold
+  f32x4 ucst = {0.f, 0.f, 0.f, 0.f};  // equally spaced codebook: score rows' offsets
+  int ready_bh = -1;  // (b, h) whose query operands A1 / A3 / ucst hold
 
   // One item: split c of KV head h of sequence b, which has Lc cached tokens.
   // kDirect: at most one split per sequence (the output is written here).
@@ -1065,6 +1087,7 @@ __global__ __launch_bounds__((split_waves<D, GP>() * 64)) void decode_split_kern
         };
         const float* xq = s_q + (used ? g : 0) * D;
         const float* yq = s_pq + (used ? g : 0) * D;
+        float usum = 0.f;
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt) {
           const int j0 = kq * (D / 4) + 8 * kt;
@@ -1081,18 +1104,43 @@ __global__ __launch_bounds__((split_waves<D, GP>() * 64)) void decode_split_kern
               w3[e / 2] = split(ys[e] * (kappa * a.logit_scale)) | (split(ys[e + 1] * (kappa * a.logit_scale)) << 16);
             A3r[kt] = __builtin_bit_cast(bf16x8, w3);
           }
+          if constexpr (UN) {
+            // slot 2j = coordinate j, slot 2j + 1 = coordinate j + 4 of the
+            // slice (the code order of the arithmetic B operand), with the
+            // codebook step folded in; usum collects the operand values
+            const float ls = a.logit_scale * dv.uni_step;
+            u32x4 w1;
 #pragma unroll
-          for (int m = 0; m < 2; ++m) {
-            const float ls = a.logit_scale;
-            const uint32_t c01 = split(xs[4 * m] * ls) | (split(xs[4 * m + 1] * ls) << 16);
-            const uint32_t c23 = split(xs[4 * m + 2] * ls) | (split(xs[4 * m + 3] * ls) << 16);
-            A1r[kt][m] = __builtin_bit_cast(bf16x8, u32x4{c01, c01, c23, c23});
+            for (int j = 0; j < 4; ++j) {
+              const uint32_t lo = split(xs[j] * ls), hi = split(xs[j + 4] * ls);
+              usum += __uint_as_float(lo << 16) + __uint_as_float(hi << 16);
+              w1[j] = lo | (hi << 16);
+            }
+            A1r[kt][0] = __builtin_bit_cast(bf16x8, w1);
+          } else {
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+              const float ls = a.logit_scale;
+              const uint32_t c01 = split(xs[4 * m] * ls) | (split(xs[4 * m + 1] * ls) << 16);
+              const uint32_t c23 = split(xs[4 * m + 2] * ls) | (split(xs[4 * m + 3] * ls) << 16);
+              A1r[kt][m] = __builtin_bit_cast(bf16x8, u32x4{c01, c01, c23, c23});
+            }
           }
+        }
+        if constexpr (UN) {
+          // Sum_j a_j (128 + idx_j) - (128 + (L-1)/2) Sum_j a_j
+          //   = Sum_j a_j (idx_j - (L-1)/2) = Sum_j a_j (c[idx_j] - c0) / step + ...,
+          // i.e. with c_k = (k - (L-1)/2) step the row's codebook term: the
+          // offset is the accumulator's start value, per output row 4 (lane / 16) + r
+          usum = lane_swap32_sum(lane_swap16_sum(usum));  // the row's operand sum (all 4 quarters)
+          const float off = -(128.0f + 0.5f * (float)((1 << KB) - 1));
+#pragma unroll
+          for (int r = 0; r < 4; ++r) ucst[r] = off * __shfl(usum, 4 * kq + r);
         }
         ready_bh = bh;
       };
-      split_cached_chunk<D, GP, KB, VB, QJ>(a, pr, h, t0, t1, s_blk, s_pair, s_sgn, s_p, s_main, s_stat, A1, A3,
-                                        s_m, s_l, b, s_claim, setup);
+      split_cached_chunk<D, GP, KB, VB, QJ, UN>(a, pr, h, t0, t1, s_blk, s_pair, s_sgn, s_p, s_main, s_stat, A1,
+                                                A3, ucst, s_m, s_l, b, s_claim, setup);
     } else if (!kDirect) {
       split_recent<D, GP>(a, b, h, seq_recent(a, b), s_p, s_merge, s_m, s_l);
     }
@@ -1123,7 +1171,7 @@ __global__ __launch_bounds__((split_waves<D, GP>() * 64)) void decode_split_kern
   if (a.direct) {
     // one item per (sequence, KV head), contiguous ranges per workgroup: no
     // work list is needed
-    if (tid < (1 << (2 * KB))) s_pair[tid] = pair_v;
+    if (!UN && tid < (1 << (2 * KB))) s_pair[tid] = pair_v;
     const int total = a.B * a.Hkv;
     const int i0 = (int)((int64_t)blockIdx.x * total / gridDim.x);
     const int i1 = (int)((int64_t)(blockIdx.x + 1) * total / gridDim.x);
@@ -1145,7 +1193,7 @@ __global__ __launch_bounds__((split_waves<D, GP>() * 64)) void decode_split_kern
       const int items = (bb < a.B && seq_preset_of(a, bb) == pr) ? a.Hkv * seq_splits(a, bb) : 0;
       int* sc = s_scan + base;
       if (bb < a.B) sc[tid] = items;
-      if (base == 0 && tid < (1 << (2 * KB))) s_pair[tid] = pair_v;
+      if (!UN && base == 0 && tid < (1 << (2 * KB))) s_pair[tid] = pair_v;
       __syncthreads();
       // Hillis-Steele inclusive scan of this block of 256 entries, in place
       for (int off = 1; off < NW * 64; off <<= 1) {
@@ -1261,9 +1309,9 @@ struct SplitLaunchCache {
   } dev[16];
 };
 
-template <int D, int GP, int KB, int VB, bool QJ>
+template <int D, int GP, int KB, int VB, bool QJ, bool UN = false>
 static hipError_t launch_split(const DArgs& a, int pr, hipStream_t s, bool dry_run) {
-  auto kern = decode_split_kernel<D, GP, KB, VB, QJ>;
+  auto kern = decode_split_kernel<D, GP, KB, VB, QJ, UN>;
   using SL = SplitLds<D, GP, KB, VB, QJ>;
   static SplitLaunchCache cache;
   int dev = 0;
@@ -1311,6 +1359,9 @@ static hipError_t launch_split(const DArgs& a, int pr, hipStream_t s, bool dry_r
 
 template <int D, int GP, bool QJ>
 static hipError_t dispatch_preset(const DArgs& a, int pr, int kb, int vb, hipStream_t s, bool dry) {
+  // 4-bit equally spaced codebooks take the arithmetic score path
+  if (kb == 4 && a.dev[pr].uni_step != 0.f)
+    return vb == 2 ? launch_split<D, GP, 4, 2, QJ, true>(a, pr, s, dry) : launch_split<D, GP, 4, 4, QJ, true>(a, pr, s, dry);
   if (kb == 2) return vb == 2 ? launch_split<D, GP, 2, 2, QJ>(a, pr, s, dry) : launch_split<D, GP, 2, 4, QJ>(a, pr, s, dry);
   if (kb == 3) return vb == 2 ? launch_split<D, GP, 3, 2, QJ>(a, pr, s, dry) : launch_split<D, GP, 3, 4, QJ>(a, pr, s, dry);
   return vb == 2 ? launch_split<D, GP, 4, 2, QJ>(a, pr, s, dry) : launch_split<D, GP, 4, 4, QJ>(a, pr, s, dry);

@@ -440,6 +440,8 @@ extern "C" int tq_codebook_init(const tq_preset* p, const int8_t* signs, const f
   c->dev.pair_lut = (const uint32_t*)(base + o_pair);
   c->dev.pair_lut_f16 = (const uint32_t*)(base + o_pair16);
   c->dev.s_tiles_perm_d2 = tiles_perm.empty() ? nullptr : (const uint16_t*)(base + o_perm);
+  // equally spaced codebook: c_k = (k - (L-1)/2) step, so c[1] - c[0] is the step
+  c->dev.uni_step = (p->flags & TQ_PRESET_UNIFORM) ? (float)(c->c64[1] - c->c64[0]) : 0.f;
   *out = c;
   return TQ_OK;
 }

@@ -37,6 +37,10 @@ struct DevTables {
   // j = 32 kt + 16 (e / 4) + 4 (l / 16) + e % 4, fp16 hi / lo;
   // layout [nt][kt][hi, lo][64][8] fp16 (empty for head_dim 256).
   const uint16_t* s_tiles_perm_d2 = nullptr;
+  // Equally spaced codebook (c_k = c0 + k step, c0 = -(L-1) step / 2): the
+  // step, which the decode uses to take c[idx] arithmetically; 0 for a
+  // Lloyd-Max codebook.
+  float uni_step = 0.f;
 };
 
 struct Layout {

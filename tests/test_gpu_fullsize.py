@@ -12,7 +12,8 @@ bf16 window's.  The pairs run on a host thread pool with one BLAS thread each.
 Workloads:
   * decode: B=32, Hq=32, Hkv=8, d=128, 8192 cached tokens, K3V4, a
     16384-block pool through a permuted block table (QJL and MSE-only keys,
-    and the deterministic schedule);
+    and the deterministic schedule); the same shape with a 4-bit equally
+    spaced key codebook (K4V4, the arithmetic score path);
   * long: B=8, Hq=16, Hkv=4, d=256, 131072 cached tokens, K4V4, a
     65536-block pool;
   * ragged: B=64, Hq=32, Hkv=8, d=128, lognormal lengths (median 16384,
@@ -122,6 +123,26 @@ def test_decode_workload_full_size_all_pairs(mse_only, deterministic):
     label = f"decode b32 ctx8192 k3v4{' mse-only' if mse_only else ''}{' deterministic' if deterministic else ''}"
     _check_all_pairs(label, [pool.cpu().numpy()], [paged.layout(d, kb, vb, qjl=not mse_only)], [prm], bt_np, lens,
                      q, G, out, scores)
+    ctx.close()
+
+
+def test_uniform_k4v4_decode_workload_full_size_all_pairs():
+    """The decode workload's shape with a 4-bit equally spaced key codebook,
+    which the decode scores arithmetically (c0 + idx * step, no pair table)."""
+    d, B, Hq, Hkv, L, kb, vb, nb, seed = 128, 32, 32, 8, 8192, 4, 4, 16384, 6
+    G = Hq // Hkv
+    prm = oracle_params(seed, d, kb, uniform=True)
+    ctx = tq.tq_codebook_init(d, kb, vb, signs=prm["signs"], S=prm["S"], uniform=True)
+    bt_np = synth.block_table(seed, B, L // 16, nb)
+    bt = torch.from_numpy(bt_np).cuda()
+    pool = torch.zeros((nb, Hkv, ctx.block_bytes), dtype=torch.uint8, device="cuda")
+    lens = np.full(B, L)
+    _fill(ctx, pool, bt, lens, Hkv, d, seed, 0.005, 20.0)
+    q = synth.bf16_round(synth.queries(seed, B, Hq, d))
+    qd = torch.from_numpy(q).to(torch.bfloat16).cuda()
+    out, scores = _decode(qd, [ctx], [pool], bt, torch.from_numpy(lens.astype(np.int32)).cuda(), L)
+    _check_all_pairs("decode b32 ctx8192 uniform k4v4", [pool.cpu().numpy()], [paged.layout(d, kb, vb)], [prm], bt_np,
+                     lens, q, G, out, scores)
     ctx.close()
 
 

@@ -1,11 +1,13 @@
 """GPU parity of the equally spaced key codebook (Roadmap §4.3, "tq4u":
 centroids idx * step + c0 with the least-squares step) against the oracle.
 
-The kernels take the codebook from the context's tables, so this checks the
-library's solver (fp32 tables identical to the oracle's) end to end: records
-bit-exact outside the 1e-6 band through both quantise kernels, and decode
+The quantise kernels take the codebook from the context's tables, so this
+checks the library's solver (fp32 tables identical to the oracle's) end to
+end: records bit-exact outside the 1e-6 band through both quantise kernels.
+The decode of 4-bit uniform presets takes c[idx] = c0 + idx * step
+arithmetically (no pair table); other widths use the table path.  Decode
 scores / outputs within 1e-3 on oracle-written caches, with and without the
-QJL sketch.
+QJL sketch, head_dim 128 and 256, four and eight query heads per KV head.
 """
 
 import numpy as np
@@ -64,9 +66,16 @@ def test_uniform_codebook_quantize(d, kb, vb, T, Hkv, mse_only):
     assert outside == 0
 
 
-@pytest.mark.parametrize("kb,vb,chunk,mse_only", [(4, 4, 512, False), (3, 2, 2048, False), (4, 4, 256, True)])
-def test_uniform_codebook_decode(kb, vb, chunk, mse_only):
-    seed, d, B, Hq, Hkv = 112 + kb, 128, 4, 8, 2
+@pytest.mark.parametrize("d,Hq,kb,vb,chunk,mse_only", [
+    (128, 8, 4, 4, 512, False),    # 4-bit: the arithmetic score path (no pair table)
+    (128, 8, 3, 2, 2048, False),   # 3-bit: the table path with the uniform table
+    (128, 8, 4, 4, 256, True),
+    (256, 8, 4, 4, 1024, False),
+    (128, 16, 4, 2, 512, False),   # eight query heads per KV head
+    (256, 16, 4, 4, 4096, True),
+])
+def test_uniform_codebook_decode(d, Hq, kb, vb, chunk, mse_only):
+    seed, B, Hkv = 112 + kb, 4, 2
     lens = np.array([1000, 33, 0, 2000])
     prm = oracle_params(seed, d, kb, uniform=True)
     prm["qjl"] = not mse_only
@@ -97,6 +106,6 @@ def test_uniform_codebook_decode(kb, vb, chunk, mse_only):
         if s.shape[1]:
             errs.append(score_errors(sc[b, :, :s.shape[1]].astype(np.float64), s))
     se, oe = max(errs), output_errors(out.astype(np.float64), np.stack(ref))
-    print(f"[uniform decode parity k{kb}v{vb} chunk {chunk} mse_only={mse_only}] max score err {se:.2e} "
+    print(f"[uniform decode parity d{d} G{Hq // Hkv} k{kb}v{vb} chunk {chunk} mse_only={mse_only}] max score err {se:.2e} "
           f"max out err {oe:.2e}", flush=True)
     assert np.all(np.isfinite(out)) and se <= TOL and oe <= TOL
