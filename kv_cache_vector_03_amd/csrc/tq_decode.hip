@@ -240,7 +240,7 @@ constexpr int kWaitVm0 = 0x0F70;
 __device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory"); }
 
 template <int D, int GP, int KB, int VB, bool QJ, bool UN, class Setup>
-__device__ void split_cached_chunk(const DArgs& a, int pr, int h, int t0, int t1, const int32_t* s_blk,
+__device__ void split_cached_chunk(const DArgs& a, int pr, int h_, int t0_, int t1_, const int32_t* s_blk,
                                    const uint2* s_pair, const u32x4* s_sgn, float* s_p, unsigned char* s_main,
                                    float* s_stat, bf16x8 (&A1)[D / 32][2], bf16x8 (&A3)[D / 32], const f32x4& ucst,
                                    float* m_out, float* l_out, int b, int* s_claim, Setup&& setup) {
@@ -257,7 +257,12 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h, int t0, int t1
   constexpr int DPS = 2 * DPR;                // DMA instructions per step
   static_assert((R::nslot - 1) * DPS < 64, "vmcnt range");
   static_assert(PPR >= 64, "a record spans at least one full DMA window");
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index, KV head and token range are wave-uniform: saying so keeps
+  // the step schedule below (ring slots, claims, waits) and the record
+  // addresses in scalar registers and scalar branches
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = __builtin_amdgcn_readfirstlane(h_);
+  const int t0 = __builtin_amdgcn_readfirstlane(t0_), t1 = __builtin_amdgcn_readfirstlane(t1_);
   const int tok = lane & 15, kq = lane >> 4;
   const uint8_t* pool = a.pool[pr];
   const int64_t rec = a.rec[pr];
