@@ -519,11 +519,15 @@ def main():
     dec = time_decode(torch, tq, s, args.steps, args.warmup)
     ms_step = dec["ms_per_step"]
     value = s["kv_bytes"] / (ms_step * 1e-3) / 1e12
-    split_ms = dec["split_median_ms"]
+    # the kernel's average launch duration: back-to-back split-only launches
+    # between two events (no events between the launches, whose own packets
+    # add a few microseconds to each interval: the kernel trace's average
+    # duration agrees with this figure)
+    split_ms = dec["split_mean_ms"]
     achieved = s["kv_bytes"] / (split_ms * 1e-3) / 1e9
     log(f"decode step {ms_step * 1e3:.1f} us (median {dec['median_ms_per_step'] * 1e3:.1f}, graph replay "
-        f"{dec['graph_ms_per_step'] * 1e3:.1f}), split kernel median {split_ms * 1e3:.1f} us "
-        f"(mean {dec['split_mean_ms'] * 1e3:.1f})")
+        f"{dec['graph_ms_per_step'] * 1e3:.1f}), split kernel mean {split_ms * 1e3:.1f} us "
+        f"(median of event intervals {dec['split_median_ms'] * 1e3:.1f})")
     det_ms, det_equal = time_split_deterministic(torch, tq, s, args.steps)
     log(f"deterministic split median {det_ms * 1e3:.1f} us, repeat bit-identical: {det_equal}")
     for p in s["pools"]:
@@ -611,11 +615,13 @@ def main():
         "graph_replay_ms_per_step": round(dec["graph_ms_per_step"], 5),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_TBS * 1000, "unit": "GB/s",
                      "frac": round(achieved / (HBM_PEAK_TBS * 1000), 4), "traffic": traffic,
-                     "kernel": "decode_split_kernel<128,4,3,4,true>", "bytes_per_launch": kv_bytes,
-                     "median_launch_ms": round(split_ms, 5), "mean_launch_ms": round(dec["split_mean_ms"], 5),
-                     "min_launch_ms": round(dec["split_min_ms"], 5),
-                     "timing": "median of per-launch event intervals over back-to-back eager split-only "
-                               "launches (3 pool copies in turn), events recorded between the library calls",
+                     "kernel": "decode_split_kernel<128,4,3,4,true,false>", "bytes_per_launch": kv_bytes,
+                     "mean_launch_ms": round(split_ms, 5),
+                     "median_event_interval_ms": round(dec["split_median_ms"], 5),
+                     "min_event_interval_ms": round(dec["split_min_ms"], 5),
+                     "timing": "mean launch duration over K back-to-back eager split-only launches (3 pool "
+                               "copies in turn) between two events; the per-launch event intervals of a "
+                               "second pass (events between the library calls) are reported beside it",
                      "consistent_with_step": bool(split_ms <= ms_step and achieved >= kv_bytes / (ms_step * 1e-3) / 1e9)},
         "workloads": workloads,
         "cpu_baseline": cpu,
