@@ -75,6 +75,11 @@ __device__ __forceinline__ float row_sum4(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 constexpr int parity(int x) { return __builtin_popcount(x) & 1; }
+// a value the compiler cannot see through (keeps a select as bit operations)
+__device__ __forceinline__ uint32_t opaque_mask(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
 
 template <int KB, int VB, bool QJ>
 __global__ __launch_bounds__(mwaves<QJ>() * 64) void quantize_mfma_kernel(QMArgs a) {
@@ -295,8 +300,11 @@ __global__ __launch_bounds__(mwaves<QJ>() * 64) void quantize_mfma_kernel(QMArgs
         auto b = __builtin_amdgcn_permlane16_swap(x, x, false, false);
         wds[nt] = b[0] | b[1];
       }
+      // a bitwise select: written as (g & 1) ? wds[4 + i] : wds[i] the compiler
+      // turns it into a lane-indexed load from a stack copy of wds
+      const uint32_t odd = opaque_mask((g & 1) ? ~0u : 0u);
 #pragma unroll
-      for (int i = 0; i < CPL; ++i) cst[i] = (g & 1) ? wds[4 + i] : wds[i];
+      for (int i = 0; i < CPL; ++i) cst[i] = (wds[4 + i] & odd) | (wds[i] & ~odd);
     }
 
     // ---- store the key record
