@@ -81,6 +81,93 @@ double first_moment(double a, double b, int twice_m) {
 
 using namespace tq;
 
+namespace {
+// Lloyd's conditions t_j = (c_j + c_{j+1}) / 2, with c_k the conditional mean
+// of cell k = (t_{k-1}, t_k], solved by Newton's method on the L - 1
+// thresholds.  Lloyd's iteration contracts by only ~1 - O(1/L^2) per step,
+// so with many levels (more than 4 bits) it is run a little and this
+// finishes the fixed point.  A cell's mean moves with its edges as
+// dc_k/dt_k = f(t_k)(t_k - c_k)/P_k and dc_k/dt_{k-1} = f(t_{k-1})(c_k - t_{k-1})/P_k,
+// so the Jacobian is tridiagonal (Thomas algorithm); steps are halved until
+// the thresholds stay ordered in (-1, 1) and the residual drops, and the
+// iterate is kept odd-symmetric.  c: centroids in, centroids out.
+void newton_refine(int d, std::vector<double>& c) {
+  const int L = (int)c.size(), n = L - 1, tm = d - 3;
+  const double m = 0.5 * tm;
+  std::vector<double> t(n), P(L), cc(L), F(n), tn(n), Pn(L), ccn(L), Fn(n);
+  std::vector<double> a(n), b(n), cu(n), delta(n);
+  for (int k = 0; k < n; ++k) t[k] = 0.5 * (c[k] + c[k + 1]);
+  // cell masses and the density without the normaliser B (it cancels in
+  // the means and in f / P)
+  auto eval = [&](const std::vector<double>& tt, std::vector<double>& PP, std::vector<double>& CC, std::vector<double>& FF) {
+    double fmax = 0.0;
+    for (int k = 0; k < L; ++k) {
+      const double lo = k == 0 ? -1.0 : tt[k - 1], hi = k == L - 1 ? 1.0 : tt[k];
+      PP[k] = J(lo, hi, tm);
+      CC[k] = first_moment(lo, hi, tm) / PP[k];
+    }
+    for (int j = 0; j < n; ++j) {
+      FF[j] = tt[j] - 0.5 * (CC[j] + CC[j + 1]);
+      fmax = std::max(fmax, std::fabs(FF[j]));
+    }
+    return fmax;
+  };
+  double f0 = eval(t, P, cc, F);
+  for (int it = 0; it < 200; ++it) {
+    double cmax = 0.0;
+    for (int k = 0; k < L; ++k) cmax = std::max(cmax, std::fabs(cc[k]));
+    if (f0 <= 1e-15 * cmax) break;
+    for (int j = 0; j < n; ++j) {
+      const double fj = pow_1mu2(t[j], m);  // (1 - t^2)^m, the density times B
+      const double up = fj * (t[j] - cc[j]) / P[j];          // dc_j / dt_j
+      const double lo = fj * (cc[j + 1] - t[j]) / P[j + 1];  // dc_{j+1} / dt_j
+      b[j] = 1.0 - 0.5 * (up + lo);
+      if (j + 1 < n) a[j + 1] = -0.5 * lo;  // dF_{j+1} / dt_j
+      if (j > 0) cu[j - 1] = -0.5 * up;     // dF_{j-1} / dt_j
+    }
+    // tridiagonal solve (Thomas): a sub-, b main, cu super-diagonal
+    std::vector<double> cp(n), dp(n);
+    cp[0] = n > 1 ? cu[0] / b[0] : 0.0;
+    dp[0] = -F[0] / b[0];
+    for (int j = 1; j < n; ++j) {
+      const double den = b[j] - a[j] * cp[j - 1];
+      cp[j] = j + 1 < n ? cu[j] / den : 0.0;
+      dp[j] = (-F[j] - a[j] * dp[j - 1]) / den;
+    }
+    delta[n - 1] = dp[n - 1];
+    for (int j = n - 2; j >= 0; --j) delta[j] = dp[j] - cp[j] * delta[j + 1];
+    double lam = 1.0, fn = 0.0;
+    bool ok = false;
+    while (lam >= 1e-12) {
+      for (int j = 0; j < n; ++j) tn[j] = t[j] + lam * delta[j];
+      for (int j = 0; j < n / 2; ++j) {
+        const double s = 0.5 * (tn[j] - tn[n - 1 - j]);
+        tn[j] = s;
+        tn[n - 1 - j] = -s;
+      }
+      if (n % 2) tn[n / 2] = 0.0;
+      bool ordered = tn[0] > -1.0 && tn[n - 1] < 1.0;
+      for (int j = 1; j < n && ordered; ++j) ordered = tn[j] > tn[j - 1];
+      if (ordered) {
+        fn = eval(tn, Pn, ccn, Fn);
+        if (fn < f0 || lam < 1e-6) {
+          ok = true;
+          break;
+        }
+      }
+      lam *= 0.5;
+    }
+    if (!ok) break;
+    t.swap(tn);
+    P.swap(Pn);
+    cc.swap(ccn);
+    F.swap(Fn);
+    f0 = fn;
+  }
+  for (int k = 0; k < L; ++k) c[k] = 0.5 * (cc[k] - cc[L - 1 - k]);
+}
+}  // namespace
+
 extern "C" int tq_lloyd_max(int32_t d, int32_t bits, double* centroids, double* thresholds) {
   if (d < 4 || (d & 1) || bits < 1 || bits > 8 || !centroids || !thresholds) {
     set_error("tq_lloyd_max: need even head_dim >= 4, bits in 1..8 and non-NULL outputs");
@@ -93,7 +180,10 @@ extern "C" int tq_lloyd_max(int32_t d, int32_t bits, double* centroids, double* 
   // single fixed point and converges to it from any ordered start.
   std::vector<double> c(L), t(L - 1), cn(L), lo(L), hi(L);
   for (int k = 0; k < L; ++k) c[k] = (2.0 * k + 1.0 - L) / L * 2.0 / std::sqrt((double)d);
-  for (int it = 0; it < 100000; ++it) {
+  // beyond 4 bits Lloyd's iteration only brings the codebook near the fixed
+  // point, which newton_refine then solves
+  const int lloyd_iters = bits <= 4 ? 100000 : 200;
+  for (int it = 0; it < lloyd_iters; ++it) {
     for (int k = 0; k + 1 < L; ++k) t[k] = 0.5 * (c[k] + c[k + 1]);
     for (int k = 0; k < L; ++k) {
       double a = k == 0 ? -1.0 : t[k - 1];
@@ -111,6 +201,7 @@ extern "C" int tq_lloyd_max(int32_t d, int32_t bits, double* centroids, double* 
     c = lo;
     if (delta <= 1e-15 * cmax) break;
   }
+  if (bits > 4) newton_refine(d, c);
   for (int k = 0; k + 1 < L; ++k) t[k] = 0.5 * (c[k] + c[k + 1]);
   std::memcpy(centroids, c.data(), sizeof(double) * L);
   std::memcpy(thresholds, t.data(), sizeof(double) * (L - 1));

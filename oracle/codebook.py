@@ -2,8 +2,8 @@
 
 Hub, "technical principle", steps 1-2: after the random orthogonal rotation
 each coordinate of the (unit) key direction follows a Beta-type law, and the
-method precomputes optimal (Lloyd-Max) scalar codebooks of 2, 3 and 4 bits for
-head_dim 128 and 256; quantising a coordinate means finding its nearest
+method precomputes optimal (Lloyd-Max) scalar codebooks (here of 2, 3, 4 and,
+for MSE-only keys, 8 bits) for head_dim 128 and 256; quantising a coordinate means finding its nearest
 codeword.  iThome, "the core idea of TurboQuant": for MSE, each rotated
 coordinate is given its closest optimal centroid.
 
@@ -103,7 +103,20 @@ def _initial_centroids(d: int, levels: int) -> np.ndarray:
     return cell_first_moment(edges[:-1], edges[1:], d) / cell_mass(edges[:-1], edges[1:], d)
 
 
+_SOLVED = {}  # (d, bits, tol, max_iter) -> (centroids, thresholds, iterations); the solve is deterministic
+
+
 def lloyd_max(d: int, bits: int, tol: float = 1e-14, max_iter: int = 100000):
+    """Lloyd-Max codebook (see _lloyd_max); solved once per argument set and
+    returned as fresh copies."""
+    key = (int(d), int(bits), float(tol), int(max_iter))
+    if key not in _SOLVED:
+        _SOLVED[key] = _lloyd_max(d, bits, tol, max_iter)
+    c, t, it = _SOLVED[key]
+    return c.copy(), t.copy(), it
+
+
+def _lloyd_max(d: int, bits: int, tol: float, max_iter: int):
     """Run Lloyd's iteration to a fixed point.
 
     Stops when no centroid moves by more than ``tol`` times the largest
@@ -114,7 +127,9 @@ def lloyd_max(d: int, bits: int, tol: float = 1e-14, max_iter: int = 100000):
     c = _initial_centroids(d, levels)
     c = 0.5 * (c - c[::-1])
     it = 0
-    for it in range(1, max_iter + 1):
+    # beyond 4 bits Lloyd's iteration only brings the codebook near the fixed
+    # point, which Newton's method then solves (see _newton_refine)
+    for it in range(1, (max_iter if bits <= 4 else 200) + 1):
         t = 0.5 * (c[:-1] + c[1:])
         lo = np.concatenate(([-1.0], t))
         hi = np.concatenate((t, [1.0]))
@@ -124,8 +139,68 @@ def lloyd_max(d: int, bits: int, tol: float = 1e-14, max_iter: int = 100000):
         c = c_new
         if delta <= tol * float(np.max(np.abs(c))):
             break
+    if bits > 4:  # many levels: finish the fixed point by Newton's method
+        c = _newton_refine(d, c)
     t = 0.5 * (c[:-1] + c[1:])
     return c, t, it
+
+
+def _newton_refine(d: int, c: np.ndarray, tol: float = 1e-15, max_iter: int = 200) -> np.ndarray:
+    """Solve Lloyd's conditions with Newton's method on the thresholds.
+
+    Lloyd's iteration (above) converges slowly when there are many levels:
+    its error shrinks by a factor ~1 - O(1/L^2) per step, so at 6-8 bits it
+    stops far from the fixed point.  The fixed point is the same set of
+    equations, F_j(t) = t_j - (c_j(t) + c_{j+1}(t)) / 2 = 0 for the L - 1
+    thresholds, where c_k(t) is the conditional mean of cell k (bounded by
+    t_{k-1} and t_k).  A cell's mean moves with its edges as
+    dc_k/dt_k = f(t_k) (t_k - c_k) / P_k and dc_k/dt_{k-1} = f(t_{k-1})
+    (c_k - t_{k-1}) / P_k (Leibniz's rule on E[U 1]/P), so the Jacobian is
+    tridiagonal and each Newton step is one banded solve.  Steps are halved
+    until the thresholds stay ordered inside (-1, 1) and the residual drops;
+    the iterate is kept odd-symmetric.  Starts from the centroids ``c`` and
+    returns the centroids of the solution."""
+    from scipy.linalg import solve_banded
+
+    L = len(c)
+    t = 0.5 * (c[:-1] + c[1:])
+
+    def cells(t):
+        lo = np.concatenate(([-1.0], t))
+        hi = np.concatenate((t, [1.0]))
+        m = cell_mass(lo, hi, d)
+        return m, cell_first_moment(lo, hi, d) / m
+
+    def resid(t):
+        m, cc = cells(t)
+        return t - 0.5 * (cc[:-1] + cc[1:]), m, cc
+
+    F, m, cc = resid(t)
+    for _ in range(max_iter):
+        if float(np.max(np.abs(F))) <= tol * float(np.max(np.abs(cc))):
+            break
+        ft = density(t, d)
+        up = ft * (t - cc[:-1]) / m[:-1]    # dc_k / dt_k, cells k = 0 .. L-2
+        lo = ft * (cc[1:] - t) / m[1:]      # dc_{k+1} / dt_k
+        ab = np.zeros((3, L - 1))
+        ab[0, 1:] = -0.5 * up[1:]           # dF_j / dt_{j+1} = -dc_{j+1}/dt_{j+1} / 2
+        ab[1, :] = 1.0 - 0.5 * (up + lo)    # dF_j / dt_j
+        ab[2, :-1] = -0.5 * lo[:-1]         # dF_{j+1} / dt_j = -dc_{j+1}/dt_j / 2
+        delta = solve_banded((1, 1), ab, -F)
+        lam = 1.0
+        f0 = float(np.max(np.abs(F)))
+        while True:
+            tn = t + lam * delta
+            tn = 0.5 * (tn - tn[::-1])
+            if np.all(np.diff(tn) > 0.0) and tn[0] > -1.0 and tn[-1] < 1.0:
+                Fn, mn, ccn = resid(tn)
+                if float(np.max(np.abs(Fn))) < f0 or lam < 1e-6:
+                    break
+            lam *= 0.5
+            if lam < 1e-12:
+                return cc
+        t, F, m, cc = tn, Fn, mn, ccn
+    return 0.5 * (cc - cc[::-1])
 
 
 def uniform(d: int, bits: int):

@@ -36,7 +36,7 @@ def test_density_integrates_to_one_and_has_variance_1_over_d():
 
 
 @pytest.mark.parametrize("d", [128, 256])
-@pytest.mark.parametrize("b", [2, 3, 4])
+@pytest.mark.parametrize("b", [2, 3, 4, 8])
 def test_fixed_point_by_independent_quadrature(d, b):
     """Each centroid equals its cell's conditional mean and each threshold is
     the midpoint — the mean computed by adaptive quadrature of the density,
@@ -54,7 +54,7 @@ def test_fixed_point_by_independent_quadrature(d, b):
 
 
 @pytest.mark.parametrize("d", [128, 256])
-@pytest.mark.parametrize("b", [1, 2, 3, 4])
+@pytest.mark.parametrize("b", [1, 2, 3, 4, 8])
 def test_symmetry_and_zero_middle_threshold(d, b):
     c, t, _ = codebook.lloyd_max(d, b)
     assert np.array_equal(c, -c[::-1])
@@ -116,3 +116,44 @@ def test_mass_and_moment_closed_forms_against_quadrature():
         m1, _ = integrate.quad(lambda u: u * codebook.density(u, d), a, b, epsabs=1e-16)
         assert abs(codebook.cell_mass(a, b, d) - m) < 1e-12
         assert abs(codebook.cell_first_moment(a, b, d) - m1) < 1e-13
+
+
+@pytest.mark.parametrize("d", [128, 256])
+@pytest.mark.parametrize("b", [3, 4])
+def test_newton_finish_leaves_a_converged_lloyd_codebook_in_place(d, b):
+    """Where Lloyd's iteration converges (few levels), Newton's method on the
+    same conditions starts at its fixed point and stays there."""
+    c, _, _ = codebook.lloyd_max(d, b)
+    assert np.max(np.abs(codebook._newton_refine(d, c) - c)) < 1e-12
+
+
+@pytest.mark.parametrize("d", [128, 256])
+def test_eight_bit_distortion_approaches_the_high_resolution_limit(d):
+    """Many-level quantisers approach the Panter-Dite asymptote
+    D ~ d (int f^(1/3))^3 / (12 L^2) of an optimal quantiser with L levels
+    (a result independent of Lloyd's conditions): within 1 % at 256 levels,
+    and the gap shrinks from 64 to 256 levels."""
+    k, _ = integrate.quad(lambda u: codebook.density(u, d) ** (1.0 / 3.0), -1, 1, epsabs=1e-14, limit=400,
+                          points=[-0.3, 0.0, 0.3])
+    gaps = []
+    for b in (6, 8):
+        c, t, _ = codebook.lloyd_max(d, b)
+        D = codebook.distortion(d, c, t)
+        pd = d * k ** 3 / (12.0 * (1 << b) ** 2)
+        gaps.append(abs(D / pd - 1.0))
+    assert gaps[1] < 0.01 and gaps[1] < gaps[0]
+
+
+def test_eight_bit_distortion_matches_monte_carlo_on_random_unit_vectors():
+    d = 128
+    c, t, _ = codebook.lloyd_max(d, 8)
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((4000, d))
+    u = x / np.linalg.norm(x, axis=1, keepdims=True)
+    # nearest centroid from the two centroids around each value (no thresholds)
+    j = np.clip(np.searchsorted(c, u), 1, len(c) - 1)
+    lo, hi = c[j - 1], c[j]
+    q = np.where(np.abs(u - lo) <= np.abs(hi - u), lo, hi)
+    err = np.sum((u - q) ** 2, axis=1)
+    D = codebook.distortion(d, c, t)
+    assert abs(np.mean(err) - D) < 4 * np.std(err) / np.sqrt(len(u))
