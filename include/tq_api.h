@@ -48,7 +48,11 @@ enum { TQ_DTYPE_F32 = 0, TQ_DTYPE_BF16 = 1 };
  *                head_dim 128 and 256).
  *   k_bits     : Lloyd-Max index bits per key coordinate, 2, 3 or 4 (Hub,
  *                step 2); each key coordinate also gets one QJL sign bit
- *                (Hub, step 3; Roadmap §1).
+ *                (Hub, step 3; Roadmap §1).  8 is accepted for MSE-only
+ *                presets (the K8V4 preset of vLLM's path, iThome "which path
+ *                vLLM takes"); 8-bit keys with the QJL sketch are rejected
+ *                with TQ_EUNSUPPORTED, and tq_extend_attention does not take
+ *                them.
  *   v_bits     : value bits, 2 or 4 (Hub, step 4).
  *   v_group    : value group size, must be 32 (Hub, step 4).
  *   block_size : tokens per paged block, must be 16.

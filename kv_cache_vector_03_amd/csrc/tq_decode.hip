@@ -131,7 +131,7 @@ struct Rec {
   static constexpr int vmeta = vcodes + (VB * D / 8) * 16;
   static constexpr int bytes = vmeta + (D / 32) * 64;
   static constexpr int slot = 2 * bytes;              // LDS bytes of one ring slot (one step)
-  static constexpr int nslot = D == 128 ? 3 : 2;      // ring depth (steps in flight + 1)
+  static constexpr int nslot = D == 128 && KB <= 4 ? 3 : 2;  // ring depth (steps in flight + 1)
 };
 
 template <int D, int GP, int KB, int VB, bool QJ>
@@ -385,7 +385,18 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h_, int t0_, int 
         const int bp = kt * TB;
         const uint32_t win =
             bp % 32 == 0 ? cw[bp / 32] : __builtin_amdgcn_alignbit(cw[bp / 32 + 1], cw[bp / 32], bp % 32);
-        if constexpr (UN) {
+        if constexpr (KB == 8) {
+          // 8-bit codes: one lookup per code in the one-code table (bf16 hi
+          // | lo << 16 of c[idx]), so MFMA m takes coordinates 4m .. 4m+3 as
+          // {hi, lo} pairs (the A operand repeats each coordinate twice)
+          const uint32_t* s_one = reinterpret_cast<const uint32_t*>(s_pair);
+#pragma unroll
+          for (int m = 0; m < 2; ++m) {
+            const uint32_t cb = cw[2 * kt + m];
+            const u32x4 b = {s_one[cb & 0xFFu], s_one[(cb >> 8) & 0xFFu], s_one[(cb >> 16) & 0xFFu], s_one[cb >> 24]};
+            am = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1[kt][m], __builtin_bit_cast(bf16x8, b), am, 0, 0, 0);
+          }
+        } else if constexpr (UN) {
           // c[idx] = c0 + step idx needs no table: B element = bf16 of
           // 128 + idx (0x4300 | idx, exact), built from the code bits alone.
           // Dword j holds codes j and j + 4 of the slice: y has codes 0-3 in
@@ -1005,10 +1016,15 @@ __global__ __launch_bounds__((split_waves<D, GP>() * 64)) void decode_split_kern
 
   // tables: centroid pairs of this preset, +-1 patterns of sign bytes
   const DevTables& dv = a.dev[pr];
-  static_assert((1 << (2 * KB)) <= NW * 64, "one centroid pair per thread");
+  static_assert(KB == 8 || (1 << (2 * KB)) <= NW * 64, "one centroid pair per thread");
+  static_assert(KB != 8 || 256 <= NW * 64, "one code-table entry per thread");
+  // entries of the score table: two-code pairs (2-4-bit keys), or single codes
+  // (8-bit keys, stored in the same LDS as dwords)
+  constexpr int kTab = KB == 8 ? 256 : (1 << (2 * KB));
   // loaded here, stored after the scan's first loads are issued, so the two
   // global round trips overlap
-  const uint2 pair_v = !UN && tid < (1 << (2 * KB)) ? make_uint2(dv.pair_lut[2 * tid], dv.pair_lut[2 * tid + 1])
+  const uint2 pair_v = KB == 8 ? make_uint2(tid < 256 ? dv.code_lut[tid] : 0u, 0u)
+                      : !UN && tid < kTab ? make_uint2(dv.pair_lut[2 * tid], dv.pair_lut[2 * tid + 1])
                                                      : make_uint2(0u, 0u);
   {
     u32x4 w;
@@ -1017,6 +1033,14 @@ __global__ __launch_bounds__((split_waves<D, GP>() * 64)) void decode_split_kern
       w[e] = (((tid >> (2 * e)) & 1) ? 0x3F80u : 0xBF80u) | ((((tid >> (2 * e + 1)) & 1) ? 0x3F80u : 0xBF80u) << 16);
     if (QJ && tid < 256) s_sgn[tid] = w;  // one entry per thread
   }
+
+  auto store_table = [&](int t) {
+    if constexpr (KB == 8) {
+      if (t < 256) reinterpret_cast<uint32_t*>(s_pair)[t] = pair_v.x;
+    } else if (!UN && t < kTab) {
+      s_pair[t] = pair_v;
+    }
+  };
 
   bf16x8 A1[KT][2], A3[KT];
   f32x4 ucst = {0.f, 0.f, 0.f, 0.f};  // equally spaced codebook: score rows' offsets
@@ -1122,6 +1146,19 @@ __global__ __launch_bounds__((split_waves<D, GP>() * 64)) void decode_split_kern
               w1[j] = lo | (hi << 16);
             }
             A1r[kt][0] = __builtin_bit_cast(bf16x8, w1);
+          } else if constexpr (KB == 8) {
+            // slots 2e, 2e + 1 = coordinate 4m + e (against the {hi, lo} pair of c[idx])
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+              const float ls = a.logit_scale;
+              u32x4 w;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const uint32_t v = split(xs[4 * m + e] * ls);
+                w[e] = v | (v << 16);
+              }
+              A1r[kt][m] = __builtin_bit_cast(bf16x8, w);
+            }
           } else {
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
@@ -1176,7 +1213,7 @@ __global__ __launch_bounds__((split_waves<D, GP>() * 64)) void decode_split_kern
   if (a.direct) {
     // one item per (sequence, KV head), contiguous ranges per workgroup: no
     // work list is needed
-    if (!UN && tid < (1 << (2 * KB))) s_pair[tid] = pair_v;
+    store_table(tid);
     const int total = a.B * a.Hkv;
     const int i0 = (int)((int64_t)blockIdx.x * total / gridDim.x);
     const int i1 = (int)((int64_t)(blockIdx.x + 1) * total / gridDim.x);
@@ -1198,7 +1235,7 @@ __global__ __launch_bounds__((split_waves<D, GP>() * 64)) void decode_split_kern
       const int items = (bb < a.B && seq_preset_of(a, bb) == pr) ? a.Hkv * seq_splits(a, bb) : 0;
       int* sc = s_scan + base;
       if (bb < a.B) sc[tid] = items;
-      if (!UN && base == 0 && tid < (1 << (2 * KB))) s_pair[tid] = pair_v;
+      if (base == 0) store_table(tid);
       __syncthreads();
       // Hillis-Steele inclusive scan of this block of 256 entries, in place
       for (int off = 1; off < NW * 64; off <<= 1) {
@@ -1364,6 +1401,9 @@ static hipError_t launch_split(const DArgs& a, int pr, hipStream_t s, bool dry_r
 
 template <int D, int GP, bool QJ>
 static hipError_t dispatch_preset(const DArgs& a, int pr, int kb, int vb, hipStream_t s, bool dry) {
+  if constexpr (!QJ)  // 8-bit keys: MSE-only presets
+    if (kb == 8)
+      return vb == 2 ? launch_split<D, GP, 8, 2, QJ>(a, pr, s, dry) : launch_split<D, GP, 8, 4, QJ>(a, pr, s, dry);
   // 4-bit equally spaced codebooks take the arithmetic score path
   if (kb == 4 && a.dev[pr].uni_step != 0.f)
     return vb == 2 ? launch_split<D, GP, 4, 2, QJ, true>(a, pr, s, dry) : launch_split<D, GP, 4, 4, QJ, true>(a, pr, s, dry);

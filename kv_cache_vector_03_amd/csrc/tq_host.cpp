@@ -311,12 +311,14 @@ int check_preset(const tq_preset* p) {
     set_error("preset is NULL");
     return TQ_EINVAL;
   }
-  if ((p->head_dim != 128 && p->head_dim != 256) || p->k_bits < 2 || p->k_bits > 4 ||
-      (p->v_bits != 2 && p->v_bits != 4) || p->v_group != 32 || p->block_size != 16 ||
+  const bool mse = (p->flags & TQ_PRESET_MSE_ONLY) != 0;
+  const bool kb_ok = (p->k_bits >= 2 && p->k_bits <= 4) || (p->k_bits == 8 && mse);
+  if ((p->head_dim != 128 && p->head_dim != 256) || !kb_ok || (p->v_bits != 2 && p->v_bits != 4) ||
+      p->v_group != 32 || p->block_size != 16 ||
       (p->flags & ~(TQ_PRESET_MSE_ONLY | TQ_PRESET_UNIFORM | TQ_PRESET_ROTATE_V)) != 0) {
     set_error("unsupported preset: head_dim %d k_bits %d v_bits %d v_group %d block_size %d flags %d "
-              "(supported: head_dim 128|256, k_bits 2..4, v_bits 2|4, v_group 32, block_size 16, "
-              "flags: an or of TQ_PRESET_MSE_ONLY, TQ_PRESET_UNIFORM, TQ_PRESET_ROTATE_V)",
+              "(supported: head_dim 128|256, k_bits 2..4, or 8 with TQ_PRESET_MSE_ONLY, v_bits 2|4, v_group 32, "
+              "block_size 16, flags: an or of TQ_PRESET_MSE_ONLY, TQ_PRESET_UNIFORM, TQ_PRESET_ROTATE_V)",
               p->head_dim, p->k_bits, p->v_bits, p->v_group, p->block_size, p->flags);
     return TQ_EUNSUPPORTED;
   }
@@ -467,7 +469,8 @@ extern "C" int tq_codebook_init(const tq_preset* p, const int8_t* signs, const f
             tiles_perm[base + (size_t)l * 8 + e] = h ^ flip;
             tiles_perm[base + 64 * 8 + (size_t)l * 8 + e] = lo ^ flip;
           }
-  const int P = 1 << (2 * kb);
+  // two-code pair tables (2-4-bit keys; 8-bit keys would need 65,536 pairs)
+  const int P = kb <= 4 ? 1 << (2 * kb) : 0;
   std::vector<uint32_t> pair((size_t)P * 2);
   for (int idx = 0; idx < P; ++idx) {
     int a = idx & (L - 1), b = idx >> kb;
@@ -487,12 +490,21 @@ extern "C" int tq_codebook_init(const tq_preset* p, const int8_t* signs, const f
     pair16[2 * idx + 1] = (uint32_t)la | ((uint32_t)lb << 16);
   }
 
+  // one-code table (the 8-bit decode): entry a = bf16 hi | bf16 lo << 16 of c[a]
+  std::vector<uint32_t> code1((size_t)L);
+  for (int a = 0; a < L; ++a) {
+    const uint16_t h = f32_to_bf16_bits(c->c32[a]);
+    const uint16_t l = f32_to_bf16_bits(c->c32[a] - bf16_bits_to_f32(h));
+    code1[a] = (uint32_t)h | ((uint32_t)l << 16);
+  }
+
   // ---- one device allocation, 256-byte aligned pieces
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   size_t o_c = 0, o_t = up(o_c + 4 * L), o_s1 = up(o_t + 4 * L), o_s2 = up(o_s1 + 4 * d), o_S = up(o_s2 + 4 * d),
          o_tiles = up(o_S + 4 * (size_t)d * d), o_tiles2 = up(o_tiles + 2 * tiles.size()),
          o_pair = up(o_tiles2 + 2 * tiles_d2.size()), o_pair16 = up(o_pair + 4 * pair.size()),
-         o_perm = up(o_pair16 + 4 * pair16.size()), total = up(o_perm + 2 * tiles_perm.size());
+         o_perm = up(o_pair16 + 4 * pair16.size()), o_code1 = up(o_perm + 2 * tiles_perm.size()),
+         total = up(o_code1 + 4 * code1.size());
   if (hipGetDevice(&c->device) != hipSuccess) {
     set_error("tq_codebook_init: no HIP device");
     delete c;
@@ -515,6 +527,7 @@ extern "C" int tq_codebook_init(const tq_preset* p, const int8_t* signs, const f
   std::memcpy(img.data() + o_pair, pair.data(), 4 * pair.size());
   std::memcpy(img.data() + o_pair16, pair16.data(), 4 * pair16.size());
   if (!tiles_perm.empty()) std::memcpy(img.data() + o_perm, tiles_perm.data(), 2 * tiles_perm.size());
+  std::memcpy(img.data() + o_code1, code1.data(), 4 * code1.size());
   if (hipMemcpy(base, img.data(), total, hipMemcpyHostToDevice) != hipSuccess) {
     set_error("tq_codebook_init: upload failed");
     (void)hipFree(c->dev_block);
@@ -531,6 +544,7 @@ extern "C" int tq_codebook_init(const tq_preset* p, const int8_t* signs, const f
   c->dev.pair_lut = (const uint32_t*)(base + o_pair);
   c->dev.pair_lut_f16 = (const uint32_t*)(base + o_pair16);
   c->dev.s_tiles_perm_d2 = tiles_perm.empty() ? nullptr : (const uint16_t*)(base + o_perm);
+  c->dev.code_lut = (const uint32_t*)(base + o_code1);
   // equally spaced codebook: c_k = (k - (L-1)/2) step, so c[1] - c[0] is the step
   c->dev.uni_step = (p->flags & TQ_PRESET_UNIFORM) ? (float)(c->c64[1] - c->c64[0]) : 0.f;
   *out = c;
@@ -804,9 +818,9 @@ extern "C" int tq_extend_attention(const tq_extend_args* a, void* stream) {
     return TQ_EINVAL;
   }
   const int G = a->num_q_heads / a->num_kv_heads;
-  if (a->ctx->d != 128 || (G != 1 && G != 2 && G != 4 && G != 8)) {
-    set_error("tq_extend_attention: head_dim %d with %d query heads per KV head is not supported (head_dim 128, "
-              "G in {1, 2, 4, 8})", a->ctx->d, G);
+  if (a->ctx->d != 128 || (G != 1 && G != 2 && G != 4 && G != 8) || a->ctx->kb > 4) {
+    set_error("tq_extend_attention: head_dim %d, %d query heads per KV head, %d-bit keys is not supported "
+              "(head_dim 128, G in {1, 2, 4, 8}, 2-4-bit keys)", a->ctx->d, G, a->ctx->kb);
     return TQ_EUNSUPPORTED;
   }
   if (a->batch == 0 || a->max_chunk == 0) return TQ_OK;

@@ -26,8 +26,11 @@ struct DevTables {
   // exactly: negating an fp16 hi/lo pair negates both parts).
   const uint16_t* s_tiles_d2 = nullptr;
   // Decode pair table: entry a | b << k_bits = (bf16 hi c[a], bf16 hi c[b]),
-  // (bf16 lo c[a], bf16 lo c[b]) as two dwords; [2^(2 k_bits)][2] uint32.
+  // (bf16 lo c[a], bf16 lo c[b]) as two dwords; [2^(2 k_bits)][2] uint32
+  // (2-4-bit keys only: empty for 8-bit keys).
   const uint32_t* pair_lut = nullptr;
+  // One-code table (the 8-bit decode): entry a = bf16 hi c[a] | bf16 lo c[a] << 16.
+  const uint32_t* code_lut = nullptr;
   // The same pair table in fp16 (extend attention): entry a | b << k_bits =
   // (fp16 hi c[a], fp16 hi c[b]), (fp16 lo c[a], fp16 lo c[b]); [2^(2 k_bits)][2].
   const uint32_t* pair_lut_f16 = nullptr;

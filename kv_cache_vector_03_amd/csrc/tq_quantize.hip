@@ -41,7 +41,7 @@ struct QLds {
   static constexpr size_t tiles_bytes = kTilesInLds ? (size_t)NT * KT * 2 * 64 * 8 * 2 : 0;
   static constexpr size_t a_bytes = (size_t)kQWaves<D> * 2 * 16 * kRowStride * 2;
   static constexpr size_t ballot_bytes = (size_t)kQWaves<D> * NT * 4 * 8;
-  static constexpr size_t cent_bytes = 64;
+  static constexpr size_t cent_bytes = 1024;  // upper centroids and thresholds (up to 8-bit codes)
   static constexpr size_t total = tiles_bytes + a_bytes + ballot_bytes + cent_bytes;
 };
 
@@ -76,14 +76,32 @@ __device__ __forceinline__ void load_row_part(const void* base, int64_t elem_off
 // u - c[index] = +-(|u| - c[H + cnt]).  Identical to the count #{t < u}
 // except where |u| equals a threshold exactly.  tU = t[H..L-2]; s_cU holds
 // c[H..L-1] in LDS.
+// With 8-bit keys (127 upper thresholds) the count is a binary search over
+// the upper thresholds in LDS (s_tU); the register copy tU is unused.
 template <int KB>
-__device__ __forceinline__ void sym_code(float u, const float (&tU)[(1 << KB) / 2 - 1], const float* s_cU,
-                                         uint32_t& code, float& r) {
+constexpr int sym_regs() {
+  return KB <= 4 ? (1 << KB) / 2 - 1 : 1;
+}
+// #{t < m} over the 2^k - 1 ascending thresholds t (LDS): k halving steps.
+template <int K>
+__device__ __forceinline__ uint32_t count_below(float m, const float* t) {
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int s = 1 << (K - 1); s >= 1; s >>= 1) cnt += m > t[cnt + s - 1] ? (uint32_t)s : 0u;
+  return cnt;
+}
+template <int KB>
+__device__ __forceinline__ void sym_code(float u, const float (&tU)[sym_regs<KB>()], const float* s_cU,
+                                         const float* s_tU, uint32_t& code, float& r) {
   constexpr uint32_t H = (1u << KB) / 2;
   const float m = fabsf(u);
   uint32_t cnt = 0;
+  if constexpr (KB <= 4) {
 #pragma unroll
-  for (int i = 0; i < (int)H - 1; ++i) cnt += m > tU[i] ? 1u : 0u;
+    for (int i = 0; i < (int)H - 1; ++i) cnt += m > tU[i] ? 1u : 0u;
+  } else {
+    cnt = count_below<KB - 1>(m, s_tU);
+  }
   const float d = m - s_cU[cnt];
   const bool pos = u > 0.f;
   code = cnt ^ (pos ? H : H - 1u);
@@ -163,12 +181,19 @@ __global__ __launch_bounds__(kQWaves<D> * 64) void quantize_kernel(QArgs a) {
     constexpr int n16 = (int)(QLds<D>::tiles_bytes / 16);
     for (int i = tid; i < n16; i += kQWaves<D> * 64) dst[i] = src[i];
   }
-  // upper half of the (odd-symmetric) codebook
+  // upper half of the (odd-symmetric) codebook: centroids in LDS, thresholds
+  // in registers (8-bit codes: in LDS after the centroids)
   constexpr int H = L / 2;
+  float* s_tU = s_c + H;
   if (tid < H) s_c[tid] = a.dev.centroids[H + tid];
-  float tU[H - 1];
+  float tU[sym_regs<KB>()];
+  if constexpr (KB <= 4) {
 #pragma unroll
-  for (int i = 0; i < H - 1; ++i) tU[i] = a.dev.thresholds[H + i];
+    for (int i = 0; i < H - 1; ++i) tU[i] = a.dev.thresholds[H + i];
+  } else {
+    tU[0] = 0.f;
+    if (tid < H - 1) s_tU[tid] = a.dev.thresholds[H + tid];
+  }
   // D1 / D2 signs of this lane's coordinates as bit masks (bit = negative)
   // D1 as sign-bit patterns: fp32 inputs per element (m1), bf16 inputs per
   // packed pair (bits 15 and 31 of each input dword).  D2 acts after the
@@ -296,7 +321,7 @@ __global__ __launch_bounds__(kQWaves<D> * 64) void quantize_kernel(QArgs a) {
     for (int e = 0; e < E; ++e) {
       uint32_t c;
       float r;
-      sym_code<KB>(x[e] * inv, tU, s_c, c, r);  // D2-free index and residual
+      sym_code<KB>(x[e] * inv, tU, s_c, s_tU, c, r);  // D2-free index and residual
       idx[e] = c;
       r = zero ? 0.f : r;
       r2 = __builtin_fmaf(r, r, r2);
@@ -525,7 +550,8 @@ __global__ __launch_bounds__(kRowWaves * 64) void quantize_rows_kernel(QArgs a) 
   __shared__ float s_r[kRowWaves][D];
   __shared__ uint8_t s_code[kRowWaves][D];
   __shared__ uint32_t s_qjl[kRowWaves][D / 32];
-  __shared__ float s_cent[16];
+  __shared__ float s_cent[L];
+  __shared__ float s_thr[KB <= 4 ? 1 : L - 1];  // 8-bit codes: the thresholds, for a binary search
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t th = (int64_t)blockIdx.x * kRowWaves + wave;
   const bool valid = th < a.num_th;  // invalid waves still take part in the barriers
@@ -534,7 +560,7 @@ __global__ __launch_bounds__(kRowWaves * 64) void quantize_rows_kernel(QArgs a) 
   const int j0 = lane * P;
 
   // issue every independent load first
-  float x[P], vx[P], sg1[P], sg2[P], thr[L - 1];
+  float x[P], vx[P], sg1[P], sg2[P], thr[KB <= 4 ? L - 1 : 1];
   int32_t slot = -1;
   if (valid) {
     load_few<BF16, P>(a.k, th * D + j0, x);
@@ -549,9 +575,14 @@ __global__ __launch_bounds__(kRowWaves * 64) void quantize_rows_kernel(QArgs a) 
     sg1[e] = a.dev.signs1[j0 + e];
     sg2[e] = a.dev.signs2[j0 + e];
   }
+  if constexpr (KB <= 4) {
 #pragma unroll
-  for (int i = 0; i < L - 1; ++i) thr[i] = a.dev.thresholds[i];
-  if (tid < L) s_cent[tid] = a.dev.centroids[tid];
+    for (int i = 0; i < L - 1; ++i) thr[i] = a.dev.thresholds[i];
+  } else {
+    thr[0] = 0.f;
+    for (int i = tid; i < L - 1; i += kRowWaves * 64) s_thr[i] = a.dev.thresholds[i];
+  }
+  for (int i = tid; i < L; i += kRowWaves * 64) s_cent[i] = a.dev.centroids[i];
   // this wave's projection tiles (column tiles wave, wave + 4, ...): they do
   // not depend on the token, so their round trip overlaps the one above
   constexpr int NTW = NT / kRowWaves;
@@ -602,15 +633,19 @@ __global__ __launch_bounds__(kRowWaves * 64) void quantize_rows_kernel(QArgs a) 
       x[e] = wht_xlane<32>(v, s32);
     }
   }
-  __syncthreads();  // s_cent
+  __syncthreads();  // s_cent, s_thr
   const float inv = zero ? 0.f : (1.0f / __builtin_sqrtf((float)D)) / n;
   float r2 = 0.f;
 #pragma unroll
   for (int e = 0; e < P; ++e) {
     const float u = x[e] * inv * sg2[e];
     uint32_t c = 0;
+    if constexpr (KB <= 4) {
 #pragma unroll
-    for (int i = 0; i < L - 1; ++i) c += (u > thr[i]) ? 1u : 0u;
+      for (int i = 0; i < L - 1; ++i) c += (u > thr[i]) ? 1u : 0u;
+    } else {
+      c = count_below<KB>(u, s_thr);
+    }
     c = zero ? 0u : c;
     const float r = zero ? 0.f : u - s_cent[c];
     r2 = __builtin_fmaf(r, r, r2);
@@ -786,6 +821,8 @@ static hipError_t dispatch_vb(const QArgs& a, int vb, hipStream_t s) {
 
 template <int D, bool BF16, bool QJ, bool ROTV>
 static hipError_t dispatch_kb(const QArgs& a, int kb, int vb, hipStream_t s) {
+  if constexpr (!QJ)  // 8-bit keys: MSE-only presets (the host rejects them with the QJL sketch)
+    if (kb == 8) return dispatch_vb<D, 8, BF16, QJ, ROTV>(a, vb, s);
   switch (kb) {
     case 2: return dispatch_vb<D, 2, BF16, QJ, ROTV>(a, vb, s);
     case 3: return dispatch_vb<D, 3, BF16, QJ, ROTV>(a, vb, s);

@@ -75,6 +75,15 @@ __device__ __forceinline__ float row_sum4(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 constexpr int parity(int x) { return __builtin_popcount(x) & 1; }
+// The code-stream dword that lane group g stores as its i-th (see the packing
+// of each key width below).
+template <int KB>
+__device__ __forceinline__ int stream_dword(int g, int i) {
+  constexpr int CPL = KB * 128 / 32 / 4;
+  if constexpr (KB == 4) return 2 * (CPL * (g & 1) + i) + (g >> 1);
+  if constexpr (KB == 8) return 4 * i + g;
+  return CPL * g + i;
+}
 // a value the compiler cannot see through (keeps a select as bit operations)
 __device__ __forceinline__ uint32_t opaque_mask(uint32_t x) {
   asm volatile("" : "+v"(x));
@@ -95,10 +104,18 @@ __global__ __launch_bounds__(mwaves<QJ>() * 64) void quantize_mfma_kernel(QMArgs
     const u32x4* src = reinterpret_cast<const u32x4*>(a.dev.s_tiles_perm_d2);
     for (int i = tid; i < 4096; i += MW * 64) const_cast<u32x4*>(s_st)[i] = src[i];
   }
+  // upper centroids in LDS; upper thresholds in registers (8-bit codes: in
+  // LDS after the centroids, for a binary search)
+  float* s_tU = s_c + H;
   if (tid < H) s_c[tid] = a.dev.centroids[H + tid];
-  float tU[H - 1];
+  float tU[KB <= 4 ? H - 1 : 1];
+  if constexpr (KB <= 4) {
 #pragma unroll
-  for (int i = 0; i < H - 1; ++i) tU[i] = a.dev.thresholds[H + i];
+    for (int i = 0; i < H - 1; ++i) tU[i] = a.dev.thresholds[H + i];
+  } else {
+    tU[0] = 0.f;
+    if (tid < H - 1) s_tU[tid] = a.dev.thresholds[H + tid];
+  }
   // D1 as bf16 sign-bit masks of the key operand: element e of slice kt is
   // coordinate 32 kt + 8 g + e
   u32x4 d1m[MKT];
@@ -142,7 +159,7 @@ __global__ __launch_bounds__(mwaves<QJ>() * 64) void quantize_mfma_kernel(QMArgs
   uint32_t m2c[CPL];
 #pragma unroll
   for (int i = 0; i < CPL; ++i) {
-    const int wd = KB == 4 ? 2 * (CPL * (g & 1) + i) + (g >> 1) : CPL * g + i;  // the stream dword this lane stores
+    const int wd = stream_dword<KB>(g, i);  // the stream dword this lane stores
     uint32_t m = 0;
     for (int j = 0; j < MD; ++j) {
       if (a.dev.signs2[j] < 0.f) {
@@ -210,8 +227,14 @@ __global__ __launch_bounds__(mwaves<QJ>() * 64) void quantize_mfma_kernel(QMArgs
         const float u = y[nt][r] * inv;
         const float m = fabsf(u);
         uint32_t cnt = 0;
+        if constexpr (KB <= 4) {
 #pragma unroll
-        for (int i = 0; i < H - 1; ++i) cnt += m > tU[i] ? 1u : 0u;
+          for (int i = 0; i < H - 1; ++i) cnt += m > tU[i] ? 1u : 0u;
+        } else {
+          // #{upper thresholds < m}: seven halving steps over the 127 in LDS
+#pragma unroll
+          for (int st = H / 2; st >= 1; st >>= 1) cnt += m > s_tU[cnt + st - 1] ? (uint32_t)st : 0u;
+        }
         const float dd = m - s_c[cnt];
         const bool pos = u > 0.f;
         const uint32_t code = cnt ^ (pos ? (uint32_t)H : (uint32_t)H - 1u);
@@ -290,6 +313,11 @@ __global__ __launch_bounds__(mwaves<QJ>() * 64) void quantize_mfma_kernel(QMArgs
       }
 #pragma unroll
       for (int i = 0; i < CPL; ++i) cst[i] = g == 0 ? wds[i] : g == 1 ? wds[3 + i] : g == 2 ? wds[6 + i] : wds[9 + i];
+    } else if constexpr (KB == 8) {
+      // 32-bit fields: the lane's four codes of column tile nt are bytes
+      // 16 nt + 4 g .. + 3 of the stream, i.e. dword 4 nt + g, whole
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) cst[i] = field[i];
     } else {
       // 16-bit fields: dword 2 nt + (g >> 1), half g & 1; or over the pair
       // (g, g ^ 1); lane g stores dwords 2 (4 (g & 1) + i) + (g >> 1), i < 4
@@ -315,7 +343,7 @@ __global__ __launch_bounds__(mwaves<QJ>() * 64) void quantize_mfma_kernel(QMArgs
       uint8_t* kc = base + a.lay.kcodes + s * (KB * MD / 8);
 #pragma unroll
       for (int i = 0; i < CPL; ++i) {
-        const int wd = KB == 4 ? 2 * (CPL * (g & 1) + i) + (g >> 1) : CPL * g + i;
+        const int wd = stream_dword<KB>(g, i);
         *reinterpret_cast<uint32_t*>(kc + 4 * wd) = zero ? 0u : (cst[i] ^ m2c[i]);
       }
       if constexpr (QJ) {
@@ -404,7 +432,7 @@ template <int KB, int VB, bool QJ>
 hipError_t launch_m(const QMArgs& a, hipStream_t stream) {
   constexpr int MW = mwaves<QJ>();
   auto kern = quantize_mfma_kernel<KB, VB, QJ>;
-  const int lds = (QJ ? 65536 : 0) + 64;
+  const int lds = (QJ ? 65536 : 0) + (KB <= 4 ? 64 : 1024);
   struct Cache {
     std::mutex mu;
     bool init[16] = {};
@@ -439,6 +467,8 @@ hipError_t launch_m(const QMArgs& a, hipStream_t stream) {
 
 template <bool QJ>
 hipError_t dispatch_m(const QMArgs& a, int kb, int vb, hipStream_t s) {
+  if constexpr (!QJ)  // 8-bit keys: MSE-only presets
+    if (kb == 8) return vb == 2 ? launch_m<8, 2, QJ>(a, s) : launch_m<8, 4, QJ>(a, s);
   if (kb == 2) return vb == 2 ? launch_m<2, 2, QJ>(a, s) : launch_m<2, 4, QJ>(a, s);
   if (kb == 3) return vb == 2 ? launch_m<3, 2, QJ>(a, s) : launch_m<3, 4, QJ>(a, s);
   return vb == 2 ? launch_m<4, 2, QJ>(a, s) : launch_m<4, 4, QJ>(a, s);
