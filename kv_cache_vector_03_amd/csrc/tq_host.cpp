@@ -180,9 +180,10 @@ extern "C" int tq_lloyd_max(int32_t d, int32_t bits, double* centroids, double* 
   // single fixed point and converges to it from any ordered start.
   std::vector<double> c(L), t(L - 1), cn(L), lo(L), hi(L);
   for (int k = 0; k < L; ++k) c[k] = (2.0 * k + 1.0 - L) / L * 2.0 / std::sqrt((double)d);
-  // beyond 4 bits Lloyd's iteration only brings the codebook near the fixed
-  // point, which newton_refine then solves
-  const int lloyd_iters = bits <= 4 ? 100000 : 200;
+  // with more than four levels Lloyd's iteration is run only to bring the
+  // codebook near the fixed point, which newton_refine then solves (the
+  // plain iteration would take seconds at 3-4 bits and never finish at 8)
+  const int lloyd_iters = bits <= 1 ? 100000 : 200;
   for (int it = 0; it < lloyd_iters; ++it) {
     for (int k = 0; k + 1 < L; ++k) t[k] = 0.5 * (c[k] + c[k + 1]);
     for (int k = 0; k < L; ++k) {
@@ -201,7 +202,7 @@ extern "C" int tq_lloyd_max(int32_t d, int32_t bits, double* centroids, double* 
     c = lo;
     if (delta <= 1e-15 * cmax) break;
   }
-  if (bits > 4) newton_refine(d, c);
+  if (bits > 1) newton_refine(d, c);
   for (int k = 0; k + 1 < L; ++k) t[k] = 0.5 * (c[k] + c[k + 1]);
   std::memcpy(centroids, c.data(), sizeof(double) * L);
   std::memcpy(thresholds, t.data(), sizeof(double) * (L - 1));
