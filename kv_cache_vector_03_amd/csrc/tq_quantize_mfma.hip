@@ -239,13 +239,14 @@ __global__ __launch_bounds__(mwaves<QJ>() * 64) void quantize_mfma_kernel(QMArgs
         const bool pos = u > 0.f;
         const uint32_t code = cnt ^ (pos ? (uint32_t)H : (uint32_t)H - 1u);
         float res = pos ? dd : -dd;
-        res = zero ? 0.f : res;
         r2 = __builtin_fmaf(res, res, r2);
         y[nt][r] = res;
         field[nt] |= code << (KB * r);
       }
     }
-    const float gamma = __builtin_sqrtf(row_sum4(r2));
+    // a zero key stores zero codes, sign bits and gamma (selected per row
+    // below, not per coordinate)
+    const float gamma = zero ? 0.f : __builtin_sqrtf(row_sum4(r2));
 
     // ---- QJL sign bits of S r (MSE-only keys skip the sketch)
     uint32_t qw = 0;  // the sign dword this lane stores (dword g of the row's d / 8 bytes)
@@ -391,20 +392,21 @@ __global__ __launch_bounds__(mwaves<QJ>() * 64) void quantize_mfma_kernel(QMArgs
       // with a value within kVBand of a half-integer redo their group with
       // the division
       constexpr float kVBand = 8e-6f;
-      const float rs = 1.0f / sc;
+      // a constant group (s = 0) codes 0: with rs = 0 every t is 0
+      const float rs = sc != 0.f ? 1.0f / sc : 0.f;
       uint32_t vw[VB];
 #pragma unroll
       for (int i = 0; i < VB; ++i) vw[i] = 0;
-      bool near = false;
+      float far = 0.f;  // largest distance of a quotient from its integer
 #pragma unroll
       for (int e = 0; e < 32; ++e) {
         const float t = (x[e] - zz) * rs;
         const float q0 = __builtin_rintf(t);
-        near |= fabsf(t - q0) >= 0.5f - kVBand;
+        far = fmaxf(far, fabsf(t - q0));
         const float q = fminf(fmaxf(q0, 0.f), LV);
-        const uint32_t qi = (sc != 0.f) ? (uint32_t)q : 0u;
-        vw[(e * VB) / 32] |= qi << ((e * VB) % 32);
+        vw[(e * VB) / 32] |= (uint32_t)q << ((e * VB) % 32);
       }
+      const bool near = far >= 0.5f - kVBand;
       if (near && sc != 0.f) {
 #pragma unroll
         for (int i = 0; i < VB; ++i) vw[i] = 0;
