@@ -185,6 +185,16 @@ __global__ __launch_bounds__(mwaves<QJ>() * 64) void quantize_mfma_kernel(QMArgs
     const int64_t tk = t0 + n;
     const bool valid = tk < a.num_tokens;
     const int64_t th = tk * a.hkv + hh;
+    // value rows: lane l holds channels 32 (l % 4) .. + 31 of row l / 4
+    const int vrow = lane >> 2, vpart = lane & 3;
+    const int64_t tv = t0 + vrow;
+    const bool vvalid = tv < a.num_tokens;
+    // Every global read of the tile is issued before its first store (the
+    // compiler cannot move a read above a store it cannot prove disjoint):
+    // the key rows and both rows' slots here, the value rows right after the
+    // rotation, so the tile waits for one memory round trip instead of four.
+    const int32_t slot = valid ? a.slot_mapping[tk] : -1;
+    const int32_t vslot = vvalid ? a.slot_mapping[tv] : -1;
     bf16x8 kbv[MKT];
     {
       const u32x4* pk = reinterpret_cast<const u32x4*>(a.k + (valid ? th : 0) * MD + 8 * g);
@@ -205,6 +215,12 @@ __global__ __launch_bounds__(mwaves<QJ>() * 64) void quantize_mfma_kernel(QMArgs
         const u32x4 hp = hv[parity(nt & (2 * kt))][parity(nt & (2 * kt + 1))];
         y[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, hp), kbv[kt], y[nt], 0, 0, 0);
       }
+    }
+    u32x4 vraw[4];
+    {
+      const u32x4* pv = reinterpret_cast<const u32x4*>(a.v + (vvalid ? tv * a.hkv + hh : 0) * MD + 32 * vpart);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vraw[i] = vvalid ? __builtin_nontemporal_load(pv + i) : u32x4{0u, 0u, 0u, 0u};
     }
     // norm: sum of squares of the rotated row (H H^T = d I) over the row's lanes
     float ss = 0.f;
@@ -336,45 +352,17 @@ __global__ __launch_bounds__(mwaves<QJ>() * 64) void quantize_mfma_kernel(QMArgs
       for (int i = 0; i < CPL; ++i) cst[i] = (wds[4 + i] & odd) | (wds[i] & ~odd);
     }
 
-    // ---- store the key record
-    const int32_t slot = valid ? a.slot_mapping[tk] : -1;
-    if (valid && slot >= 0 && (int64_t)slot < a.slots_total) {
-      uint8_t* base = a.pool + ((int64_t)(slot >> 4) * a.hkv + hh) * a.rec;
-      const int s = slot & 15;
-      uint8_t* kc = base + a.lay.kcodes + s * (KB * MD / 8);
-#pragma unroll
-      for (int i = 0; i < CPL; ++i) {
-        const int wd = stream_dword<KB>(g, i);
-        *reinterpret_cast<uint32_t*>(kc + 4 * wd) = zero ? 0u : (cst[i] ^ m2c[i]);
-      }
-      if constexpr (QJ) {
-        *reinterpret_cast<uint32_t*>(base + a.lay.kqjl + s * (MD / 8) + 4 * g) = qw;
-        if (g == 0)
-          *reinterpret_cast<uint32_t*>(base + a.lay.kmeta + s * 4) =
-              (uint32_t)f32_to_f16_bits(zero ? 0.f : nrm) | ((uint32_t)f32_to_f16_bits(gamma) << 16);
-      } else if (g == 0) {
-        *reinterpret_cast<uint16_t*>(base + a.lay.kmeta + s * 2) = f32_to_f16_bits(zero ? 0.f : nrm);
-      }
-    }
-
     // -------------------------------------------------------------- value
     // row-part layout: lane l holds channels 32 (l % 4) .. + 31 of row l / 4
     {
-      const int vrow = lane >> 2, part = lane & 3;
-      const int64_t tv = t0 + vrow;
-      const bool vvalid = tv < a.num_tokens;
-      const int64_t thv = tv * a.hkv + hh;
+      const int part = vpart;
       float x[32];
-      {
-        const u32x4* pv = reinterpret_cast<const u32x4*>(a.v + (vvalid ? thv : 0) * MD + 32 * part);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const u32x4 w = vvalid ? __builtin_nontemporal_load(pv + i) : u32x4{0u, 0u, 0u, 0u};
+      for (int i = 0; i < 4; ++i) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            x[8 * i + 2 * j] = __uint_as_float(w[j] << 16);
-            x[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
-          }
+        for (int j = 0; j < 4; ++j) {
+          x[8 * i + 2 * j] = __uint_as_float(vraw[i][j] << 16);
+          x[8 * i + 2 * j + 1] = __uint_as_float(vraw[i][j] & 0xFFFF0000u);
         }
       }
       constexpr float LV = (float)((1 << VB) - 1);
@@ -417,7 +405,26 @@ __global__ __launch_bounds__(mwaves<QJ>() * 64) void quantize_mfma_kernel(QMArgs
           vw[(e * VB) / 32] |= (uint32_t)q << ((e * VB) % 32);
         }
       }
-      const int32_t vslot = vvalid ? a.slot_mapping[tv] : -1;
+      // ---- store the key record (after the value arithmetic: a wait for the
+      // value rows issued after these stores would also wait for the stores)
+      if (valid && slot >= 0 && (int64_t)slot < a.slots_total) {
+        uint8_t* base = a.pool + ((int64_t)(slot >> 4) * a.hkv + hh) * a.rec;
+        const int s = slot & 15;
+        uint8_t* kc = base + a.lay.kcodes + s * (KB * MD / 8);
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+          const int wd = stream_dword<KB>(g, i);
+          *reinterpret_cast<uint32_t*>(kc + 4 * wd) = zero ? 0u : (cst[i] ^ m2c[i]);
+        }
+        if constexpr (QJ) {
+          *reinterpret_cast<uint32_t*>(base + a.lay.kqjl + s * (MD / 8) + 4 * g) = qw;
+          if (g == 0)
+            *reinterpret_cast<uint32_t*>(base + a.lay.kmeta + s * 4) =
+                (uint32_t)f32_to_f16_bits(zero ? 0.f : nrm) | ((uint32_t)f32_to_f16_bits(gamma) << 16);
+        } else if (g == 0) {
+          *reinterpret_cast<uint16_t*>(base + a.lay.kmeta + s * 2) = f32_to_f16_bits(zero ? 0.f : nrm);
+        }
+      }
       if (vvalid && vslot >= 0 && (int64_t)vslot < a.slots_total) {
         uint8_t* base = a.pool + ((int64_t)(vslot >> 4) * a.hkv + hh) * a.rec;
         const int s = vslot & 15;
