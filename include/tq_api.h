@@ -208,7 +208,8 @@ typedef struct {
   int32_t q_dtype;           /* TQ_DTYPE_BF16 or TQ_DTYPE_F32 */
   int32_t batch;             /* 0 .. 8192 */
   int32_t num_q_heads;
-  int32_t num_kv_heads;      /* num_q_heads % num_kv_heads == 0, G <= 8 */
+  int32_t num_kv_heads;      /* num_q_heads % num_kv_heads == 0, G <= 8; num_kv_heads x the
+                                record bytes of a block < 2^31 */
   int32_t num_presets;       /* 1 or 2 */
   const tq_ctx* ctx[2];      /* same head_dim; one pool per preset */
   const void* pool[2];       /* device pools written by tq_quantize_store */

@@ -25,11 +25,11 @@
 //            from an LDS byte table for the sign bits (MSE-only keys: the
 //            first product alone);
 //   softmax  running max / sum per head in the exp2 domain;
-//   values   acc[(group, head)][channel] += (p s)_hi,lo . (1024 + sigma q) on
-//            v_mfma_f32_16x16x32_f16, with the zero-points folded into one
-//            per-(group, head) scalar and the bias removed by one more
-//            product; only the rows of each column's own group are kept at
-//            the end.
+//   values   acc[(group, head)][channel] += (p s)_hi,lo . (sigma q 2^-24) on
+//            v_mfma_f32_16x16x32_f16, the codes masked in place as fp16
+//            subnormals, with the zero-points folded into one
+//            per-(group, head) scalar; only the rows of each column's own
+//            group are kept at the end.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -264,9 +264,12 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h_, int t0_, int 
   const int h = __builtin_amdgcn_readfirstlane(h_);
   const int t0 = __builtin_amdgcn_readfirstlane(t0_), t1 = __builtin_amdgcn_readfirstlane(t1_);
   const int tok = lane & 15, kq = lane >> 4;
-  const uint8_t* pool = a.pool[pr];
   const int64_t rec = a.rec[pr];
-  const int64_t pblocks = a.pool_blocks[pr];
+  // record (block, h) starts at head_base + block * blk_stride; the host
+  // keeps num_kv_heads * record bytes below 2^31, so the product is one
+  // 32 x 32 -> 64-bit multiply
+  const uint64_t head_base = reinterpret_cast<uint64_t>(a.pool[pr]) + (uint64_t)h * (uint64_t)rec;
+  const uint32_t blk_stride = (uint32_t)(a.Hkv * rec);
   float* sp = s_p + wave * SplitLds<D, GP, KB, VB, QJ>::kPWave;
   unsigned char* ring = s_main + wave * R::nslot * R::slot;
   const uint32_t ring_lds = lds_offset(ring);
@@ -297,7 +300,7 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h_, int t0_, int 
     for (int half = 0; half < 2; ++half) {
       const int blk = __builtin_amdgcn_readfirstlane(s_blk[2 * st + half]);
       const bool ok = blk >= 0;  // validated at staging
-      const uint64_t base = reinterpret_cast<uint64_t>(pool + ((int64_t)(ok ? blk : 0) * a.Hkv + h) * rec);
+      const uint64_t base = head_base + (uint64_t)(uint32_t)(ok ? blk : 0) * blk_stride;
       const uint32_t dst = ring_lds + sl * R::slot + half * R::bytes;
 #pragma unroll
       for (int j = 0; j < DPR; ++j) {
@@ -307,12 +310,11 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h_, int t0_, int 
     }
   };
 
-  f32x4 accv[CS][RT][CT], accb[CS][RT];
+  f32x4 accv[CS][RT][CT];
 #pragma unroll
   for (int cs = 0; cs < CS; ++cs)
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      accb[cs][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) accv[cs][rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -325,9 +327,7 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h_, int t0_, int 
 #pragma unroll
   for (int g = 0; g < GP; ++g) m_run[g] = -INFINITY;
   float lsum[4] = {0.f, 0.f, 0.f, 0.f};  // per-lane partial sums (rows of lanes 0..31)
-  const uint32_t c1024 = opaque_u32(0x64006400u);  // two fp16 1024.0
   const uint32_t k4300 = UN ? opaque_u32(0x43004300u) : 0u;  // two bf16 128.0
-  const f16x8 k1024 = __builtin_bit_cast(f16x8, u32x4{c1024, c1024, c1024, c1024});
   const int arow = lane & 15;
   // VB = 2: lane column j takes bytes 2 (j >> 3) and 2 (j >> 3) + 1 of its dword column
   uint32_t vsel[2];
@@ -517,7 +517,6 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h_, int t0_, int 
           for (int r = 0; r < 4; ++r) {
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) accv[cs][rt][ct][r] *= alpha[4 * rt + r];
-            accb[cs][rt][r] *= alpha[4 * rt + r];
           }
           float az = alpha[4 * rt];
 #pragma unroll
@@ -542,11 +541,12 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h_, int t0_, int 
     wait_lgkm0();  // the weights are in LDS
     __builtin_amdgcn_s_setprio(0);
     // ------------------------------------------------------------ values
-    // fp16 MFMA: A = p s as fp16 hi + lo, B = 1024 + sigma q exactly (code bits
-    // or-ed into mantissa bits 4..7 of 1024, so sigma = 16, or 64 for the upper
-    // 2-bit field); the 1024 sum_t A_t bias comes from one MFMA against a
-    // constant 1024 tile.  Keeping the codes in the upper mantissa bits keeps
-    // the bias within a factor ~10 of the signal it is subtracted from.
+    // fp16 MFMA: A = p s as fp16 hi + lo, B = the code bits masked in place:
+    // a code at mantissa bits k .. k + b - 1 of a zero exponent is the fp16
+    // subnormal q 2^(k - 24), exact, so B needs one AND per dword and no
+    // offset (sigma = 2^k is divided out per column at the end).  The matrix
+    // cores take subnormal fp16 operands as they are, and with no offset the
+    // fp32 accumulators carry only the signal.
     const bool vblk_ok = vhalf ? ok1 : ok0;
     const int vtok0 = base + 8 * kq;
 #pragma unroll
@@ -566,17 +566,17 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h_, int t0_, int 
 #pragma unroll
           for (int bi = 0; bi < 4; ++bi) {
             const uint32_t y = __builtin_amdgcn_perm(xv[2 * i + 1], xv[2 * i], (uint32_t)bi | ((uint32_t)(4 + bi) << 16));
-            bv[2 * bi][i] = and_or(y << 4, 0x00F000F0u, c1024);
-            bv[2 * bi + 1][i] = and_or(y, 0x00F000F0u, c1024);
+            bv[2 * bi][i] = y & 0x000F000Fu;
+            bv[2 * bi + 1][i] = y & 0x00F000F0u;
           }
         } else {
 #pragma unroll
           for (int bb = 0; bb < 2; ++bb) {
             const uint32_t y = __builtin_amdgcn_perm(xv[2 * i + 1], xv[2 * i], vsel[bb]);
-            bv[4 * bb + 0][i] = and_or(y << 4, 0x00300030u, c1024);
-            bv[4 * bb + 1][i] = and_or(y << 4, 0x00C000C0u, c1024);
-            bv[4 * bb + 2][i] = and_or(y, 0x00300030u, c1024);
-            bv[4 * bb + 3][i] = and_or(y, 0x00C000C0u, c1024);
+            bv[4 * bb + 0][i] = y & 0x00030003u;
+            bv[4 * bb + 1][i] = y & 0x000C000Cu;
+            bv[4 * bb + 2][i] = y & 0x00300030u;
+            bv[4 * bb + 3][i] = y & 0x00C000C0u;
           }
         }
       }
@@ -597,8 +597,6 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h_, int t0_, int 
           z = __builtin_fmaf(pw[e], f16_bits_to_f32((uint16_t)(sz[e] >> 16)), z);
         }
         zacc[cs][rt] = z;
-        accb[cs][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, k1024, accb[cs][rt], 0, 0, 0);
-        accb[cs][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Al, k1024, accb[cs][rt], 0, 0, 0);
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
           const f16x8 B = __builtin_bit_cast(f16x8, bv[ct]);
@@ -691,22 +689,22 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h_, int t0_, int 
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        // zero-point term of row (group gl, head 4 rt + r) sits in A row 4 gl + r;
-        // the bias row-sum sits in this lane's own output row
+        // zero-point term of row (group gl, head 4 rt + r) sits in A row 4 gl + r
         const float zv = __shfl(zacc[cs][rt], 4 * gl + r, 64);
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
           int ch;
-          float inv;  // 1 / sigma of the tile's field position
+          float inv;  // 2^24 / sigma of the tile's field position (low nibble sigma 1, high 16)
           if constexpr (VB == 4) {
             ch = 128 * cs + 8 * j + 2 * (ct >> 1) + (ct & 1);
-            inv = 0.0625f;
+            inv = (ct & 1) ? 1048576.f : 16777216.f;
           } else {
             ch = 128 * cs + 16 * (j & 7) + 4 * (2 * (j >> 3) + (ct >> 2)) + (ct & 3);
-            inv = (ct & 1) ? 0.015625f : 0.0625f;
+            // 2-bit fields at bits 0, 2, 4, 6: sigma 1, 4, 16, 64
+            inv = (ct & 3) == 0 ? 16777216.f : (ct & 3) == 1 ? 4194304.f : (ct & 3) == 2 ? 1048576.f : 262144.f;
           }
           if ((ch >> 5) - 4 * cs == gl)
-            mw[(4 * rt + r) * D + ch] = __builtin_fmaf(accv[cs][rt][ct][r] - accb[cs][rt][r], inv, zv);
+            mw[(4 * rt + r) * D + ch] = __builtin_fmaf(accv[cs][rt][ct][r], inv, zv);
         }
       }
   // l per head: row sums of the lane groups that held the head's two token halves

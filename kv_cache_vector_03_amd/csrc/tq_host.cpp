@@ -690,6 +690,13 @@ int check_decode_shape(const tq_decode_args* a) {
               a->num_kv_heads);
     return TQ_EINVAL;
   }
+  for (int i = 0; i < a->num_presets; ++i) {
+    if ((int64_t)a->num_kv_heads * a->ctx[i]->lay.bytes >= ((int64_t)1 << 31)) {
+      set_error("decode: num_kv_heads %d x %d-byte records per block exceeds 2^31 bytes", a->num_kv_heads,
+                (int)a->ctx[i]->lay.bytes);
+      return TQ_EUNSUPPORTED;
+    }
+  }
   int G = a->num_q_heads / a->num_kv_heads;
   if (G > 8) {
     set_error("decode: query heads per KV head %d > 8 is not supported", G);
