@@ -26,8 +26,9 @@
 //            first product alone);
 //   softmax  running max / sum per head in the exp2 domain;
 //   values   acc[(group, head)][channel] += (p s)_hi,lo . (sigma q 2^-24) on
-//            v_mfma_f32_16x16x32_f16, the codes masked in place as fp16
-//            subnormals, with the zero-points folded into one
+//            v_mfma_f32_16x16x32_f16, each code placed at mantissa bit 4 (or
+//            bit 6 for half of the 2-bit codes) of an fp16 subnormal, with the
+//            zero-points folded into one
 //            per-(group, head) scalar; only the rows of each column's own
 //            group are kept at the end.
 #include <hip/hip_runtime.h>
@@ -541,12 +542,14 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h_, int t0_, int 
     wait_lgkm0();  // the weights are in LDS
     __builtin_amdgcn_s_setprio(0);
     // ------------------------------------------------------------ values
-    // fp16 MFMA: A = p s as fp16 hi + lo, B = the code bits masked in place:
-    // a code at mantissa bits k .. k + b - 1 of a zero exponent is the fp16
-    // subnormal q 2^(k - 24), exact, so B needs one AND per dword and no
-    // offset (sigma = 2^k is divided out per column at the end).  The matrix
-    // cores take subnormal fp16 operands as they are, and with no offset the
-    // fp32 accumulators carry only the signal.
+    // fp16 MFMA: A = p s as fp16 hi + lo, B = the code bits placed in the
+    // mantissa of a zero exponent: a code at bits k .. k + b - 1 is the fp16
+    // subnormal q 2^(k - 24), exact, with no offset to subtract (sigma = 2^k
+    // is divided out per column at the end), so B costs one shift and / or
+    // one AND per dword.  The codes sit at bit 4 or above: the matrix cores
+    // take subnormal operands, but products with the smallest ones (codes in
+    // bits 0..3) measured ~8x less precise per product than with codes at
+    // bits 4..7, which are as precise as normal operands.
     const bool vblk_ok = vhalf ? ok1 : ok0;
     const int vtok0 = base + 8 * kq;
 #pragma unroll
@@ -566,15 +569,15 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h_, int t0_, int 
 #pragma unroll
           for (int bi = 0; bi < 4; ++bi) {
             const uint32_t y = __builtin_amdgcn_perm(xv[2 * i + 1], xv[2 * i], (uint32_t)bi | ((uint32_t)(4 + bi) << 16));
-            bv[2 * bi][i] = y & 0x000F000Fu;
+            bv[2 * bi][i] = (y << 4) & 0x00F000F0u;
             bv[2 * bi + 1][i] = y & 0x00F000F0u;
           }
         } else {
 #pragma unroll
           for (int bb = 0; bb < 2; ++bb) {
             const uint32_t y = __builtin_amdgcn_perm(xv[2 * i + 1], xv[2 * i], vsel[bb]);
-            bv[4 * bb + 0][i] = y & 0x00030003u;
-            bv[4 * bb + 1][i] = y & 0x000C000Cu;
+            bv[4 * bb + 0][i] = (y << 4) & 0x00300030u;
+            bv[4 * bb + 1][i] = (y << 4) & 0x00C000C0u;
             bv[4 * bb + 2][i] = y & 0x00300030u;
             bv[4 * bb + 3][i] = y & 0x00C000C0u;
           }
@@ -694,14 +697,14 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h_, int t0_, int 
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
           int ch;
-          float inv;  // 2^24 / sigma of the tile's field position (low nibble sigma 1, high 16)
+          float inv;  // 2^24 / sigma of the tile's field position
           if constexpr (VB == 4) {
             ch = 128 * cs + 8 * j + 2 * (ct >> 1) + (ct & 1);
-            inv = (ct & 1) ? 1048576.f : 16777216.f;
+            inv = 1048576.f;
           } else {
             ch = 128 * cs + 16 * (j & 7) + 4 * (2 * (j >> 3) + (ct >> 2)) + (ct & 3);
-            // 2-bit fields at bits 0, 2, 4, 6: sigma 1, 4, 16, 64
-            inv = (ct & 3) == 0 ? 16777216.f : (ct & 3) == 1 ? 4194304.f : (ct & 3) == 2 ? 1048576.f : 262144.f;
+            // 2-bit fields at bits 4 and 6: sigma 16 and 64
+            inv = (ct & 1) ? 262144.f : 1048576.f;
           }
           if ((ch >> 5) - 4 * cs == gl)
             mw[(4 * rt + r) * D + ch] = __builtin_fmaf(accv[cs][rt][ct][r], inv, zv);
