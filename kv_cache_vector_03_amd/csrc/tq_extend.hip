@@ -3,11 +3,14 @@
 // kernel over the compressed pool beside the fused decode kernel; §4.4: the
 // prefill path is where rotation and quantisation cost shows).
 //
-// One workgroup of four waves per (sequence b, KV head h, tile of 64 query
+// One workgroup of eight waves per (sequence b, KV head h, tile of 128 query
 // rows); a row is one (chunk token, query head) pair, row r = token r / G,
 // head h G + r % G, and wave w owns rows 16 w .. 16 w + 15.  The workgroup
-// reads the compressed prefix once, 32 tokens (two paged records) per step:
-//   build  (all 256 threads): the step's records go to LDS, and from them the
+// reads the compressed prefix once, 32 tokens (two paged records) per step,
+// software-pipelined with one barrier per step (the records of step s + 2 are
+// stored and those of step s + 3 loaded while step s + 1 is built and step s
+// computed):
+//   build  (all 512 threads): the step's records go to LDS, and from them the
 //          MFMA B tiles every wave shares: the rotated centroids c[idx] of the
 //          32 tokens as fp16 hi and lo parts (two codes per lookup of an fp16
 //          pair table), the QJL sign bits as fp16 +-1 (one lookup per sign
@@ -36,7 +39,7 @@ namespace {
 
 constexpr int ED = 128;                 // head_dim of the extend kernels
 constexpr int EKT = ED / 32;            // k-slices of one MFMA row
-constexpr int ENW = 4;                  // waves per workgroup
+constexpr int ENW = 8;                  // waves per workgroup
 constexpr int ERPW = 16;                // query rows per wave
 constexpr int EROWS = ENW * ERPW;       // query rows per workgroup
 constexpr int EKR = ED + 8;             // chunk K tile row stride (bf16 elements)
@@ -63,16 +66,20 @@ struct ELds {
   using R = ERec<KB, VB, QJ>;
   static constexpr int pair = 0;                                  // uint2 [2^(2 KB)]
   static constexpr int sgn = pair + 8 * (1 << (2 * KB));          // u32x4 [256] (QJL)
-  static constexpr int rows = sgn + (QJ ? 256 * 16 : 0);          // float uq[64], up[64]
-  static constexpr int ring = rows + 2 * EROWS * 4;               // the step's two records
-  static constexpr int kc = align16(ring + 2 * R::bytes);         // u32x4 [2 half][EKT][2 part][64]
-  static constexpr int ks = kc + 2 * EKT * 2 * 64 * 16;           // u32x4 [2 half][EKT][64]
-  static constexpr int vt = ks + (QJ ? 2 * EKT * 64 * 16 : 0);    // u32x4 [8 ct][2 part][64]
-  static constexpr int ps = vt + 8 * 2 * 64 * 16;                 // float [ENW][16][EPS]
+  static constexpr int rows = sgn + (QJ ? 256 * 16 : 0);          // float uq[EROWS], up[EROWS]
+  static constexpr int ring = rows + 2 * EROWS * 4;               // three slots of a step's two records
+  static constexpr int ring_slot = align16(2 * R::bytes);
+  static constexpr int kc = align16(ring + 3 * ring_slot);        // two buffers of u32x4 [2 half][EKT][2 part][64]
+  static constexpr int kc_buf = 2 * EKT * 2 * 64 * 16;
+  static constexpr int ks = kc + 2 * kc_buf;                      // two buffers of u32x4 [2 half][EKT][64]
+  static constexpr int ks_buf = QJ ? 2 * EKT * 64 * 16 : 0;
+  static constexpr int vt = ks + 2 * ks_buf;                      // two buffers of u32x4 [8 ct][2 part][64]
+  static constexpr int vt_buf = 8 * 2 * 64 * 16;
+  static constexpr int ps = vt + 2 * vt_buf;                      // float [ENW][16][EPS]
   static constexpr int ck = ps + ENW * 16 * EPS * 4;              // bf16 [32][EKR]
   static constexpr int cv = ck + 32 * EKR * 2;                    // fp16 [ED][EVS]
   static constexpr int end = cv + ED * EVS * 2;
-  static constexpr int stage = kc;                                // prologue: float q~ [64][ED], p [64][ED]
+  static constexpr int stage = kc;                                // prologue: float q~ [EROWS][ED], p [EROWS][ED]
   static constexpr int stage_end = stage + 2 * EROWS * ED * 4;
   static constexpr int total = end > stage_end ? end : stage_end;
   static_assert(total <= 160 * 1024, "extend workgroup LDS");
@@ -204,9 +211,6 @@ __global__ __launch_bounds__(ENW * 64) void extend_kernel(EArgs a) {
   float* s_uq = reinterpret_cast<float*>(lds + LD::rows);
   float* s_up = s_uq + EROWS;
   unsigned char* ring = lds + LD::ring;
-  const u32x4* s_kc = reinterpret_cast<const u32x4*>(lds + LD::kc);
-  const u32x4* s_ks = reinterpret_cast<const u32x4*>(lds + LD::ks);
-  const u32x4* s_vt = reinterpret_cast<const u32x4*>(lds + LD::vt);
   float* sp = reinterpret_cast<float*>(lds + LD::ps) + wave * 16 * EPS;
   uint16_t* s_ck = reinterpret_cast<uint16_t*>(lds + LD::ck);
   uint16_t* s_cv = reinterpret_cast<uint16_t*>(lds + LD::cv);
@@ -221,7 +225,7 @@ __global__ __launch_bounds__(ENW * 64) void extend_kernel(EArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       w[e] = (((tid >> (2 * e)) & 1) ? 0x3C00u : 0xBC00u) | ((((tid >> (2 * e + 1)) & 1) ? 0x3C00u : 0xBC00u) << 16);
-    s_sgn[tid] = w;  // 256 threads, one entry each
+    if (tid < 256) s_sgn[tid] = w;  // one entry per thread
   }
 
   // ---- rotate this wave's 16 query rows: q~ = D2 (H / sqrt d) D1 q into st_q
@@ -381,48 +385,62 @@ __global__ __launch_bounds__(ENW * 64) void extend_kernel(EArgs a) {
   for (int ct = 0; ct < 8; ++ct) st.acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // ---------------------------------------------------------- the prefix
+  // A software pipeline over 32-token steps with one barrier per step: the
+  // iteration of step s stores the records of step s + 2 into its ring slot
+  // (three slots), issues the loads of step s + 3, computes the scores of
+  // step s, builds the B tiles of step s + 1 into the tile buffer step s does
+  // not use (between the score and value products, in the same basic block,
+  // so the compiler can interleave the build's VALU and LDS work with the
+  // matrix products), and finishes step s.  The barrier that ends the
+  // iteration orders its writes before the next iteration's reads: a ring
+  // slot is rewritten two iterations after its step was built and one after
+  // it was computed, a tile buffer one iteration after its step was computed.
+  // Measured on the prefill workload: 2017 us with four-wave workgroups and
+  // two barriers per step, 1625 us with eight waves, 1481 us pipelined,
+  // 1433 us with the build placed between the products.
   const int nsteps = (P + 31) / 32;
   const int32_t* btrow = a.bt + (int64_t)b * a.max_blocks;
-  // 16-byte pieces of the step's two records: thread t copies pieces t and t + 256
+  // 16-byte pieces of a step's two records: thread t copies pieces t, t + ENW * 64, ..
   constexpr int NPC = 2 * R::pieces;
-  auto fetch = [&](int s, u32x4 (&pf)[2], bool (&okb)[2]) {
+  constexpr int NFJ = (NPC + ENW * 64 - 1) / (ENW * 64);
+  auto fetch = [&](int st, u32x4 (&pf)[NFJ]) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < NFJ; ++j) {
       const int pc = tid + j * ENW * 64;
       pf[j] = u32x4{0u, 0u, 0u, 0u};
-      okb[j] = false;
       if (pc < NPC) {
         const int rr = pc / R::pieces, off = (pc % R::pieces) * 16;
-        const int bi = 2 * s + rr;
+        const int bi = 2 * st + rr;
         const int blk = (bi < a.max_blocks && 16 * bi < P) ? btrow[bi] : -1;
-        if (blk >= 0 && (int64_t)blk < a.pool_blocks) {
+        if (blk >= 0 && (int64_t)blk < a.pool_blocks)
           pf[j] = __builtin_nontemporal_load(
               reinterpret_cast<const u32x4*>(a.pool + ((int64_t)blk * a.Hkv + h) * a.rec + off));
-          okb[j] = true;
-        }
       }
     }
   };
-  u32x4 pf[2];
-  bool pok[2];
-  if (nsteps > 0) fetch(0, pf, pok);
-  for (int s = 0; s < nsteps; ++s) {
-    // records of step s into the ring, then the next step's loads go out
+  auto ring_at = [&](int st) -> unsigned char* { return ring + (st % 3) * LD::ring_slot; };
+  auto store_ring = [&](int st, const u32x4 (&pf)[NFJ]) {
+    unsigned char* rg = ring_at(st);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < NFJ; ++j) {
       const int pc = tid + j * ENW * 64;
-      if (pc < NPC) *reinterpret_cast<u32x4*>(ring + pc * 16) = pf[j];
+      if (pc < NPC) *reinterpret_cast<u32x4*>(rg + pc * 16) = pf[j];
     }
-    if (s + 1 < nsteps) fetch(s + 1, pf, pok);
-    __syncthreads();  // ring complete; every wave is done with the previous step's tiles
-    // ---- build the shared B tiles (two slots of each kind per thread)
-    const int t_base = 32 * s;
+  };
+  // the shared B tiles of step st from its ring slot (512 slots of each kind)
+  auto build = [&](int st) {
+    const unsigned char* rg = ring_at(st);
+    u32x4* kcb = reinterpret_cast<u32x4*>(lds + LD::kc + (st & 1) * LD::kc_buf);
+    u32x4* ksb = reinterpret_cast<u32x4*>(lds + LD::ks + (st & 1) * LD::ks_buf);
+    u32x4* vtb = reinterpret_cast<u32x4*>(lds + LD::vt + (st & 1) * LD::vt_buf);
+    // one slot of each kind per thread
+    const int t_base = 32 * st;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < 512 / (ENW * 64); ++j) {
       const int slot = tid + j * ENW * 64;  // (half, kt, lane) = (slot / 256, (slot / 64) % 4, slot % 64)
       const int half = slot >> 8, kt = (slot >> 6) & 3, ln = slot & 63;
       const int n = ln & 15, kq = ln >> 4;
-      const unsigned char* rec = ring + half * R::bytes;
+      const unsigned char* rec = rg + half * R::bytes;
       // 8 codes (coordinates 32 kt + 8 kq ..) of token n
       const int bit0 = KB * (32 * kt + 8 * kq);
       const unsigned char* cs = rec + R::kcodes + n * (KB * ED / 8);
@@ -442,19 +460,19 @@ __global__ __launch_bounds__(ENW * 64) void extend_kernel(EArgs a) {
         bh[pi] = pe.x;
         bl[pi] = pe.y;
       }
-      u32x4* kcw = reinterpret_cast<u32x4*>(lds + LD::kc) + ((half * EKT + kt) * 2) * 64 + ln;
+      u32x4* kcw = kcb + ((half * EKT + kt) * 2) * 64 + ln;
       kcw[0] = bh;
       kcw[64] = bl;
       if constexpr (QJ) {
         const uint32_t byte = rec[R::kqjl + n * (ED / 8) + 4 * kt + kq];
-        reinterpret_cast<u32x4*>(lds + LD::ks)[(half * EKT + kt) * 64 + ln] = s_sgn[byte];
+        ksb[(half * EKT + kt) * 64 + ln] = s_sgn[byte];
       }
       // values: channel tile ct = slot / 64, channel 16 ct + n, tokens 8 kq .. + 7
       // (record kq / 2, slots 8 (kq % 2) .. + 7)
       {
         const int ct = slot >> 6;
         const int c = 16 * ct + n;
-        const unsigned char* vr = ring + (kq >> 1) * R::bytes;
+        const unsigned char* vr = rg + (kq >> 1) * R::bytes;
         const int s0 = 8 * (kq & 1);
         constexpr int CPB = 8 / VB;              // codes per byte
         const int f = c / CPB;                   // byte of the code stream
@@ -483,12 +501,34 @@ __global__ __launch_bounds__(ENW * 64) void extend_kernel(EArgs a) {
           vh[e2] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
           vl[e2] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
         }
-        u32x4* vtw = reinterpret_cast<u32x4*>(lds + LD::vt) + (ct * 2) * 64 + ln;
+        u32x4* vtw = vtb + (ct * 2) * 64 + ln;
         vtw[0] = vh;
         vtw[64] = vl;
       }
     }
-    __syncthreads();
+  };
+  u32x4 pf[NFJ];
+  if (nsteps > 0) {
+    fetch(0, pf);
+    store_ring(0, pf);
+  }
+  if (nsteps > 1) {
+    fetch(1, pf);
+    store_ring(1, pf);
+  }
+  if (nsteps > 2) fetch(2, pf);
+  __syncthreads();
+  if (nsteps > 0) build(0);
+  __syncthreads();
+  for (int s = 0; s < nsteps; ++s) {
+    // unconditional: past the prefix the loads read nothing (zeros), and the
+    // ring slot and tile buffer written are never read
+    store_ring(s + 2, pf);
+    fetch(s + 3, pf);
+    const u32x4* s_kc = reinterpret_cast<const u32x4*>(lds + LD::kc + (s & 1) * LD::kc_buf);
+    const u32x4* s_ks = reinterpret_cast<const u32x4*>(lds + LD::ks + (s & 1) * LD::ks_buf);
+    const u32x4* s_vt = reinterpret_cast<const u32x4*>(lds + LD::vt + (s & 1) * LD::vt_buf);
+    const int t_base = 32 * s;
     // ---- scores of the wave's 16 rows against the step's 32 tokens
     float x[2][4];
 #pragma unroll
@@ -507,7 +547,7 @@ __global__ __launch_bounds__(ENW * 64) void extend_kernel(EArgs a) {
           aq = __builtin_amdgcn_mfma_f32_16x16x32_f16(apl[kt], bs, aq, 0, 0, 0);
         }
       }
-      const unsigned char* rec = ring + half * R::bytes;
+      const unsigned char* rec = ring_at(s) + half * R::bytes;
       const int tok = t_base + 16 * half + col;
       const int bi = 2 * s + half;
       const int blk = 16 * bi < P ? btrow[bi] : -1;  // uniform
@@ -523,6 +563,7 @@ __global__ __launch_bounds__(ENW * 64) void extend_kernel(EArgs a) {
         x[half][r] = live ? nv * v : -INFINITY;
       }
     }
+    build(s + 1);
     softmax_stage(st, x, sp, lane);
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the weights are in LDS
     __builtin_amdgcn_wave_barrier();
@@ -536,6 +577,7 @@ __global__ __launch_bounds__(ENW * 64) void extend_kernel(EArgs a) {
       st.acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, bl, st.acc[ct], 0, 0, 0);
       st.acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Al, bh, st.acc[ct], 0, 0, 0);
     }
+    __syncthreads();
   }
 
   // ------------------------------------------------------- the chunk itself
@@ -544,7 +586,7 @@ __global__ __launch_bounds__(ENW * 64) void extend_kernel(EArgs a) {
     __syncthreads();  // every wave is done with the previous tiles
     // K tile [32][D] bf16 and V tile transposed [D][32] fp16
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < 512 / (ENW * 64); ++j) {
       const int pc = tid + j * ENW * 64;  // 512 pieces of 16 bytes: token pc / 16, channels 8 (pc % 16) ..
       const int t = pc >> 4, c8 = (pc & 15) * 8;
       const int tok = j0 + t;
