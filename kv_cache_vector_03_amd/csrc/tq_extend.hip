@@ -37,6 +37,8 @@
 namespace tq {
 namespace {
 
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
 constexpr int ED = 128;                 // head_dim of the extend kernels
 constexpr int EKT = ED / 32;            // k-slices of one MFMA row
 constexpr int ENW = 8;                  // waves per workgroup
@@ -111,6 +113,14 @@ __device__ __forceinline__ void split_f16(float x, _Float16& hi, _Float16& lo) {
   hi = (_Float16)x;
   lo = (_Float16)(x - (float)hi);
 }
+// fp16 hi / lo parts of two values packed in dwords: hi truncated (round
+// toward zero, one instruction for both), x - hi exact in fp32, lo truncated:
+// x = hi + lo to ~2^-22 relative
+__device__ __forceinline__ uint2 split2_f16(float x, float y) {
+  const auto h = __builtin_amdgcn_cvt_pkrtz(x, y);
+  const auto l = __builtin_amdgcn_cvt_pkrtz(x - (float)h[0], y - (float)h[1]);
+  return make_uint2(__builtin_bit_cast(uint32_t, h), __builtin_bit_cast(uint32_t, l));
+}
 __device__ __forceinline__ float row16_max(float x) {
   x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false)));
   x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false)));
@@ -177,13 +187,15 @@ __device__ __forceinline__ void weights_a(const float* sp, int lane, f16x8& Ah, 
   const f32x4 a = *reinterpret_cast<const f32x4*>(src);
   const f32x4 b = *reinterpret_cast<const f32x4*>(src + 4);
   const float w[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  u32x4 hv, lv;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    _Float16 h, l;
-    split_f16(w[e], h, l);
-    Ah[e] = h;
-    Al[e] = l;
+  for (int e2 = 0; e2 < 4; ++e2) {
+    const uint2 hl = split2_f16(w[2 * e2], w[2 * e2 + 1]);
+    hv[e2] = hl.x;
+    lv[e2] = hl.y;
   }
+  Ah = __builtin_bit_cast(f16x8, hv);
+  Al = __builtin_bit_cast(f16x8, lv);
 }
 
 template <int KB, int VB, bool QJ>
@@ -397,7 +409,8 @@ __global__ __launch_bounds__(ENW * 64) void extend_kernel(EArgs a) {
   // it was computed, a tile buffer one iteration after its step was computed.
   // Measured on the prefill workload: 2017 us with four-wave workgroups and
   // two barriers per step, 1625 us with eight waves, 1481 us pipelined,
-  // 1433 us with the build placed between the products.
+  // 1433 us with the build placed between the products, 1402 us with the
+  // two-value fp16 splits.
   const int nsteps = (P + 31) / 32;
   const int32_t* btrow = a.bt + (int64_t)b * a.max_blocks;
   // 16-byte pieces of a step's two records: thread t copies pieces t, t + ENW * 64, ..
@@ -491,15 +504,13 @@ __global__ __launch_bounds__(ENW * 64) void extend_kernel(EArgs a) {
             const int e = 2 * e2 + u;
             const int tok = t_base + 16 * (kq >> 1) + s0 + e;
             const float qv = (float)((cd[e] >> sh) & ((1u << VB) - 1u));
-            const float v = __builtin_fmaf(qv, f16_bits_to_f32((uint16_t)(md[e] & 0xFFFFu)),
-                                           f16_bits_to_f32((uint16_t)(md[e] >> 16)));
+            const f16x2 sz = __builtin_bit_cast(f16x2, md[e]);  // {s, z}
+            const float v = __builtin_fmaf(qv, (float)sz[0], (float)sz[1]);
             vv[u] = (tok < P) ? v : 0.f;  // tokens past the prefix (or in a skipped block) hold no data
           }
-          _Float16 h0, l0, h1, l1;
-          split_f16(vv[0], h0, l0);
-          split_f16(vv[1], h1, l1);
-          vh[e2] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-          vl[e2] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+          const uint2 hl = split2_f16(vv[0], vv[1]);
+          vh[e2] = hl.x;
+          vl[e2] = hl.y;
         }
         u32x4* vtw = vtb + (ct * 2) * 64 + ln;
         vtw[0] = vh;
