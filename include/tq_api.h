@@ -239,14 +239,11 @@ typedef struct {
 } tq_decode_args;
 
 /* Decode flags.
- *   TQ_DECODE_DETERMINISTIC : the waves of a workgroup take the 32-token steps
- *     of a split in a fixed order instead of claiming the next free step, so
- *     every fp32 sum is formed in the same order on every call and the outputs
- *     (and scores) are bit-identical from run to run and between eager and
- *     graph-replayed launches.  Without it the step a wave takes depends on
- *     issue timing and outputs differ run to run by fp32 reassociation
- *     (~1e-5 relative); it is the faster schedule when the waves of a CU
- *     progress unevenly.
+ *   TQ_DECODE_DETERMINISTIC : accepted and has no further effect: every call
+ *     takes the 32-token steps of a split in a fixed order per wave, so every
+ *     fp32 sum is formed in the same order and the outputs (and scores) are
+ *     bit-identical from run to run and between eager and graph-replayed
+ *     launches, with or without the flag.
  * Other bits are rejected with TQ_EINVAL. */
 enum { TQ_DECODE_DETERMINISTIC = 1 };
 

@@ -407,8 +407,9 @@ def tq_decode_attention(q, ctxs, pools, block_tables, seq_lens, out, workspace, 
     workspace: device uint8 tensor of tq_decode_workspace_bytes(...) bytes.
     Keyword arguments: seq_preset (int8 [B]), recent_k / recent_v (bf16
     [B, Hkv, W, d]) with recent_lens (int32 [B]), sm_scale, chunk_tokens,
-    max_seq_len, scores_out (float32 [B, Hq, stride]), deterministic (a fixed
-    step order per wave: bit-identical outputs run to run)."""
+    max_seq_len, scores_out (float32 [B, Hq, stride]), deterministic (sets
+    TQ_DECODE_DETERMINISTIC, which changes nothing: every call takes the
+    steps in a fixed order per wave, so outputs are bit-identical run to run)."""
     a = _decode_args(q, ctxs, pools, block_tables, seq_lens, out, workspace, **kw)
     _check(load().tq_decode_attention(ctypes.byref(a), _stream(stream)), "tq_decode_attention")
 

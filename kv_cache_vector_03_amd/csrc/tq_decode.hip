@@ -85,7 +85,6 @@ struct DArgs {
   float* scores;
   int scores_stride;
   int direct;  // every sequence has at most one split: write the normalised output, no partials
-  int det;     // fixed step order per wave (bit-identical outputs run to run)
 };
 
 __device__ __forceinline__ int seq_cached(const DArgs& a, int b) {
@@ -244,7 +243,7 @@ template <int D, int GP, int KB, int VB, bool QJ, bool UN, class Setup>
 __device__ void split_cached_chunk(const DArgs& a, int pr, int h_, int t0_, int t1_, const int32_t* s_blk,
                                    const uint2* s_pair, const u32x4* s_sgn, float* s_p, unsigned char* s_main,
                                    float* s_stat, bf16x8 (&A1)[D / 32][2], bf16x8 (&A3)[D / 32], const f32x4& ucst,
-                                   float* m_out, float* l_out, int b, int* s_claim, Setup&& setup) {
+                                   float* m_out, float* l_out, int b, Setup&& setup) {
   using R = Rec<D, KB, VB, QJ>;
   constexpr int NW = split_waves<D, GP>();
   constexpr int KT = D / 32;
@@ -610,27 +609,22 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h_, int t0_, int 
     }
   };
 
-  // ---- the stream.  Wave w starts with steps w + NW k (k < nslot - 1);
-  // after those, steps are handed out by the per-item LDS counter *s_claim
-  // (NW (nslot - 1) at item start): a wave claims the next unprocessed step
-  // whenever a ring slot frees up, so waves that get more issue cycles take
-  // more steps and the item's waves finish together.  Ring depth R::nslot;
-  // stq[k] is the step held by slot k (-1: none).  Claims are increasing per
-  // wave, and once the counter passes the last step every later claim fails.
-  // In deterministic mode (a.det) every wave claims from its own counter
-  // s_claim[1 + wave] instead, which starts at NW (nslot - 1) + wave and
-  // advances by NW: wave w takes steps w, w + NW, w + 2 NW, ... in order, so
-  // every wave sums the same steps in the same order on every call.
+  // ---- the stream.  Wave w takes steps w, w + NW, w + 2 NW, ... in order,
+  // from a scalar counter: every call sums the same steps in the same order,
+  // so outputs and scores are bit-identical from run to run and between eager
+  // and graph-replayed launches.  (A schedule in which each wave claimed the
+  // next free step from an LDS counter measured no faster on the decode
+  // workload and ~2 % slower on the long and ragged ones: the claim's atomic
+  // and its wait sat on every step's critical path.)  Ring depth R::nslot;
+  // stq[k] is the step held by slot k (-1: none).
   const int nsteps = (t1 - t0 + 31) / 32;
   const bool exact_wait = a.scores == nullptr;  // score stores also count in vmcnt
   bool more = true;
-  int* const ctr = s_claim + (a.det ? 1 + wave : 0);
-  const int ctr_inc = a.det ? NW : 1;
+  int nxt = NW * (R::nslot - 1) + wave;
   auto claim = [&](int) -> int {
     if (!more) return -1;
-    int v = 0;
-    if ((int)opaque_u32((uint32_t)lane) == 0) v = atomicAdd(ctr, ctr_inc);
-    v = __builtin_amdgcn_readfirstlane(v);
+    const int v = nxt;
+    nxt += NW;
     more = v < nsteps;
     return more ? v : -1;
   };
@@ -640,7 +634,7 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h_, int t0_, int 
     stq[k] = wave + NW * k < nsteps ? wave + NW * k : -1;
     if (stq[k] >= 0) issue(stq[k], k);
   }
-  more = stq[R::nslot - 2] >= 0;  // the counter starts at NW (nslot - 1)
+  more = stq[R::nslot - 2] >= 0;
   stq[R::nslot - 1] = -1;
   setup(A1, A3);  // per-item work that needs no cache data runs while the first steps stream in
   // one ring lap per outer iteration, so every slot offset is a constant
@@ -1012,7 +1006,6 @@ __global__ __launch_bounds__((split_waves<D, GP>() * 64)) void decode_split_kern
   __shared__ int s_exp[GP];
   // next unclaimed step of the current item: [0] shared by the waves, [1 + w]
   // wave w's own sequence in deterministic mode
-  __shared__ int s_claim[1 + split_waves<D, GP>()];
   const int tid = threadIdx.x, lane = tid & 63;
 
   // tables: centroid pairs of this preset, +-1 patterns of sign bytes
@@ -1085,9 +1078,6 @@ __global__ __launch_bounds__((split_waves<D, GP>() * 64)) void decode_split_kern
         const int i = tid + r * NW * 64;
         if (i < nstage) s_blk[i] = (i < nblk && blk[r] >= 0 && (int64_t)blk[r] < pblocks) ? blk[r] : -1;
       }
-      // steps wave + NW k, k < nslot - 1, are handed out statically
-      if (tid == 0) s_claim[0] = NW * (R::nslot - 1);
-      if (tid < NW) s_claim[1 + tid] = NW * (R::nslot - 1) + tid;
       // every path through the masked stores above has its loads complete
       // here; otherwise the compiler keeps a load pending on the path that
       // skips a store and answers a later write of that register with a full
@@ -1183,7 +1173,7 @@ __global__ __launch_bounds__((split_waves<D, GP>() * 64)) void decode_split_kern
         ready_bh = bh;
       };
       split_cached_chunk<D, GP, KB, VB, QJ, UN>(a, pr, h, t0, t1, s_blk, s_pair, s_sgn, s_p, s_main, s_stat, A1,
-                                                A3, ucst, s_m, s_l, b, s_claim, setup);
+                                                A3, ucst, s_m, s_l, b, setup);
     } else if (!kDirect) {
       split_recent<D, GP>(a, b, h, seq_recent(a, b), s_p, s_merge, s_m, s_l);
     }
@@ -1489,7 +1479,6 @@ static DArgs make_dargs(const tq_decode_args* args, const DecodePlan& plan) {
   a.out = args->out;
   a.scores = args->scores_out;
   a.scores_stride = args->scores_stride;
-  a.det = (args->flags & TQ_DECODE_DETERMINISTIC) ? 1 : 0;
   return a;
 }
 

@@ -11,8 +11,8 @@ bf16 window's.  The pairs run on a host thread pool with one BLAS thread each.
 
 Workloads:
   * decode: B=32, Hq=32, Hkv=8, d=128, 8192 cached tokens, K3V4, a
-    16384-block pool through a permuted block table (QJL and MSE-only keys,
-    and the deterministic schedule); the same shape with 8-bit MSE-only keys
+    16384-block pool through a permuted block table (QJL and MSE-only
+    keys); the same shape with 8-bit MSE-only keys
     (K8V4) and with a 4-bit equally spaced key codebook (K4V4, the
     arithmetic score path);
   * long: B=8, Hq=16, Hkv=4, d=256, 131072 cached tokens, K4V4, a
@@ -103,12 +103,10 @@ def _check_all_pairs(label, pools_host, lays, prms, bt_np, cached, q, G, out, sc
     assert not bad, f"{len(bad)} pairs out of tolerance, first {bad[:4]}"
 
 
-@pytest.mark.parametrize("mse_only,deterministic,kb", [(False, False, 3), (True, False, 3), (False, True, 3),
-                                                       (True, False, 8)])
-def test_decode_workload_full_size_all_pairs(mse_only, deterministic, kb):
+@pytest.mark.parametrize("mse_only,kb", [(False, 3), (True, 3), (True, 8)])
+def test_decode_workload_full_size_all_pairs(mse_only, kb):
     """The benchmark's decode workload, with QJL keys and with MSE-only keys
-    (the benchmark's mse_only section), on the deterministic schedule, and
-    with 8-bit MSE-only keys (K8V4)."""
+    (the benchmark's mse_only section), and with 8-bit MSE-only keys (K8V4)."""
     d, B, Hq, Hkv, L, vb, nb, seed = 128, 32, 32, 8, 8192, 4, 16384, 3
     G = Hq // Hkv
     prm = oracle_params(seed, d, kb)
@@ -121,9 +119,8 @@ def test_decode_workload_full_size_all_pairs(mse_only, deterministic, kb):
     _fill(ctx, pool, bt, lens, Hkv, d, seed, 0.0, 20.0)
     q = synth.bf16_round(synth.queries(seed, B, Hq, d))
     qd = torch.from_numpy(q).to(torch.bfloat16).cuda()
-    out, scores = _decode(qd, [ctx], [pool], bt, torch.from_numpy(lens.astype(np.int32)).cuda(), L,
-                          deterministic=deterministic)
-    label = f"decode b32 ctx8192 k{kb}v4{' mse-only' if mse_only else ''}{' deterministic' if deterministic else ''}"
+    out, scores = _decode(qd, [ctx], [pool], bt, torch.from_numpy(lens.astype(np.int32)).cuda(), L)
+    label = f"decode b32 ctx8192 k{kb}v4{' mse-only' if mse_only else ''}"
     _check_all_pairs(label, [pool.cpu().numpy()], [paged.layout(d, kb, vb, qjl=not mse_only)], [prm], bt_np, lens,
                      q, G, out, scores)
     ctx.close()
