@@ -49,13 +49,6 @@
 namespace tq {
 
 constexpr int kMaxG = 8;
-// Waves per split workgroup.  d = 128 with up to 4 query heads per KV head
-// fits two waves per SIMD (<= 256 VGPRs), so one 8-wave workgroup fills a CU
-// and its waves share one item; the wider variants run one wave per SIMD.
-template <int D, int GP>
-constexpr int split_waves() {
-  return (D == 128 && GP == 4) ? 8 : 4;
-}
 
 struct DArgs {
   const void* q;
@@ -131,8 +124,35 @@ struct Rec {
   static constexpr int vmeta = vcodes + (VB * D / 8) * 16;
   static constexpr int bytes = vmeta + (D / 32) * 64;
   static constexpr int slot = 2 * bytes;              // LDS bytes of one ring slot (one step)
-  static constexpr int nslot = D == 128 && KB <= 4 ? 3 : 2;  // ring depth (steps in flight + 1)
+  // records small enough for eight query heads per KV head to run 8-wave
+  // workgroups (see split_waves)
+  static constexpr bool kWide = D == 128 && bytes <= 2400;
 };
+
+// Waves per split workgroup.  d = 128 with up to 4 query heads per KV head
+// fits two waves per SIMD (<= 256 VGPRs), so one 8-wave workgroup fills a CU
+// and its waves share one item.  With eight query heads the value
+// accumulators double; for records of at most 2400 bytes (2- and 3-bit keys,
+// 4-bit keys with 2-bit values or without the sketch) the score A operands
+// then move to LDS (lds_a) and the ring to two steps, which brings the
+// kernel under 256 VGPRs and to 8-wave workgroups as well (the decode
+// workload's shape at 64 query heads: 128 -> 102 us).  The other variants run
+// one wave per SIMD.
+template <int D, int GP, int KB, int VB, bool QJ>
+constexpr int split_waves() {
+  return (D == 128 && GP == 4) ? 8 : (D == 128 && GP == 8 && Rec<D, KB, VB, QJ>::kWide) ? 8 : 4;
+}
+// ring depth (steps in flight + 1) of each wave
+template <int D, int GP, int KB, int VB, bool QJ>
+constexpr int ring_depth() {
+  return (D == 128 && GP == 8 && Rec<D, KB, VB, QJ>::kWide) ? 2 : (D == 128 && KB <= 4 ? 3 : 2);
+}
+// the item's score A operands live in LDS (one copy the waves share) instead
+// of registers
+template <int D, int GP, int KB, int VB, bool QJ>
+constexpr bool lds_a() {
+  return GP == 8 && split_waves<D, GP, KB, VB, QJ>() == 8;
+}
 
 template <int D, int GP, int KB, int VB, bool QJ>
 struct SplitLds {
@@ -140,14 +160,15 @@ struct SplitLds {
   // per-wave softmax weights [GP][32]; with GP = 4 the idle lanes 32-63 store
   // theirs to a second, never-read copy so that the store needs no lane mask
   static constexpr int kPWave = GP * 32 * (GP == 4 ? 2 : 1);
-  static constexpr int NW = split_waves<D, GP>();
+  static constexpr int NW = split_waves<D, GP, KB, VB, QJ>();
   static constexpr int kPBytes = NW * kPWave * 4;
   static constexpr int kStatBytes = NW * GP * 2 * 4;
   static constexpr int kBlkBytes = (kMaxChunk / 16 + 16) * 4;
-  static constexpr int kRingBytes = NW * Rec<D, KB, VB, QJ>::nslot * Rec<D, KB, VB, QJ>::slot;
+  static constexpr int kRingBytes = NW * ring_depth<D, GP, KB, VB, QJ>() * Rec<D, KB, VB, QJ>::slot;
   static constexpr int kMergeBytes = NW * GP * D * 4;  // overlays the ring after the stream
   static constexpr int kMainBytes = kRingBytes > kMergeBytes ? kRingBytes : kMergeBytes;
-  static constexpr int kMainOffset = kPBytes + kStatBytes + kBlkBytes;
+  static constexpr int kABytes = lds_a<D, GP, KB, VB, QJ>() ? (D / 32) * 3 * 64 * 16 : 0;  // score A operands
+  static constexpr int kMainOffset = kPBytes + kStatBytes + kBlkBytes + kABytes;
   static_assert(kMainOffset % 16 == 0, "ring alignment");
   static constexpr int total = kMainOffset + kMainBytes;
   // with the static tables (< 16 KB) the workgroup must fit a CU's 160 KB
@@ -242,10 +263,12 @@ __device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0
 template <int D, int GP, int KB, int VB, bool QJ, bool UN, class Setup>
 __device__ void split_cached_chunk(const DArgs& a, int pr, int h_, int t0_, int t1_, const int32_t* s_blk,
                                    const uint2* s_pair, const u32x4* s_sgn, float* s_p, unsigned char* s_main,
-                                   float* s_stat, bf16x8 (&A1)[D / 32][2], bf16x8 (&A3)[D / 32], const f32x4& ucst,
+                                   float* s_stat, bf16x8 (&A1)[D / 32][2], bf16x8 (&A3)[D / 32], const u32x4* s_A,
+                                   const f32x4& ucst,
                                    float* m_out, float* l_out, int b, Setup&& setup) {
   using R = Rec<D, KB, VB, QJ>;
-  constexpr int NW = split_waves<D, GP>();
+  constexpr int NS = ring_depth<D, GP, KB, VB, QJ>();
+  constexpr int NW = split_waves<D, GP, KB, VB, QJ>();
   constexpr int KT = D / 32;
   constexpr int CS = D / 128;      // value column sets
   constexpr int RT = GP / 4;       // value row tiles per column set
@@ -255,7 +278,7 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h_, int t0_, int 
   constexpr int PPR = R::bytes / 16;          // 16-byte pieces per record
   constexpr int DPR = (PPR + 63) / 64;        // DMA instructions per record
   constexpr int DPS = 2 * DPR;                // DMA instructions per step
-  static_assert((R::nslot - 1) * DPS < 64, "vmcnt range");
+  static_assert((NS - 1) * DPS < 64, "vmcnt range");
   static_assert(PPR >= 64, "a record spans at least one full DMA window");
   // the wave index, KV head and token range are wave-uniform: saying so keeps
   // the step schedule below (ring slots, claims, waits) and the record
@@ -271,7 +294,7 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h_, int t0_, int 
   const uint64_t head_base = reinterpret_cast<uint64_t>(a.pool[pr]) + (uint64_t)h * (uint64_t)rec;
   const uint32_t blk_stride = (uint32_t)(a.Hkv * rec);
   float* sp = s_p + wave * SplitLds<D, GP, KB, VB, QJ>::kPWave;
-  unsigned char* ring = s_main + wave * R::nslot * R::slot;
+  unsigned char* ring = s_main + wave * NS * R::slot;
   const uint32_t ring_lds = lds_offset(ring);
 
   // per-lane byte offsets inside a record
@@ -362,29 +385,44 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h_, int t0_, int 
     // (column = token); rows 0..GP-1 carry the hi parts of the heads, rows
     // GP..2GP-1 the lo parts.
     float v[2][4];
+    // k-slice outer, record inner: only one slice's A operands are live
+    f32x4 am[2], aq[2];
+    uint32_t cw[2][QW + 1], kj[2][D / 128], km[2];
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const unsigned char* hb = sb + half * R::bytes;
       // equally spaced codebook: the accumulator starts at the rows' offset
       // constant (see the arithmetic operands below)
-      f32x4 am = UN ? ucst : f32x4{0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
-      uint32_t cw[QW + 1];
+      am[half] = UN ? ucst : f32x4{0.f, 0.f, 0.f, 0.f};
+      aq[half] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < QW; ++i) cw[i] = *reinterpret_cast<const uint32_t*>(hb + off_kc + 4 * i);
-      cw[QW] = 0;
-      uint32_t kj[D / 128];
+      for (int i = 0; i < QW; ++i) cw[half][i] = *reinterpret_cast<const uint32_t*>(hb + off_kc + 4 * i);
+      cw[half][QW] = 0;
       if constexpr (QJ) {
 #pragma unroll
-        for (int i = 0; i < D / 128; ++i) kj[i] = *reinterpret_cast<const uint32_t*>(hb + off_kj + 4 * i);
+        for (int i = 0; i < D / 128; ++i) kj[half][i] = *reinterpret_cast<const uint32_t*>(hb + off_kj + 4 * i);
       }
-      const uint32_t km = QJ ? *reinterpret_cast<const uint32_t*>(hb + off_km)
-                             : (uint32_t)*reinterpret_cast<const uint16_t*>(hb + off_km);
+      km[half] = QJ ? *reinterpret_cast<const uint32_t*>(hb + off_km)
+                    : (uint32_t)*reinterpret_cast<const uint16_t*>(hb + off_km);
+    }
 #pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
+    for (int kt = 0; kt < KT; ++kt) {
+      bf16x8 a1[2], a3;
+      if constexpr (lds_a<D, GP, KB, VB, QJ>()) {
+        a1[0] = __builtin_bit_cast(bf16x8, s_A[(3 * kt) * 64 + lane]);
+        a1[1] = __builtin_bit_cast(bf16x8, s_A[(3 * kt + 1) * 64 + lane]);
+        if constexpr (QJ) a3 = __builtin_bit_cast(bf16x8, s_A[(3 * kt + 2) * 64 + lane]);
+      } else {
+        a1[0] = A1[kt][0];
+        a1[1] = A1[kt][1];
+        a3 = A3[kt];
+      }
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
         constexpr int TB = 8 * KB;
         const int bp = kt * TB;
-        const uint32_t win =
-            bp % 32 == 0 ? cw[bp / 32] : __builtin_amdgcn_alignbit(cw[bp / 32 + 1], cw[bp / 32], bp % 32);
+        const uint32_t win = bp % 32 == 0 ? cw[half][bp / 32]
+                                          : __builtin_amdgcn_alignbit(cw[half][bp / 32 + 1], cw[half][bp / 32], bp % 32);
         if constexpr (KB == 8) {
           // 8-bit codes: one lookup per code in the one-code table (bf16 hi
           // | lo << 16 of c[idx]), so MFMA m takes coordinates 4m .. 4m+3 as
@@ -392,9 +430,9 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h_, int t0_, int 
           const uint32_t* s_one = reinterpret_cast<const uint32_t*>(s_pair);
 #pragma unroll
           for (int m = 0; m < 2; ++m) {
-            const uint32_t cb = cw[2 * kt + m];
+            const uint32_t cb = cw[half][2 * kt + m];
             const u32x4 b = {s_one[cb & 0xFFu], s_one[(cb >> 8) & 0xFFu], s_one[(cb >> 16) & 0xFFu], s_one[cb >> 24]};
-            am = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1[kt][m], __builtin_bit_cast(bf16x8, b), am, 0, 0, 0);
+            am[half] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[m], __builtin_bit_cast(bf16x8, b), am[half], 0, 0, 0);
           }
         } else if constexpr (UN) {
           // c[idx] = c0 + step idx needs no table: B element = bf16 of
@@ -408,7 +446,7 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h_, int t0_, int 
           u32x4 bu;
 #pragma unroll
           for (int j = 0; j < 4; ++j) bu[j] = and_or(y >> (KB * j), m2, k4300);
-          am = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1[kt][0], __builtin_bit_cast(bf16x8, bu), am, 0, 0, 0);
+          am[half] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[0], __builtin_bit_cast(bf16x8, bu), am[half], 0, 0, 0);
         } else {
           // pair entries {hi, lo}: MFMA m takes pairs 2m, 2m+1 (coordinates 4m .. 4m+3)
           uint2 pe[4];
@@ -416,25 +454,28 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h_, int t0_, int 
           for (int pi = 0; pi < 4; ++pi) pe[pi] = s_pair[(win >> (2 * KB * pi)) & ((1u << (2 * KB)) - 1u)];
           const u32x4 b0 = {pe[0].x, pe[0].y, pe[1].x, pe[1].y};
           const u32x4 b1 = {pe[2].x, pe[2].y, pe[3].x, pe[3].y};
-          am = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1[kt][0], __builtin_bit_cast(bf16x8, b0), am, 0, 0, 0);
-          am = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1[kt][1], __builtin_bit_cast(bf16x8, b1), am, 0, 0, 0);
+          am[half] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[0], __builtin_bit_cast(bf16x8, b0), am[half], 0, 0, 0);
+          am[half] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[1], __builtin_bit_cast(bf16x8, b1), am[half], 0, 0, 0);
         }
         if constexpr (QJ) {
-          const u32x4 bq = s_sgn[(kj[kt / 4] >> (8 * (kt % 4))) & 0xFFu];
-          aq = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A3[kt], __builtin_bit_cast(bf16x8, bq), aq, 0, 0, 0);
+          const u32x4 bq = s_sgn[(kj[half][kt / 4] >> (8 * (kt % 4))) & 0xFFu];
+          aq[half] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a3, __builtin_bit_cast(bf16x8, bq), aq[half], 0, 0, 0);
         }
       }
-      // logit = log2(e) sm_scale n (q~.c + kappa gamma p.sign), with
-      // log2(e) sm_scale folded into q~ and kappa log2(e) sm_scale into p (the
-      // A operands)
-      const float n = f16_bits_to_f32((uint16_t)(km & 0xFFFFu));
-      if constexpr (QJ) {
-        const float nk = n * f16_bits_to_f32((uint16_t)(km >> 16));
+    }
+    // logit = log2(e) sm_scale n (q~.c + kappa gamma p.sign), with
+    // log2(e) sm_scale folded into q~ and kappa log2(e) sm_scale into p (the
+    // A operands)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[half][r] = __builtin_fmaf(nk, aq[r], n * am[r]);
+    for (int half = 0; half < 2; ++half) {
+      const float n = f16_bits_to_f32((uint16_t)(km[half] & 0xFFFFu));
+      if constexpr (QJ) {
+        const float nk = n * f16_bits_to_f32((uint16_t)(km[half] >> 16));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[half][r] = __builtin_fmaf(nk, aq[half][r], n * am[half][r]);
       } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[half][r] = n * am[r];
+        for (int r = 0; r < 4; ++r) v[half][r] = n * am[half][r];
       }
     }
     // x[r]: hi + lo of head row r, one swap per row.  GP = 4: the hi and lo
@@ -615,12 +656,12 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h_, int t0_, int 
   // and graph-replayed launches.  (A schedule in which each wave claimed the
   // next free step from an LDS counter measured no faster on the decode
   // workload and ~2 % slower on the long and ragged ones: the claim's atomic
-  // and its wait sat on every step's critical path.)  Ring depth R::nslot;
+  // and its wait sat on every step's critical path.)  Ring depth NS;
   // stq[k] is the step held by slot k (-1: none).
   const int nsteps = (t1 - t0 + 31) / 32;
   const bool exact_wait = a.scores == nullptr;  // score stores also count in vmcnt
   bool more = true;
-  int nxt = NW * (R::nslot - 1) + wave;
+  int nxt = NW * (NS - 1) + wave;
   auto claim = [&](int) -> int {
     if (!more) return -1;
     const int v = nxt;
@@ -628,19 +669,19 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h_, int t0_, int 
     more = v < nsteps;
     return more ? v : -1;
   };
-  int stq[R::nslot];
+  int stq[NS];
 #pragma unroll
-  for (int k = 0; k < R::nslot - 1; ++k) {  // the first steps of each wave are fixed: wave + NW k
+  for (int k = 0; k < NS - 1; ++k) {  // the first steps of each wave are fixed: wave + NW k
     stq[k] = wave + NW * k < nsteps ? wave + NW * k : -1;
     if (stq[k] >= 0) issue(stq[k], k);
   }
-  more = stq[R::nslot - 2] >= 0;
-  stq[R::nslot - 1] = -1;
+  more = stq[NS - 2] >= 0;
+  stq[NS - 1] = -1;
   setup(A1, A3);  // per-item work that needs no cache data runs while the first steps stream in
   // one ring lap per outer iteration, so every slot offset is a constant
   auto stream_step = [&](auto slot_c) -> bool {
     constexpr int SL = decltype(slot_c)::value;
-    constexpr int FREE = (SL + R::nslot - 1) % R::nslot;  // the slot of the step computed last
+    constexpr int FREE = (SL + NS - 1) % NS;  // the slot of the step computed last
     if (stq[SL] < 0) return false;
     stq[FREE] = claim(stq[SL]);
     if (stq[FREE] >= 0) {
@@ -649,20 +690,20 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h_, int t0_, int 
     }
     int ahead = 0;  // steps issued after this one (the slots after SL in ring order)
 #pragma unroll
-    for (int k = 1; k < R::nslot; ++k) ahead += stq[(SL + k) % R::nslot] >= 0 ? 1 : 0;
+    for (int k = 1; k < NS; ++k) ahead += stq[(SL + k) % NS] >= 0 ? 1 : 0;
     if (!exact_wait || ahead == 0)
       wait_vmcnt<0>();
     else if (ahead == 1)
       wait_vmcnt<DPS>();
     else
-      wait_vmcnt<(R::nslot - 1) * DPS>();
+      wait_vmcnt<(NS - 1) * DPS>();
     compute(ring + SL * R::slot, stq[SL]);
     return true;
   };
   for (;;) {
     if (!stream_step(std::integral_constant<int, 0>{})) break;
     if (!stream_step(std::integral_constant<int, 1>{})) break;
-    if constexpr (R::nslot == 3)
+    if constexpr (NS == 3)
       if (!stream_step(std::integral_constant<int, 2>{})) break;
   }
   wait_vmcnt<0>();
@@ -763,10 +804,9 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h_, int t0_, int 
 // channels each, so every row is one coalesced read, and the dot products
 // are wave reductions.  The softmax runs per head over the window; the
 // waves' partial value sums are added in LDS in wave order (deterministic).
-template <int D, int GP>
+template <int D, int GP, int NW>
 __device__ void split_recent(const DArgs& a, int b, int h, int R, float* s_p, float* s_merge, float* m_out,
                              float* l_out) {
-  constexpr int NW = split_waves<D, GP>();
   constexpr int P = D / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint16_t* kb = a.rk + (((int64_t)b * a.Hkv + h) * a.W) * D;
@@ -872,12 +912,12 @@ __device__ void split_recent(const DArgs& a, int b, int h, int R, float* s_p, fl
 // index bits, shuffles for the others), then p = S q~ on the matrix cores into
 // s_pq: A rows = heads (fp16 hi/lo of q~ 2^-e_g, with 2^e_g above the head's
 // largest |q~_j| so fp16 cannot overflow), B = the 16 S tiles of the context,
-// three products per tile; wave w takes column tiles w, w + 4, ...
+// three products per tile; wave w takes column tiles w, w + NW, ...
 template <int D, int NW, bool QJ>
 __device__ __forceinline__ void rotate_project(const DArgs& a, const DevTables& dv, int b, int h, float* s_q, float* s_pq,
                                int* s_exp) {
   constexpr int P = D / 64;
-  constexpr int KT = D / 32, NT = D / 16, NTW = NT / NW;
+  constexpr int KT = D / 32, NT = D / 16, NTW = (NT + NW - 1) / NW;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int G = a.G;
   const int64_t q0 = ((int64_t)b * a.Hq + (int64_t)h * G) * D;
@@ -887,7 +927,8 @@ __device__ __forceinline__ void rotate_project(const DArgs& a, const DevTables& 
   for (int i = 0; i < (QJ ? NTW : 0); ++i) {
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
-      const size_t tb = ((((size_t)(wave + NW * i)) * KT + kt) * 2) * 64 * 8;
+      const int ntc = wave + NW * i < NT ? wave + NW * i : 0;  // waves past the last tile read tile 0, unused
+      const size_t tb = ((((size_t)ntc) * KT + kt) * 2) * 64 * 8;
       bhi[i][kt] = *reinterpret_cast<const f16x8*>(dv.s_tiles + tb + lane * 8);
       blo[i][kt] = *reinterpret_cast<const f16x8*>(dv.s_tiles + tb + 512 + lane * 8);
     }
@@ -962,6 +1003,7 @@ __device__ __forceinline__ void rotate_project(const DArgs& a, const DevTables& 
 #pragma unroll
   for (int i = 0; i < NTW; ++i) {
     const int nt = wave + NW * i;
+    if (nt >= NT) break;  // uniform
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
@@ -988,8 +1030,8 @@ __device__ __forceinline__ void rotate_project(const DArgs& a, const DevTables& 
 // UN: the preset's codebook is equally spaced (c_k = c0 + k step) and the
 // score takes c[idx] arithmetically instead of from the pair table.
 template <int D, int GP, int KB, int VB, bool QJ, bool UN>
-__global__ __launch_bounds__((split_waves<D, GP>() * 64)) void decode_split_kernel(DArgs a, int pr) {
-  constexpr int NW = split_waves<D, GP>();
+__global__ __launch_bounds__((split_waves<D, GP, KB, VB, QJ>() * 64)) void decode_split_kernel(DArgs a, int pr) {
+  constexpr int NW = split_waves<D, GP, KB, VB, QJ>();
   constexpr int KT = D / 32;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   using SL = SplitLds<D, GP, KB, VB, QJ>;
@@ -998,14 +1040,13 @@ __global__ __launch_bounds__((split_waves<D, GP>() * 64)) void decode_split_kern
   int32_t* s_blk = reinterpret_cast<int32_t*>(s_stat + NW * GP * 2);
   unsigned char* s_main = lds + SL::kMainOffset;
   float* s_merge = reinterpret_cast<float*>(s_main);
+  u32x4* s_A = reinterpret_cast<u32x4*>(lds + SL::kPBytes + SL::kStatBytes + SL::kBlkBytes);
   __shared__ uint2 s_pair[256];  // centroid pair -> {bf16 hi parts, bf16 lo parts}
   __shared__ u32x4 s_sgn[QJ ? 256 : 1];  // sign byte -> 8 bf16 of +-1 (bit i -> element i)
   __shared__ float s_m[kMaxG], s_l[kMaxG];
   __shared__ __attribute__((aligned(16))) float s_q[GP * D];
   __shared__ __attribute__((aligned(16))) float s_pq[GP * D];
   __shared__ int s_exp[GP];
-  // next unclaimed step of the current item: [0] shared by the waves, [1 + w]
-  // wave w's own sequence in deterministic mode
   const int tid = threadIdx.x, lane = tid & 63;
 
   // tables: centroid pairs of this preset, +-1 patterns of sign bytes
@@ -1170,12 +1211,21 @@ __global__ __launch_bounds__((split_waves<D, GP>() * 64)) void decode_split_kern
 #pragma unroll
           for (int r = 0; r < 4; ++r) ucst[r] = off * __shfl(usum, 4 * kq + r);
         }
+        // with lds_a, every wave stores the same operands to the shared copy
+        // the steps read (no wave of the previous item reads it any more: the
+        // item start is past the merge barrier)
+#pragma unroll
+        for (int kt = 0; kt < (lds_a<D, GP, KB, VB, QJ>() ? KT : 0); ++kt) {
+          s_A[(3 * kt) * 64 + lane] = __builtin_bit_cast(u32x4, A1r[kt][0]);
+          if constexpr (!UN) s_A[(3 * kt + 1) * 64 + lane] = __builtin_bit_cast(u32x4, A1r[kt][1]);
+          if constexpr (QJ) s_A[(3 * kt + 2) * 64 + lane] = __builtin_bit_cast(u32x4, A3r[kt]);
+        }
         ready_bh = bh;
       };
       split_cached_chunk<D, GP, KB, VB, QJ, UN>(a, pr, h, t0, t1, s_blk, s_pair, s_sgn, s_p, s_main, s_stat, A1,
-                                                A3, ucst, s_m, s_l, b, setup);
+                                                A3, s_A, ucst, s_m, s_l, b, setup);
     } else if (!kDirect) {
-      split_recent<D, GP>(a, b, h, seq_recent(a, b), s_p, s_merge, s_m, s_l);
+      split_recent<D, GP, NW>(a, b, h, seq_recent(a, b), s_p, s_merge, s_m, s_l);
     }
     if (kDirect) {
       // the only split of this (sequence, KV head): acc / l is the output
