@@ -281,7 +281,7 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h_, int t0_, int 
   static_assert((NS - 1) * DPS < 64, "vmcnt range");
   static_assert(PPR >= 64, "a record spans at least one full DMA window");
   // the wave index, KV head and token range are wave-uniform: saying so keeps
-  // the step schedule below (ring slots, claims, waits) and the record
+  // the step schedule below (ring slots, step indices, waits) and the record
   // addresses in scalar registers and scalar branches
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = __builtin_amdgcn_readfirstlane(h_);
@@ -662,7 +662,7 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h_, int t0_, int 
   const bool exact_wait = a.scores == nullptr;  // score stores also count in vmcnt
   bool more = true;
   int nxt = NW * (NS - 1) + wave;
-  auto claim = [&](int) -> int {
+  auto next_step = [&](int) -> int {
     if (!more) return -1;
     const int v = nxt;
     nxt += NW;
@@ -683,7 +683,7 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h_, int t0_, int 
     constexpr int SL = decltype(slot_c)::value;
     constexpr int FREE = (SL + NS - 1) % NS;  // the slot of the step computed last
     if (stq[SL] < 0) return false;
-    stq[FREE] = claim(stq[SL]);
+    stq[FREE] = next_step(stq[SL]);
     if (stq[FREE] >= 0) {
       wait_lgkm0();  // ring slot reuse: the reads of the step that used it are complete
       issue(stq[FREE], FREE);

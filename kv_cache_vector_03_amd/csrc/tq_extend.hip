@@ -121,6 +121,36 @@ __device__ __forceinline__ uint2 split2_f16(float x, float y) {
   const auto l = __builtin_amdgcn_cvt_pkrtz(x - (float)h[0], y - (float)h[1]);
   return make_uint2(__builtin_bit_cast(uint32_t, h), __builtin_bit_cast(uint32_t, l));
 }
+// acc[ct][r] *= a for the eight column tiles of one output row, skipped when
+// go == 0, as one block whose branch the compiler does not see: the
+// accumulators stay in their registers on both paths.  Written as a C++
+// branch, the compiler renames them inside it and copies all 32 of them on
+// the (common) path that skips it, every step (prefill workload 1400 -> 1370
+// us without those copies).  The accumulators were last written by the value
+// products of the previous step, a barrier and the whole score phase earlier.
+template <int CT>
+__device__ __forceinline__ void rescale_row(f32x4 (&acc)[CT], int r, float a, uint32_t go) {
+  static_assert(CT == 8, "eight column tiles");
+  float e0 = acc[0][r], e1 = acc[1][r], e2 = acc[2][r], e3 = acc[3][r];
+  float e4 = acc[4][r], e5 = acc[5][r], e6 = acc[6][r], e7 = acc[7][r];
+  asm volatile(
+      "s_cmp_eq_u32 %9, 0\n\t"
+      "s_cbranch_scc1 .Lrs_skip%=\n\t"
+      "v_mul_f32 %0, %0, %8\n\t"
+      "v_mul_f32 %1, %1, %8\n\t"
+      "v_mul_f32 %2, %2, %8\n\t"
+      "v_mul_f32 %3, %3, %8\n\t"
+      "v_mul_f32 %4, %4, %8\n\t"
+      "v_mul_f32 %5, %5, %8\n\t"
+      "v_mul_f32 %6, %6, %8\n\t"
+      "v_mul_f32 %7, %7, %8\n"
+      ".Lrs_skip%=:"
+      : "+v"(e0), "+v"(e1), "+v"(e2), "+v"(e3), "+v"(e4), "+v"(e5), "+v"(e6), "+v"(e7)
+      : "v"(a), "s"(go)
+      : "scc");
+  acc[0][r] = e0; acc[1][r] = e1; acc[2][r] = e2; acc[3][r] = e3;
+  acc[4][r] = e4; acc[5][r] = e5; acc[6][r] = e6; acc[7][r] = e7;
+}
 __device__ __forceinline__ float row16_max(float x) {
   x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false)));
   x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false)));
@@ -155,18 +185,21 @@ __device__ __forceinline__ void softmax_stage(ERowState& st, float (&x)[2][4], f
   for (int c = 0; c < 2; ++c)
 #pragma unroll
     for (int r = 0; r < 4; ++r) over |= x[c][r] > st.m[r] + kELazy;
-  if (__builtin_amdgcn_ballot_w64(over) != 0) {  // uniform: some row's max passed its reference
+  float alpha[4] = {1.f, 1.f, 1.f, 1.f};
+  const bool grow = __builtin_amdgcn_ballot_w64(over) != 0;
+  if (grow) {  // uniform: some row's max passed its reference
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float bm = row16_max(fmaxf(x[0][r], x[1][r]));
       const float mn = fmaxf(st.m[r], bm);
-      const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(st.m[r] - mn);
+      alpha[r] = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(st.m[r] - mn);
       st.m[r] = mn;
-      st.l[r] *= alpha;
-#pragma unroll
-      for (int ct = 0; ct < 8; ++ct) st.acc[ct][r] *= alpha;
+      st.l[r] *= alpha[r];
     }
   }
+  const uint32_t go = __builtin_amdgcn_readfirstlane(grow ? 1u : 0u);  // uniform: an SGPR operand
+#pragma unroll
+  for (int r = 0; r < 4; ++r) rescale_row<8>(st.acc, r, alpha[r], go);
   const int col = lane & 15, rg = lane >> 4;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -410,7 +443,7 @@ __global__ __launch_bounds__(ENW * 64) void extend_kernel(EArgs a) {
   // Measured on the prefill workload: 2017 us with four-wave workgroups and
   // two barriers per step, 1625 us with eight waves, 1481 us pipelined,
   // 1433 us with the build placed between the products, 1402 us with the
-  // two-value fp16 splits.
+  // two-value fp16 splits, 1370 us with the copy-free rescale.
   const int nsteps = (P + 31) / 32;
   const int32_t* btrow = a.bt + (int64_t)b * a.max_blocks;
   // 16-byte pieces of a step's two records: thread t copies pieces t, t + ENW * 64, ..
