@@ -207,3 +207,64 @@ def test_random_extend_configuration(i):
         worst = max(worst, output_errors(out[rows].astype(np.float64).reshape(-1, d), ref.reshape(-1, d)))
     print(f"[random extend {i}] max out err {worst:.2e}", flush=True)
     assert np.all(np.isfinite(out)) and worst <= TOL
+
+
+def test_gqa8_many_items_per_workgroup():
+    """Eight query heads per KV head with many split items per workgroup (so
+    the score operands kept in LDS by the 2-3-bit kernels are reused and
+    rebuilt across consecutive items), two presets (K3V4: operands in LDS;
+    K4V4 with the sketch: operands in registers), ragged lengths, 64-token
+    splits and a bf16 recent window."""
+    d, B, Hq, Hkv, W, chunk, seed = 128, 16, 64, 8, 32, 64, 9900
+    kinds = [(3, 4), (4, 4)]
+    lens = synth.ragged_lengths(seed, B, lo=100, hi=3000, median=1200.0)
+    lens[3] = 0
+    print(f"[gqa8 many items] lens={lens.tolist()} chunk={chunk} W={W}", flush=True)
+    seq_preset = (np.arange(B) % 2).astype(np.int8)
+    mb = int(np.ceil(lens.max() / 16))
+    nb = B * mb + 2
+    bt = synth.block_table(seed, B, mb, nb)
+    prms, ctxs, pools, fields = [], [], [], {}
+    for p, (kb, vb) in enumerate(kinds):
+        prm = oracle_params(seed + 7 * p, d, kb)
+        pool = paged.new_pool(nb, Hkv, paged.layout(d, kb, vb))
+        seqs = [b for b in range(B) if seq_preset[b] == p]
+        fields.update(oracle_cache(prm, d, kb, vb, lens, Hkv, bt, pool, seed, p=0.005, seqs=seqs))
+        prms.append(prm)
+        pools.append(pool)
+        ctxs.append(tq.tq_codebook_init(d, kb, vb, signs=prm["signs"], S=prm["S"]))
+    rng = np.random.default_rng([seed, 1])
+    rlens = rng.integers(0, W + 1, B)
+    rk32 = synth.bf16_round(rng.standard_normal((B, Hkv, W, d)).astype(np.float32))
+    rv32 = synth.bf16_round(rng.standard_normal((B, Hkv, W, d)).astype(np.float32))
+    kw = dict(seq_preset=torch.from_numpy(seq_preset).cuda(),
+              recent_k=torch.from_numpy(synth.bf16_bits(rk32).view(np.int16)).cuda().view(torch.bfloat16),
+              recent_v=torch.from_numpy(synth.bf16_bits(rv32).view(np.int16)).cuda().view(torch.bfloat16),
+              recent_lens=torch.from_numpy(rlens.astype(np.int32)).cuda())
+    q = synth.bf16_round(synth.queries(seed, B, Hq, d))
+    qd = torch.from_numpy(q).to(torch.bfloat16).cuda()
+    pd = [torch.from_numpy(p).cuda() for p in pools]
+    btd = torch.from_numpy(bt.astype(np.int32)).cuda()
+    ld = torch.from_numpy(lens.astype(np.int32)).cuda()
+    msl = mb * 16
+    out = torch.full((B, Hq, d), float("nan"), dtype=torch.float32, device="cuda")
+    sc = torch.full((B, Hq, msl + W), float("nan"), dtype=torch.float32, device="cuda")
+    nbytes = tq.tq_decode_workspace_bytes(qd, ctxs, pd, btd, ld, out, chunk_tokens=chunk, max_seq_len=msl, **kw)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    tq.tq_decode_attention(qd, ctxs, pd, btd, ld, out, ws, chunk_tokens=chunk, max_seq_len=msl, scores_out=sc, **kw)
+    torch.cuda.synchronize()
+    out, sc = out.cpu().numpy(), sc.cpu().numpy()
+    for cx in ctxs:
+        cx.close()
+    ref, serr = [], []
+    for b in range(B):
+        pr, R, L = int(seq_preset[b]), int(rlens[b]), int(lens[b])
+        o, s = attention.decode_one_sequence(q[b].astype(np.float64), fields[b], prms[pr],
+                                             rk32[b, :, :R].astype(np.float64), rv32[b, :, :R].astype(np.float64))
+        ref.append(o)
+        if L + R:
+            got = np.concatenate([sc[b, :, :L], sc[b, :, L:L + R]], axis=1)
+            serr.append(score_errors(got.astype(np.float64), s))
+    oe = output_errors(out.astype(np.float64), np.stack(ref))
+    print(f"[gqa8 many items] max score err {max(serr):.2e} max out err {oe:.2e}", flush=True)
+    assert np.all(np.isfinite(out)) and max(serr) <= TOL and oe <= TOL
