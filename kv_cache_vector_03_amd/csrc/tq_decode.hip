@@ -136,38 +136,46 @@ struct Rec {
 // 4-bit keys with 2-bit values or without the sketch) the score A operands
 // then move to LDS (lds_a) and the ring to two steps, which brings the
 // kernel under 256 VGPRs and to 8-wave workgroups as well (the decode
-// workload's shape at 64 query heads: 128 -> 102 us).  The other variants run
-// one wave per SIMD.
-template <int D, int GP, int KB, int VB, bool QJ>
+// workload's shape at 64 query heads: 128 -> 102 us).  MSE-only keys of up to
+// 4 bits with the Lloyd-Max codebook and four query heads per KV head carry
+// no sketch registers: with the A operands in LDS and a two-step ring they fit
+// three waves per SIMD (<= 168 VGPRs), so 12-wave workgroups share an item
+// (the MSE-only decode workload: 65 -> 62 us); the equally spaced codebook's
+// variant would spill there and keeps 8.  The other variants run one wave per
+// SIMD.
+template <int D, int GP, int KB, int VB, bool QJ, bool UN>
 constexpr int split_waves() {
-  return (D == 128 && GP == 4) ? 8 : (D == 128 && GP == 8 && Rec<D, KB, VB, QJ>::kWide) ? 8 : 4;
+  return (D == 128 && GP == 4) ? (!QJ && !UN && KB <= 4 && Rec<D, KB, VB, QJ>::kWide ? 12 : 8)
+                               : (D == 128 && GP == 8 && Rec<D, KB, VB, QJ>::kWide) ? 8 : 4;
 }
 // ring depth (steps in flight + 1) of each wave
-template <int D, int GP, int KB, int VB, bool QJ>
+template <int D, int GP, int KB, int VB, bool QJ, bool UN>
 constexpr int ring_depth() {
-  return (D == 128 && GP == 8 && Rec<D, KB, VB, QJ>::kWide) ? 2 : (D == 128 && KB <= 4 ? 3 : 2);
+  return split_waves<D, GP, KB, VB, QJ, UN>() == 12 || (D == 128 && GP == 8 && Rec<D, KB, VB, QJ>::kWide)
+             ? 2
+             : (D == 128 && KB <= 4 ? 3 : 2);
 }
 // the item's score A operands live in LDS (one copy the waves share) instead
 // of registers
-template <int D, int GP, int KB, int VB, bool QJ>
+template <int D, int GP, int KB, int VB, bool QJ, bool UN>
 constexpr bool lds_a() {
-  return GP == 8 && split_waves<D, GP, KB, VB, QJ>() == 8;
+  return split_waves<D, GP, KB, VB, QJ, UN>() == 12 || (GP == 8 && split_waves<D, GP, KB, VB, QJ, UN>() == 8);
 }
 
-template <int D, int GP, int KB, int VB, bool QJ>
+template <int D, int GP, int KB, int VB, bool QJ, bool UN>
 struct SplitLds {
   static_assert(Rec<D, KB, VB, QJ>::bytes % 16 == 0, "record size");
   // per-wave softmax weights [GP][32]; with GP = 4 the idle lanes 32-63 store
   // theirs to a second, never-read copy so that the store needs no lane mask
   static constexpr int kPWave = GP * 32 * (GP == 4 ? 2 : 1);
-  static constexpr int NW = split_waves<D, GP, KB, VB, QJ>();
+  static constexpr int NW = split_waves<D, GP, KB, VB, QJ, UN>();
   static constexpr int kPBytes = NW * kPWave * 4;
   static constexpr int kStatBytes = NW * GP * 2 * 4;
   static constexpr int kBlkBytes = (kMaxChunk / 16 + 16) * 4;
-  static constexpr int kRingBytes = NW * ring_depth<D, GP, KB, VB, QJ>() * Rec<D, KB, VB, QJ>::slot;
+  static constexpr int kRingBytes = NW * ring_depth<D, GP, KB, VB, QJ, UN>() * Rec<D, KB, VB, QJ>::slot;
   static constexpr int kMergeBytes = NW * GP * D * 4;  // overlays the ring after the stream
   static constexpr int kMainBytes = kRingBytes > kMergeBytes ? kRingBytes : kMergeBytes;
-  static constexpr int kABytes = lds_a<D, GP, KB, VB, QJ>() ? (D / 32) * 3 * 64 * 16 : 0;  // score A operands
+  static constexpr int kABytes = lds_a<D, GP, KB, VB, QJ, UN>() ? (D / 32) * 3 * 64 * 16 : 0;  // score A operands
   static constexpr int kMainOffset = kPBytes + kStatBytes + kBlkBytes + kABytes;
   static_assert(kMainOffset % 16 == 0, "ring alignment");
   static constexpr int total = kMainOffset + kMainBytes;
@@ -267,8 +275,8 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h_, int t0_, int 
                                    const f32x4& ucst,
                                    float* m_out, float* l_out, int b, Setup&& setup) {
   using R = Rec<D, KB, VB, QJ>;
-  constexpr int NS = ring_depth<D, GP, KB, VB, QJ>();
-  constexpr int NW = split_waves<D, GP, KB, VB, QJ>();
+  constexpr int NS = ring_depth<D, GP, KB, VB, QJ, UN>();
+  constexpr int NW = split_waves<D, GP, KB, VB, QJ, UN>();
   constexpr int KT = D / 32;
   constexpr int CS = D / 128;      // value column sets
   constexpr int RT = GP / 4;       // value row tiles per column set
@@ -293,7 +301,7 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h_, int t0_, int 
   // 32 x 32 -> 64-bit multiply
   const uint64_t head_base = reinterpret_cast<uint64_t>(a.pool[pr]) + (uint64_t)h * (uint64_t)rec;
   const uint32_t blk_stride = (uint32_t)(a.Hkv * rec);
-  float* sp = s_p + wave * SplitLds<D, GP, KB, VB, QJ>::kPWave;
+  float* sp = s_p + wave * SplitLds<D, GP, KB, VB, QJ, UN>::kPWave;
   unsigned char* ring = s_main + wave * NS * R::slot;
   const uint32_t ring_lds = lds_offset(ring);
 
@@ -408,7 +416,7 @@ __device__ void split_cached_chunk(const DArgs& a, int pr, int h_, int t0_, int 
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
       bf16x8 a1[2], a3;
-      if constexpr (lds_a<D, GP, KB, VB, QJ>()) {
+      if constexpr (lds_a<D, GP, KB, VB, QJ, UN>()) {
         a1[0] = __builtin_bit_cast(bf16x8, s_A[(3 * kt) * 64 + lane]);
         a1[1] = __builtin_bit_cast(bf16x8, s_A[(3 * kt + 1) * 64 + lane]);
         if constexpr (QJ) a3 = __builtin_bit_cast(bf16x8, s_A[(3 * kt + 2) * 64 + lane]);
@@ -1030,11 +1038,11 @@ __device__ __forceinline__ void rotate_project(const DArgs& a, const DevTables& 
 // UN: the preset's codebook is equally spaced (c_k = c0 + k step) and the
 // score takes c[idx] arithmetically instead of from the pair table.
 template <int D, int GP, int KB, int VB, bool QJ, bool UN>
-__global__ __launch_bounds__((split_waves<D, GP, KB, VB, QJ>() * 64)) void decode_split_kernel(DArgs a, int pr) {
-  constexpr int NW = split_waves<D, GP, KB, VB, QJ>();
+__global__ __launch_bounds__((split_waves<D, GP, KB, VB, QJ, UN>() * 64)) void decode_split_kernel(DArgs a, int pr) {
+  constexpr int NW = split_waves<D, GP, KB, VB, QJ, UN>();
   constexpr int KT = D / 32;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-  using SL = SplitLds<D, GP, KB, VB, QJ>;
+  using SL = SplitLds<D, GP, KB, VB, QJ, UN>;
   float* s_p = reinterpret_cast<float*>(lds);
   float* s_stat = s_p + NW * SL::kPWave;
   int32_t* s_blk = reinterpret_cast<int32_t*>(s_stat + NW * GP * 2);
@@ -1215,7 +1223,7 @@ __global__ __launch_bounds__((split_waves<D, GP, KB, VB, QJ>() * 64)) void decod
         // the steps read (no wave of the previous item reads it any more: the
         // item start is past the merge barrier)
 #pragma unroll
-        for (int kt = 0; kt < (lds_a<D, GP, KB, VB, QJ>() ? KT : 0); ++kt) {
+        for (int kt = 0; kt < (lds_a<D, GP, KB, VB, QJ, UN>() ? KT : 0); ++kt) {
           s_A[(3 * kt) * 64 + lane] = __builtin_bit_cast(u32x4, A1r[kt][0]);
           if constexpr (!UN) s_A[(3 * kt + 1) * 64 + lane] = __builtin_bit_cast(u32x4, A1r[kt][1]);
           if constexpr (QJ) s_A[(3 * kt + 2) * 64 + lane] = __builtin_bit_cast(u32x4, A3r[kt]);
@@ -1395,7 +1403,7 @@ struct SplitLaunchCache {
 template <int D, int GP, int KB, int VB, bool QJ, bool UN = false>
 static hipError_t launch_split(const DArgs& a, int pr, hipStream_t s, bool dry_run) {
   auto kern = decode_split_kernel<D, GP, KB, VB, QJ, UN>;
-  using SL = SplitLds<D, GP, KB, VB, QJ>;
+  using SL = SplitLds<D, GP, KB, VB, QJ, UN>;
   static SplitLaunchCache cache;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
