@@ -458,34 +458,22 @@ __global__ __launch_bounds__(kQWaves<D> * 64) void quantize_kernel(QArgs a) {
       const uint16_t s16 = f32_to_f16_bits((mx - mn) / LV);
       const uint16_t z16 = f32_to_f16_bits(mn);
       const float sc = f16_bits_to_f32(s16), zz = f16_bits_to_f32(z16);
-      // q = rint((v - z) / s) with the IEEE quotient.  The product with the
-      // rounded reciprocal lies within 3e-6 of that quotient (|q| <= 16), so
-      // it rounds the same way unless it falls within kVBand of a
-      // half-integer; such lanes redo the group with the division.
-      constexpr float kVBand = 8e-6f;
-      const float rs = 1.0f / sc;
+      // q = rint((v - z) / s) with the IEEE quotient, from the product with
+      // the rounded reciprocal and one correction by the exact residual
+      // (Markstein's theorem: the corrected quotient is the correctly rounded
+      // one; checked for every fp16 scale around every half-integer).  A
+      // constant group (s = 0) codes 0: with rs = 0 every quotient is 0.
+      const float rs = sc != 0.f ? 1.0f / sc : 0.f;
       uint32_t vw[VB];
 #pragma unroll
       for (int i = 0; i < VB; ++i) vw[i] = 0;
-      bool near = false;
 #pragma unroll
       for (int e = 0; e < 32; ++e) {
-        const float t = (x[32 * gl + e] - zz) * rs;
-        const float q0 = __builtin_rintf(t);
-        near |= fabsf(t - q0) >= 0.5f - kVBand;
-        const float q = fminf(fmaxf(q0, 0.f), LV);
-        uint32_t qi = (sc != 0.f) ? (uint32_t)q : 0u;
-        vw[(e * VB) / 32] |= qi << ((e * VB) % 32);
-      }
-      if (near && sc != 0.f) {
-#pragma unroll
-        for (int i = 0; i < VB; ++i) vw[i] = 0;
-#pragma unroll
-        for (int e = 0; e < 32; ++e) {
-          float q = __builtin_rintf((x[32 * gl + e] - zz) / sc);
-          q = fminf(fmaxf(q, 0.f), LV);
-          vw[(e * VB) / 32] |= (uint32_t)q << ((e * VB) % 32);
-        }
+        const float dv = x[32 * gl + e] - zz;
+        const float q0 = dv * rs;
+        const float t = __builtin_fmaf(__builtin_fmaf(-q0, sc, dv), rs, q0);
+        const float q = fminf(fmaxf(__builtin_rintf(t), 0.f), LV);
+        vw[(e * VB) / 32] |= (uint32_t)q << ((e * VB) % 32);
       }
       if (store) {
         const int g = part * GL + gl;

@@ -90,6 +90,17 @@ __device__ __forceinline__ uint32_t opaque_mask(uint32_t x) {
   return x;
 }
 
+// LDS: the QJL tiles (64 KB), the upper centroids (and, for 8-bit codes, the
+// upper thresholds), the row's D2 code patterns
+template <int KB, bool QJ>
+constexpr int m_lds_m2() {
+  return (QJ ? 65536 : 0) + (KB <= 4 ? 64 : 1024);
+}
+template <int KB, bool QJ>
+constexpr int m_lds_bytes() {
+  return m_lds_m2<KB, QJ>() + KB * MD / 8;
+}
+
 template <int KB, int VB, bool QJ>
 __global__ __launch_bounds__(mwaves<QJ>() * 64) void quantize_mfma_kernel(QMArgs a) {
   constexpr int MW = mwaves<QJ>();
@@ -152,35 +163,41 @@ __global__ __launch_bounds__(mwaves<QJ>() * 64) void quantize_mfma_kernel(QMArgs
         for (int w = 0; w < 4; ++w) hv[s0][s1][w] = pos[w] ^ flip;
       }
   }
-  // D2 as code-word xor patterns of this lane's stored code dwords (index
-  // ^ (L - 1) where D2 = -1; the kernel works on D2-free coordinates)
+  // D2 as code-word xor patterns of the row's code stream (index ^ (L - 1)
+  // where D2 = -1; the kernel works on D2-free coordinates), or-ed together in
+  // LDS by one thread per coordinate
   constexpr int CWD = KB * MD / 32;   // code dwords per row
   constexpr int CPL = CWD / 4;        // code dwords stored per lane
-  uint32_t m2c[CPL];
-#pragma unroll
-  for (int i = 0; i < CPL; ++i) {
-    const int wd = stream_dword<KB>(g, i);  // the stream dword this lane stores
-    uint32_t m = 0;
-    for (int j = 0; j < MD; ++j) {
-      if (a.dev.signs2[j] < 0.f) {
-        const int bp = j * KB;
-        if (bp / 32 == wd) m |= (uint32_t)(L - 1) << (bp % 32);
-        if (bp / 32 + 1 == wd && (bp % 32) + KB > 32) m |= (uint32_t)(L - 1) >> (32 - bp % 32);
-      }
-    }
-    m2c[i] = m;
+  uint32_t* s_m2 = reinterpret_cast<uint32_t*>(lds + m_lds_m2<KB, QJ>());
+  if (tid < CWD) s_m2[tid] = 0;
+  __syncthreads();
+  if (tid < MD && a.dev.signs2[tid] < 0.f) {
+    const int bp = tid * KB;
+    atomicOr(&s_m2[bp / 32], (uint32_t)(L - 1) << (bp % 32));
+    if ((bp % 32) + KB > 32) atomicOr(&s_m2[bp / 32 + 1], (uint32_t)(L - 1) >> (32 - bp % 32));
   }
   __syncthreads();
+  uint32_t m2c[CPL];  // the patterns of the stream dwords this lane stores
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) m2c[i] = s_m2[stream_dword<KB>(g, i)];
 
   const float inv_sqrt_d = 1.0f / __builtin_sqrtf((float)MD);
   const float rscale = (float)(1 << kRScaleLog2);
+  // A tile is 16 consecutive tokens of one KV head (so that, when their slots
+  // fill a paged block in order, every region of the block's record is
+  // written by this wave in contiguous runs): tile = token block * hkv + head.
+  // The wave's tiles advance by a fixed stride, so the (token block, head)
+  // pair advances by the stride's quotient and remainder.
   const int64_t tstride = (int64_t)gridDim.x * MW;
-  for (int64_t tile = (int64_t)blockIdx.x * MW + wave; tile < a.num_tiles; tile += tstride) {
-    // A tile is 16 consecutive tokens of one KV head (so that, when their slots
-    // fill a paged block in order, every region of the block's record is
-    // written by this wave in contiguous runs).
-    const int64_t t0 = (tile / a.hkv) * 16;
-    const int hh = (int)(tile % a.hkv);
+  const int64_t tile0 = (int64_t)blockIdx.x * MW + __builtin_amdgcn_readfirstlane(wave);
+  const int64_t blk_step = tstride / a.hkv;
+  const int head_step = (int)(tstride % a.hkv);
+  int64_t tblk = tile0 / a.hkv;
+  int hh = (int)(tile0 % a.hkv);
+  for (int64_t tile = tile0; tile < a.num_tiles;
+       tile += tstride, tblk += blk_step + (hh + head_step >= a.hkv ? 1 : 0),
+               hh = hh + head_step >= a.hkv ? hh + head_step - a.hkv : hh + head_step) {
+    const int64_t t0 = tblk * 16;
     // ---------------------------------------------------------------- key
     const int64_t tk = t0 + n;
     const bool valid = tk < a.num_tokens;
@@ -273,9 +290,9 @@ __global__ __launch_bounds__(mwaves<QJ>() * 64) void quantize_mfma_kernel(QMArgs
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float x = y[2 * kt + (e >> 2)][e & 3] * rscale;
-          const _Float16 hh = (_Float16)x;
-          rbh[kt][e] = hh;
-          rbl[kt][e] = (_Float16)(x - (float)hh);
+          const _Float16 xh = (_Float16)x;
+          rbh[kt][e] = xh;
+          rbl[kt][e] = (_Float16)(x - (float)xh);
         }
       // one column tile of z at a time (the S tiles come from LDS per tile);
       // bit i = 16 nt + 4 g + r of the row's stream is bit 16 (nt % 2) + 4 g + r
@@ -375,35 +392,22 @@ __global__ __launch_bounds__(mwaves<QJ>() * 64) void quantize_mfma_kernel(QMArgs
       const uint16_t s16 = f32_to_f16_bits((mx - mn) / LV);
       const uint16_t z16 = f32_to_f16_bits(mn);
       const float sc = f16_bits_to_f32(s16), zz = f16_bits_to_f32(z16);
-      // q = rint((v - z) / s) with the IEEE quotient: the product with the
-      // rounded reciprocal is within 3e-6 of it (|q| <= 16), so only lanes
-      // with a value within kVBand of a half-integer redo their group with
-      // the division
-      constexpr float kVBand = 8e-6f;
-      // a constant group (s = 0) codes 0: with rs = 0 every t is 0
+      // q = rint((v - z) / s) with the IEEE quotient, from the product with
+      // the rounded reciprocal and one correction by the exact residual
+      // (Markstein's theorem: the corrected quotient is the correctly rounded
+      // one; checked for every fp16 scale around every half-integer).  A
+      // constant group (s = 0) codes 0: with rs = 0 every quotient is 0.
       const float rs = sc != 0.f ? 1.0f / sc : 0.f;
       uint32_t vw[VB];
 #pragma unroll
       for (int i = 0; i < VB; ++i) vw[i] = 0;
-      float far = 0.f;  // largest distance of a quotient from its integer
 #pragma unroll
       for (int e = 0; e < 32; ++e) {
-        const float t = (x[e] - zz) * rs;
-        const float q0 = __builtin_rintf(t);
-        far = fmaxf(far, fabsf(t - q0));
-        const float q = fminf(fmaxf(q0, 0.f), LV);
+        const float dv = x[e] - zz;
+        const float q0 = dv * rs;
+        const float t = __builtin_fmaf(__builtin_fmaf(-q0, sc, dv), rs, q0);
+        const float q = fminf(fmaxf(__builtin_rintf(t), 0.f), LV);
         vw[(e * VB) / 32] |= (uint32_t)q << ((e * VB) % 32);
-      }
-      const bool near = far >= 0.5f - kVBand;
-      if (near && sc != 0.f) {
-#pragma unroll
-        for (int i = 0; i < VB; ++i) vw[i] = 0;
-#pragma unroll
-        for (int e = 0; e < 32; ++e) {
-          float q = __builtin_rintf((x[e] - zz) / sc);
-          q = fminf(fmaxf(q, 0.f), LV);
-          vw[(e * VB) / 32] |= (uint32_t)q << ((e * VB) % 32);
-        }
       }
       // ---- store the key record (after the value arithmetic: a wait for the
       // value rows issued after these stores would also wait for the stores)
@@ -441,7 +445,7 @@ template <int KB, int VB, bool QJ>
 hipError_t launch_m(const QMArgs& a, hipStream_t stream) {
   constexpr int MW = mwaves<QJ>();
   auto kern = quantize_mfma_kernel<KB, VB, QJ>;
-  const int lds = (QJ ? 65536 : 0) + (KB <= 4 ? 64 : 1024);
+  const int lds = m_lds_bytes<KB, QJ>();
   struct Cache {
     std::mutex mu;
     bool init[16] = {};
