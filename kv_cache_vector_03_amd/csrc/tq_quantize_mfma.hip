@@ -38,6 +38,8 @@
 namespace tq {
 namespace {
 
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
 constexpr int MD = 128, MKT = 4, MNT = 8;
 // waves per workgroup: with the QJL tiles (64 KB of LDS) one workgroup fills a
 // CU at three waves per SIMD; MSE-only keys need no tiles and run 8-wave
@@ -74,6 +76,18 @@ __device__ __forceinline__ float row_sum4(float x) {
   auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
+// Two or-reductions with one lane exchange.  Across the wave halves: lanes
+// 0..31 get a[l] | a[l + 32], lanes 32..63 get b[l - 32] | b[l].
+__device__ __forceinline__ uint32_t or_halves(uint32_t a, uint32_t b) {
+  auto s = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+  return s[0] | s[1];
+}
+// Across 16-lane row pairs: row 0 gets a.r0 | a.r1, row 1 b.r0 | b.r1, row 2
+// a.r2 | a.r3, row 3 b.r2 | b.r3.
+__device__ __forceinline__ uint32_t or_row_pairs(uint32_t a, uint32_t b) {
+  auto s = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+  return s[0] | s[1];
+}
 constexpr int parity(int x) { return __builtin_popcount(x) & 1; }
 // The code-stream dword that lane group g stores as its i-th (see the packing
 // of each key width below).
@@ -84,12 +98,6 @@ __device__ __forceinline__ int stream_dword(int g, int i) {
   if constexpr (KB == 8) return 4 * i + g;
   return CPL * g + i;
 }
-// a value the compiler cannot see through (keeps a select as bit operations)
-__device__ __forceinline__ uint32_t opaque_mask(uint32_t x) {
-  asm volatile("" : "+v"(x));
-  return x;
-}
-
 // LDS: the QJL tiles (64 KB), the upper centroids (and, for 8-bit codes, the
 // upper thresholds), the row's D2 code patterns
 template <int KB, bool QJ>
@@ -116,16 +124,20 @@ __global__ __launch_bounds__(mwaves<QJ>() * 64) void quantize_mfma_kernel(QMArgs
     for (int i = tid; i < 4096; i += MW * 64) const_cast<u32x4*>(s_st)[i] = src[i];
   }
   // upper centroids in LDS; upper thresholds in registers (8-bit codes: in
-  // LDS after the centroids, for a binary search)
+  // LDS after the centroids, for a binary search).  The key path works on
+  // coordinates scaled by the power of two R = 2^kRScaleLog2 that the QJL
+  // operands need, so centroids and thresholds are scaled by R here (exact:
+  // every decision and rounding is the same as unscaled, times R).
+  const float rscale = (float)(1 << kRScaleLog2);
   float* s_tU = s_c + H;
-  if (tid < H) s_c[tid] = a.dev.centroids[H + tid];
+  if (tid < H) s_c[tid] = a.dev.centroids[H + tid] * rscale;
   float tU[KB <= 4 ? H - 1 : 1];
   if constexpr (KB <= 4) {
 #pragma unroll
-    for (int i = 0; i < H - 1; ++i) tU[i] = a.dev.thresholds[H + i];
+    for (int i = 0; i < H - 1; ++i) tU[i] = a.dev.thresholds[H + i] * rscale;
   } else {
     tU[0] = 0.f;
-    if (tid < H - 1) s_tU[tid] = a.dev.thresholds[H + tid];
+    if (tid < H - 1) s_tU[tid] = a.dev.thresholds[H + tid] * rscale;
   }
   // D1 as bf16 sign-bit masks of the key operand: element e of slice kt is
   // coordinate 32 kt + 8 g + e
@@ -182,7 +194,6 @@ __global__ __launch_bounds__(mwaves<QJ>() * 64) void quantize_mfma_kernel(QMArgs
   for (int i = 0; i < CPL; ++i) m2c[i] = s_m2[stream_dword<KB>(g, i)];
 
   const float inv_sqrt_d = 1.0f / __builtin_sqrtf((float)MD);
-  const float rscale = (float)(1 << kRScaleLog2);
   // A tile is 16 consecutive tokens of one KV head (so that, when their slots
   // fill a paged block in order, every region of the block's record is
   // written by this wave in contiguous runs): tile = token block * hkv + head.
@@ -248,7 +259,7 @@ __global__ __launch_bounds__(mwaves<QJ>() * 64) void quantize_mfma_kernel(QMArgs
     ss = row_sum4(ss);
     const float nrm = __builtin_sqrtf(ss * (1.0f / MD));
     const bool zero = !(nrm > 0.f);
-    const float inv = zero ? 0.f : inv_sqrt_d / nrm;
+    const float inv = zero ? 0.f : (inv_sqrt_d / nrm) * rscale;  // R / (sqrt(d) n)
     // Lloyd-Max index of the D2-free coordinate from its magnitude, and the residual
     uint32_t field[MNT];
     float r2 = 0.f;
@@ -279,20 +290,25 @@ __global__ __launch_bounds__(mwaves<QJ>() * 64) void quantize_mfma_kernel(QMArgs
     }
     // a zero key stores zero codes, sign bits and gamma (selected per row
     // below, not per coordinate)
-    const float gamma = zero ? 0.f : __builtin_sqrtf(row_sum4(r2));
+    // (r2 holds R^2 |r|^2: the root scales exactly by R)
+    const float gamma = zero ? 0.f : __builtin_sqrtf(row_sum4(r2)) * (1.0f / rscale);
 
     // ---- QJL sign bits of S r (MSE-only keys skip the sketch)
     uint32_t qw = 0;  // the sign dword this lane stores (dword g of the row's d / 8 bytes)
     if constexpr (QJ) {
+      // fp16 hi / lo parts of R r, two elements per packed conversion
       f16x8 rbh[MKT], rbl[MKT];
 #pragma unroll
       for (int kt = 0; kt < MKT; ++kt)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float x = y[2 * kt + (e >> 2)][e & 3] * rscale;
-          const _Float16 xh = (_Float16)x;
-          rbh[kt][e] = xh;
-          rbl[kt][e] = (_Float16)(x - (float)xh);
+        for (int e = 0; e < 8; e += 2) {
+          const f32x2 x = {y[2 * kt + (e >> 2)][e & 3], y[2 * kt + (e >> 2)][(e & 3) + 1]};
+          const f16x2 xh = __builtin_convertvector(x, f16x2);
+          const f16x2 xl = __builtin_convertvector(x - __builtin_convertvector(xh, f32x2), f16x2);
+          rbh[kt][e] = xh[0];
+          rbh[kt][e + 1] = xh[1];
+          rbl[kt][e] = xl[0];
+          rbl[kt][e + 1] = xl[1];
         }
       // one column tile of z at a time (the S tiles come from LDS per tile);
       // bit i = 16 nt + 4 g + r of the row's stream is bit 16 (nt % 2) + 4 g + r
@@ -323,50 +339,45 @@ __global__ __launch_bounds__(mwaves<QJ>() * 64) void quantize_mfma_kernel(QMArgs
       qw = zero ? 0u : qw;
     }
 
-    // ---- code stream of the row: field nt (4 codes) at bit KB (16 nt + 4 g)
+    // ---- code stream of the row: field nt (4 codes) at bit KB (16 nt + 4 g).
+    // Each lane places its fields in the stream dwords they fall into; the
+    // or over the row's four lanes is a reduce-scatter with lane exchanges,
+    // leaving in lane group g exactly the dwords it stores.
     uint32_t cst[CPL];
     if constexpr (KB == 2) {
       // 8-bit fields: dword nt, byte g; lane g stores dwords 2 g, 2 g + 1
-      uint32_t wds[MNT];
+      uint32_t h[4];
 #pragma unroll
-      for (int nt = 0; nt < MNT; ++nt) wds[nt] = row_or4(field[nt] << (8 * g));
+      for (int k = 0; k < 4; ++k) h[k] = or_halves(field[k] << (8 * g), field[k + 4] << (8 * g));
 #pragma unroll
-      for (int i = 0; i < CPL; ++i) cst[i] = g == 0 ? wds[i] : g == 1 ? wds[2 + i] : g == 2 ? wds[4 + i] : wds[6 + i];
+      for (int i = 0; i < CPL; ++i) cst[i] = or_row_pairs(h[i], h[i + 2]);
     } else if constexpr (KB == 3) {
       // pairs of 12-bit fields in three dwords 3 p .. 3 p + 2: F_2p at bit 12 g,
       // F_2p+1 at bit 48 + 12 g; lane g stores dwords 3 g .. 3 g + 2
-      uint32_t wds[12];
+      uint32_t c[12];
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         const uint64_t x = (uint64_t)field[2 * p] | ((uint64_t)field[2 * p + 1] << 48);
         const uint64_t lo = x << (12 * g);
-        const uint32_t hi = (uint32_t)(((uint64_t)field[2 * p + 1] << (12 * g + 16)) >> 32);
-        wds[3 * p] = row_or4((uint32_t)lo);
-        wds[3 * p + 1] = row_or4((uint32_t)(lo >> 32));
-        wds[3 * p + 2] = row_or4(hi);
+        c[3 * p] = (uint32_t)lo;
+        c[3 * p + 1] = (uint32_t)(lo >> 32);
+        c[3 * p + 2] = (uint32_t)(((uint64_t)field[2 * p + 1] << (12 * g + 16)) >> 32);
       }
+      uint32_t h[6];
 #pragma unroll
-      for (int i = 0; i < CPL; ++i) cst[i] = g == 0 ? wds[i] : g == 1 ? wds[3 + i] : g == 2 ? wds[6 + i] : wds[9 + i];
+      for (int k = 0; k < 6; ++k) h[k] = or_halves(c[k], c[k + 6]);
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) cst[i] = or_row_pairs(h[i], h[i + 3]);
     } else if constexpr (KB == 8) {
       // 32-bit fields: the lane's four codes of column tile nt are bytes
       // 16 nt + 4 g .. + 3 of the stream, i.e. dword 4 nt + g, whole
 #pragma unroll
       for (int i = 0; i < CPL; ++i) cst[i] = field[i];
     } else {
-      // 16-bit fields: dword 2 nt + (g >> 1), half g & 1; or over the pair
-      // (g, g ^ 1); lane g stores dwords 2 (4 (g & 1) + i) + (g >> 1), i < 4
-      uint32_t wds[MNT];
+      // 16-bit fields: dword 2 nt + (g >> 1), half g & 1 (an or over the lane
+      // pair g, g ^ 1); lane g stores dwords 2 (4 (g & 1) + i) + (g >> 1), i < 4
 #pragma unroll
-      for (int nt = 0; nt < MNT; ++nt) {
-        uint32_t x = field[nt] << (16 * (g & 1));
-        auto b = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-        wds[nt] = b[0] | b[1];
-      }
-      // a bitwise select: written as (g & 1) ? wds[4 + i] : wds[i] the compiler
-      // turns it into a lane-indexed load from a stack copy of wds
-      const uint32_t odd = opaque_mask((g & 1) ? ~0u : 0u);
-#pragma unroll
-      for (int i = 0; i < CPL; ++i) cst[i] = (wds[4 + i] & odd) | (wds[i] & ~odd);
+      for (int i = 0; i < CPL; ++i) cst[i] = or_row_pairs(field[i] << (16 * (g & 1)), field[4 + i] << (16 * (g & 1)));
     }
 
     // -------------------------------------------------------------- value
