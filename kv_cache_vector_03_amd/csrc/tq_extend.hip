@@ -282,15 +282,21 @@ __global__ __launch_bounds__(ENW * 64) void extend_kernel(EArgs a) {
     const float d1a = a.dev.signs1[2 * lane], d1b = a.dev.signs1[2 * lane + 1];
     const float d2a = a.dev.signs2[2 * lane], d2b = a.dev.signs2[2 * lane + 1];
     const float inv = 1.0f / __builtin_sqrtf((float)ED);
+    // the 16 rows' loads are issued together (one round trip), rows past the
+    // chunk read as zeros
+    uint32_t qraw[ERPW];
+#pragma unroll
     for (int i = 0; i < ERPW; ++i) {
       const int r = wave * ERPW + i;
       const int tok = tq0 + r / G, hq = h * G + r % G;
-      float x0 = 0.f, x1 = 0.f;
-      if (tok < C) {  // uniform
-        const uint32_t w = *reinterpret_cast<const uint32_t*>(a.q + ((int64_t)(cu0 + tok) * a.Hq + hq) * ED + 2 * lane);
-        x0 = __uint_as_float(w << 16) * d1a;
-        x1 = __uint_as_float(w & 0xFFFF0000u) * d1b;
-      }
+      qraw[i] = tok < C ? *reinterpret_cast<const uint32_t*>(a.q + ((int64_t)(cu0 + tok) * a.Hq + hq) * ED + 2 * lane)
+                        : 0u;  // uniform condition
+    }
+#pragma unroll
+    for (int i = 0; i < ERPW; ++i) {
+      const int r = wave * ERPW + i;
+      const float x0 = __uint_as_float(qraw[i] << 16) * d1a;
+      const float x1 = __uint_as_float(qraw[i] & 0xFFFF0000u) * d1b;
       float y0 = x0 + x1, y1 = x0 - x1;
       y0 = wht_xlane<1>(y0, s1);
       y1 = wht_xlane<1>(y1, s1);
