@@ -104,9 +104,30 @@ template <int KB, bool QJ>
 constexpr int m_lds_m2() {
   return (QJ ? 65536 : 0) + (KB <= 4 ? 64 : 1024);
 }
+// then each wave's buffer for the key rows of its next tile (16 rows x d bf16)
+template <int KB, bool QJ>
+constexpr int m_lds_kbuf() {
+  return (m_lds_m2<KB, QJ>() + KB * MD / 8 + 15) / 16 * 16;
+}
+constexpr int kKeyTileBytes = 16 * MD * 2;
 template <int KB, bool QJ>
 constexpr int m_lds_bytes() {
-  return m_lds_m2<KB, QJ>() + KB * MD / 8;
+  return m_lds_kbuf<KB, QJ>() + mwaves<QJ>() * kKeyTileBytes;
+}
+// Direct global -> LDS copy of 16 bytes per lane (lane l's bytes land at LDS
+// byte address m0 + 16 l), as inline assembly so that the compiler does not
+// fence later LDS reads on it; completion is awaited with s_waitcnt vmcnt.
+__device__ __forceinline__ void key_dma16(uint32_t lds_byte_addr, uint64_t sbase, uint32_t voff) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)sbase);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(sbase >> 32));
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %1"
+      :
+      : "s"((uint32_t)__builtin_amdgcn_readfirstlane((int)lds_byte_addr)), "s"(((uint64_t)hi << 32) | (uint64_t)lo),
+        "v"(voff)
+      : "memory");
 }
 
 template <int KB, int VB, bool QJ>
@@ -205,6 +226,20 @@ __global__ __launch_bounds__(mwaves<QJ>() * 64) void quantize_mfma_kernel(QMArgs
   const int head_step = (int)(tstride % a.hkv);
   int64_t tblk = tile0 / a.hkv;
   int hh = (int)(tile0 % a.hkv);
+  // The key rows of a wave's next tile are copied to its LDS buffer while the
+  // current tile is processed (lane (n, g) copies row n's coordinates
+  // 32 kt + 8 g .. + 7 for kt < 4; rows past the batch copy row t0 instead).
+  unsigned char* kbuf = lds + m_lds_kbuf<KB, QJ>() + __builtin_amdgcn_readfirstlane(wave) * kKeyTileBytes;
+  const uint32_t kbuf_addr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)kbuf;
+  auto fetch_keys = [&](int64_t tb, int hd) {
+    const int64_t row0 = tb * 16;
+    const int64_t r = row0 + n < a.num_tokens ? n : 0;
+    const uint64_t sbase = (uint64_t)(uintptr_t)(a.k + (row0 * a.hkv + hd) * MD);
+    const uint32_t voff = (uint32_t)((r * a.hkv * MD + 8 * g) * 2);
+#pragma unroll
+    for (int kt = 0; kt < MKT; ++kt) key_dma16(kbuf_addr + kt * 1024, sbase, voff + kt * 64);
+  };
+  if (tile0 < a.num_tiles) fetch_keys(tblk, hh);
   for (int64_t tile = tile0; tile < a.num_tiles;
        tile += tstride, tblk += blk_step + (hh + head_step >= a.hkv ? 1 : 0),
                hh = hh + head_step >= a.hkv ? hh + head_step - a.hkv : hh + head_step) {
@@ -212,7 +247,6 @@ __global__ __launch_bounds__(mwaves<QJ>() * 64) void quantize_mfma_kernel(QMArgs
     // ---------------------------------------------------------------- key
     const int64_t tk = t0 + n;
     const bool valid = tk < a.num_tokens;
-    const int64_t th = tk * a.hkv + hh;
     // value rows: lane l holds channels 32 (l % 4) .. + 31 of row l / 4
     const int vrow = lane >> 2, vpart = lane & 3;
     const int64_t tv = t0 + vrow;
@@ -225,10 +259,20 @@ __global__ __launch_bounds__(mwaves<QJ>() * 64) void quantize_mfma_kernel(QMArgs
     const int32_t vslot = vvalid ? a.slot_mapping[tv] : -1;
     bf16x8 kbv[MKT];
     {
-      const u32x4* pk = reinterpret_cast<const u32x4*>(a.k + (valid ? th : 0) * MD + 8 * g);
+      // this tile's key rows (copied during the previous tile), then the copy
+      // of the next tile's into the same buffer once they are read
+      asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
+      u32x4 kw[MKT];
+#pragma unroll
+      for (int kt = 0; kt < MKT; ++kt) kw[kt] = *reinterpret_cast<const u32x4*>(kbuf + kt * 1024 + lane * 16);
+      asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+      if (tile + tstride < a.num_tiles) {  // uniform
+        const int nh = hh + head_step;
+        fetch_keys(tblk + blk_step + (nh >= a.hkv ? 1 : 0), nh >= a.hkv ? nh - a.hkv : nh);
+      }
 #pragma unroll
       for (int kt = 0; kt < MKT; ++kt) {
-        u32x4 w = valid ? __builtin_nontemporal_load(pk + 4 * kt) : u32x4{0u, 0u, 0u, 0u};
+        u32x4 w = valid ? kw[kt] : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int i = 0; i < 4; ++i) w[i] ^= d1m[kt][i];
         kbv[kt] = __builtin_bit_cast(bf16x8, w);
