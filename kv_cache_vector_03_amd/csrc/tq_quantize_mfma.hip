@@ -259,9 +259,12 @@ __global__ __launch_bounds__(mwaves<QJ>() * 64) void quantize_mfma_kernel(QMArgs
     const int32_t vslot = vvalid ? a.slot_mapping[tv] : -1;
     bf16x8 kbv[MKT];
     {
-      // this tile's key rows (copied during the previous tile), then the copy
-      // of the next tile's into the same buffer once they are read
-      asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
+      // this tile's key rows, then the copy of the next tile's into the same
+      // buffer once they are read.  The copy issued during the previous tile
+      // completed at that tile's wait before its value stage (below), so
+      // only the first tile waits here, and no tile waits at its start for
+      // the previous tile's record stores.
+      if (tile == tile0) asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
       u32x4 kw[MKT];
 #pragma unroll
       for (int kt = 0; kt < MKT; ++kt) kw[kt] = *reinterpret_cast<const u32x4*>(kbuf + kt * 1024 + lane * 16);
@@ -425,6 +428,9 @@ __global__ __launch_bounds__(mwaves<QJ>() * 64) void quantize_mfma_kernel(QMArgs
     }
 
     // -------------------------------------------------------------- value
+    // the value rows, the slots and the next tile's key copy were all issued
+    // before any store of this tile: this waits for loads only
+    asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
     // row-part layout: lane l holds channels 32 (l % 4) .. + 31 of row l / 4
     {
       const int part = vpart;
