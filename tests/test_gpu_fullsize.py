@@ -164,6 +164,32 @@ def test_long_context_d256_full_size_all_pairs():
     ctx.close()
 
 
+@pytest.mark.parametrize("mse_only,kb", [(False, 3), (True, 4)])
+def test_long_context_d256_gqa8_all_pairs(mse_only, kb):
+    """d = 256 with eight query heads per KV head (the variants that keep one
+    wave per SIMD and hold the most registers) over 65,536- and 40,001-token
+    sequences: every output row and score against the oracle decode of the
+    GPU-written pool."""
+    d, B, Hq, Hkv, vb, seed = 256, 2, 32, 4, 4, 7
+    lens = np.array([65536, 40001])
+    L = int(lens.max())
+    nb = B * (L // 16) + 8
+    G = Hq // Hkv
+    prm = oracle_params(seed, d, kb)
+    prm["qjl"] = not mse_only
+    ctx = tq.tq_codebook_init(d, kb, vb, signs=prm["signs"], S=prm["S"], mse_only=mse_only)
+    bt_np = synth.block_table(seed, B, L // 16, nb)
+    bt = torch.from_numpy(bt_np).cuda()
+    pool = torch.zeros((nb, Hkv, ctx.block_bytes), dtype=torch.uint8, device="cuda")
+    _fill(ctx, pool, bt, lens, Hkv, d, seed, 0.005, 20.0)
+    q = synth.bf16_round(synth.queries(seed, B, Hq, d))
+    qd = torch.from_numpy(q).to(torch.bfloat16).cuda()
+    out, scores = _decode(qd, [ctx], [pool], bt, torch.from_numpy(lens.astype(np.int32)).cuda(), L)
+    _check_all_pairs(f"long d256 G8 k{kb}v4{' mse-only' if mse_only else ''}", [pool.cpu().numpy()],
+                     [paged.layout(d, kb, vb, qjl=not mse_only)], [prm], bt_np, lens, q, G, out, scores)
+    ctx.close()
+
+
 def test_ragged_mixed_presets_recent_window_full_size_all_pairs():
     d, B, Hq, Hkv, W, seed = 128, 64, 32, 8, 128, 5
     G = Hq // Hkv
