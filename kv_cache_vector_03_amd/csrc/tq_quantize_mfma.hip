@@ -25,6 +25,8 @@
 //             gets z_i for i = 16 nt + 4 g + r and packs its sign bits.
 //   pack      code and sign-bit fields are placed at their stream offsets in
 //             the lane and or-ed over the four lanes of a row (permlane swaps).
+// The key rows of a wave's next tile are copied into its LDS buffer while the
+// current tile runs (global_load_lds), so tiles start without a key round trip.
 // Values are quantised in the row-part layout (lane: row l / 4, 32-channel
 // group l % 4), one group per lane.
 #include <hip/hip_runtime.h>
