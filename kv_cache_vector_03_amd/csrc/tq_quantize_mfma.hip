@@ -321,8 +321,22 @@ __global__ __launch_bounds__(mwaves<QJ>() * 64) void quantize_mfma_kernel(QMArgs
         const float m = fabsf(u);
         uint32_t cnt = 0;
         if constexpr (KB <= 4) {
-#pragma unroll
-          for (int i = 0; i < H - 1; ++i) cnt += m > tU[i] ? 1u : 0u;
+          // #{upper thresholds < m} by binary search over the sorted
+          // thresholds in registers (each level picks its threshold with
+          // selects on the bits found so far)
+          if constexpr (H == 2) {
+            cnt = m > tU[0] ? 1u : 0u;
+          } else if constexpr (H == 4) {
+            const bool b1 = m > tU[1];
+            const float t = b1 ? tU[2] : tU[0];
+            cnt = (b1 ? 2u : 0u) + (m > t ? 1u : 0u);
+          } else {
+            const bool b2 = m > tU[3];
+            const float t1 = b2 ? tU[5] : tU[1];
+            const bool b1 = m > t1;
+            const float t0 = b2 ? (b1 ? tU[6] : tU[4]) : (b1 ? tU[2] : tU[0]);
+            cnt = (b2 ? 4u : 0u) + (b1 ? 2u : 0u) + (m > t0 ? 1u : 0u);
+          }
         } else {
           // #{upper thresholds < m}: seven halving steps over the 127 in LDS
 #pragma unroll
