@@ -227,3 +227,38 @@ def test_large_batch_store_kernel_edges(kb, vb, mse_only):
           f"differing bits outside band={outside} inside={inside}; codes in band "
           f"{sum(b['codes'] for b in bands)}", flush=True)
     assert outside == 0
+
+
+@pytest.mark.parametrize("kb,vb,mse_only", [(3, 4, False), (4, 2, True)])
+def test_store_kernel_several_tiles_per_wave(kb, vb, mse_only):
+    """More 16-token tiles than the persistent grid holds waves, with 7 KV heads
+    (so a wave's stride through the tiles advances the head as well as the
+    token block, and the key rows copied ahead into LDS belong to another
+    head): 16,000 tokens x 7 heads in one call, the whole pool compared bit
+    for bit with the oracle (outside the 1e-6 band)."""
+    T, Hkv, d = 16000, 7, 128
+    rng = np.random.default_rng(77 + kb + 10 * vb)
+    K = synth.normal_with_outliers(rng, (T, Hkv, d), 0.005, 20.0)
+    V = synth.normal_with_outliers(rng, (T, Hkv, d), 0.005, 20.0)
+    nb = T // 16 + 5
+    slots = rng.permutation(nb * 16)[:T].astype(np.int64)
+    prm = oracle_params(77 + kb, d, kb)
+    ctx = tq.tq_codebook_init(d, kb, vb, signs=prm["signs"], S=prm["S"], mse_only=mse_only)
+    k = torch.from_numpy(np.ascontiguousarray(K)).to(torch.bfloat16).cuda()
+    v = torch.from_numpy(np.ascontiguousarray(V)).to(torch.bfloat16).cuda()
+    pool = torch.full((nb, Hkv, ctx.block_bytes), 0x5C, dtype=torch.uint8, device="cuda")
+    tq.tq_quantize_store(ctx, k, v, torch.from_numpy(slots.astype(np.int32)).cuda(), pool)
+    torch.cuda.synchronize()
+    gpu = pool.cpu().numpy()
+    ctx.close()
+    Kx = k.float().cpu().numpy().astype(np.float64)
+    Vx = v.float().cpu().numpy()
+    lay = paged.layout(d, kb, vb, qjl=not mse_only)
+    exp = np.full((nb, Hkv, lay["bytes"]), 0x5C, np.uint8)
+    mask = paged.new_pool(nb, Hkv, lay)
+    for h in range(Hkv):
+        expected_records(Kx[:, h], Vx[:, h], slots, h, prm, d, kb, vb, exp, mask, qjl=not mse_only)
+    outside, inside = compare_pools(gpu, exp, mask)
+    print(f"[quantize parity several tiles per wave k{kb}v{vb}{' mse-only' if mse_only else ''}] {T * Hkv} "
+          f"token-heads: differing bits outside band={outside} inside={inside}", flush=True)
+    assert outside == 0
