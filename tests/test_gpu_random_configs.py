@@ -209,30 +209,33 @@ def test_random_extend_configuration(i):
     assert np.all(np.isfinite(out)) and worst <= TOL
 
 
-def test_gqa8_many_items_per_workgroup():
-    """Eight query heads per KV head with many split items per workgroup (so
-    the score operands kept in LDS by the 2-3-bit kernels are reused and
-    rebuilt across consecutive items), two presets (K3V4: operands in LDS;
-    K4V4 with the sketch: operands in registers), ragged lengths, 64-token
-    splits and a bf16 recent window."""
-    d, B, Hq, Hkv, W, chunk, seed = 128, 16, 64, 8, 32, 64, 9900
-    kinds = [(3, 4), (4, 4)]
+@pytest.mark.parametrize("Hq,mse_first", [(64, False), (32, True)])
+def test_gqa8_many_items_per_workgroup(Hq, mse_first):
+    """Many split items per workgroup (so the score operands kept in LDS are
+    reused and rebuilt across consecutive items), two presets, ragged
+    lengths, 64-token splits and a bf16 recent window.  Eight query heads
+    per KV head: K3V4 (operands in LDS, 8-wave workgroups) beside K4V4 with
+    the sketch (operands in registers).  Four: K3V4 with MSE-only keys
+    (operands in LDS, 12-wave workgroups) beside K4V4 with the sketch."""
+    d, B, Hkv, W, chunk, seed = 128, 16, 8, 32, 64, 9900 if Hq == 64 else 9932
+    kinds = [(3, 4, not mse_first), (4, 4, True)]
     lens = synth.ragged_lengths(seed, B, lo=100, hi=3000, median=1200.0)
     lens[3] = 0
-    print(f"[gqa8 many items] lens={lens.tolist()} chunk={chunk} W={W}", flush=True)
+    print(f"[many items G{Hq // Hkv}] lens={lens.tolist()} chunk={chunk} W={W}", flush=True)
     seq_preset = (np.arange(B) % 2).astype(np.int8)
     mb = int(np.ceil(lens.max() / 16))
     nb = B * mb + 2
     bt = synth.block_table(seed, B, mb, nb)
     prms, ctxs, pools, fields = [], [], [], {}
-    for p, (kb, vb) in enumerate(kinds):
+    for p, (kb, vb, qjl) in enumerate(kinds):
         prm = oracle_params(seed + 7 * p, d, kb)
-        pool = paged.new_pool(nb, Hkv, paged.layout(d, kb, vb))
+        prm["qjl"] = qjl
+        pool = paged.new_pool(nb, Hkv, paged.layout(d, kb, vb, qjl=qjl))
         seqs = [b for b in range(B) if seq_preset[b] == p]
-        fields.update(oracle_cache(prm, d, kb, vb, lens, Hkv, bt, pool, seed, p=0.005, seqs=seqs))
+        fields.update(oracle_cache(prm, d, kb, vb, lens, Hkv, bt, pool, seed, p=0.005, seqs=seqs, qjl=qjl))
         prms.append(prm)
         pools.append(pool)
-        ctxs.append(tq.tq_codebook_init(d, kb, vb, signs=prm["signs"], S=prm["S"]))
+        ctxs.append(tq.tq_codebook_init(d, kb, vb, signs=prm["signs"], S=prm["S"], mse_only=not qjl))
     rng = np.random.default_rng([seed, 1])
     rlens = rng.integers(0, W + 1, B)
     rk32 = synth.bf16_round(rng.standard_normal((B, Hkv, W, d)).astype(np.float32))
@@ -266,5 +269,5 @@ def test_gqa8_many_items_per_workgroup():
             got = np.concatenate([sc[b, :, :L], sc[b, :, L:L + R]], axis=1)
             serr.append(score_errors(got.astype(np.float64), s))
     oe = output_errors(out.astype(np.float64), np.stack(ref))
-    print(f"[gqa8 many items] max score err {max(serr):.2e} max out err {oe:.2e}", flush=True)
+    print(f"[many items G{Hq // Hkv}] max score err {max(serr):.2e} max out err {oe:.2e}", flush=True)
     assert np.all(np.isfinite(out)) and max(serr) <= TOL and oe <= TOL
