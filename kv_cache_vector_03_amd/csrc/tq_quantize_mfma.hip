@@ -65,13 +65,7 @@ struct QMArgs {
   int64_t num_tiles;
 };
 
-// or / sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the lanes of one row)
-__device__ __forceinline__ uint32_t row_or4(uint32_t x) {
-  auto a = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-  x = a[0] | a[1];
-  auto b = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-  return b[0] | b[1];
-}
+// sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the lanes of one row)
 __device__ __forceinline__ float row_sum4(float x) {
   auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
@@ -376,29 +370,38 @@ __global__ __launch_bounds__(mwaves<QJ>() * 64) void quantize_mfma_kernel(QMArgs
       // one column tile of z at a time (the S tiles come from LDS per tile);
       // bit i = 16 nt + 4 g + r of the row's stream is bit 16 (nt % 2) + 4 g + r
       // of dword nt / 2, which lane g = nt / 2 keeps
-      uint32_t dw = 0;
+      // dword p (of the row's four sign dwords) gets bits 16 (nt % 2) + 4 g + r
+      // of column tiles nt = 2 p, 2 p + 1 from every lane group g; the four
+      // partial dwords rotate through d0..d3 and one reduce-scatter over the
+      // row's lanes leaves dword g in lane group g
+      uint32_t d0 = 0, d1 = 0, d2 = 0, d3 = 0;
 #pragma unroll 1
-      for (int nt = 0; nt < MNT; ++nt) {
-        f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        const u32x4* tp = s_st + (nt * MKT * 2) * 64 + lane;
+      for (int p = 0; p < MNT / 2; ++p) {
+        uint32_t dw = 0;
 #pragma unroll
-        for (int kt = 0; kt < MKT; ++kt) {
-          const f16x8 ah = __builtin_bit_cast(f16x8, tp[(2 * kt) * 64]);
-          const f16x8 al = __builtin_bit_cast(f16x8, tp[(2 * kt + 1) * 64]);
-          z = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, rbh[kt], z, 0, 0, 0);
-          z = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, rbl[kt], z, 0, 0, 0);
-          z = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, rbh[kt], z, 0, 0, 0);
-        }
-        uint32_t nib = 0;
+        for (int hn = 0; hn < 2; ++hn) {
+          const int nt = 2 * p + hn;
+          f32x4 z = {0.f, 0.f, 0.f, 0.f};
+          const u32x4* tp = s_st + (nt * MKT * 2) * 64 + lane;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) nib |= (z[r] >= 0.f ? 1u : 0u) << r;
-        dw |= nib << (16 * (nt & 1) + 4 * g);
-        if (nt & 1) {  // uniform
-          dw = row_or4(dw);
-          if (g == (nt >> 1)) qw = dw;
-          dw = 0;
+          for (int kt = 0; kt < MKT; ++kt) {
+            const f16x8 ah = __builtin_bit_cast(f16x8, tp[(2 * kt) * 64]);
+            const f16x8 al = __builtin_bit_cast(f16x8, tp[(2 * kt + 1) * 64]);
+            z = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, rbh[kt], z, 0, 0, 0);
+            z = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, rbl[kt], z, 0, 0, 0);
+            z = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, rbh[kt], z, 0, 0, 0);
+          }
+          uint32_t nib = 0;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) nib |= (z[r] >= 0.f ? 1u : 0u) << r;
+          dw |= nib << (16 * hn + 4 * g);
         }
+        d0 = d1;
+        d1 = d2;
+        d2 = d3;
+        d3 = dw;
       }
+      qw = or_row_pairs(or_halves(d0, d2), or_halves(d1, d3));
       qw = zero ? 0u : qw;
     }
 
